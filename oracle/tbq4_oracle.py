@@ -1,0 +1,334 @@
+"""Plain, slow, fp64 CPU oracle for TBQ4 attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: it is used by ``tests/``, by ``__graft_entry__.smoke()``
+and by the ``cpu_baseline`` leg of ``bench.py``, and by nothing else.  It shares
+no code, tables or constants with the HIP library; every constant below is
+written out here independently.
+
+What it computes, and where that comes from
+-------------------------------------------
+Source page: "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq"
+(trefon.com notes).
+
+* Section "Od czego zacząłem": a TBQ4 block holds 128 values in 66 bytes -- a
+  2-byte scale followed by 64 bytes of 4-bit indices (4.125 bits per value) --
+  and attention runs in the rotated (Hadamard) domain, with dequantisation in
+  the inner loop and no F16 buffer.
+* Section "Konfiguracja": both the K and the V cache use the ``tbq4_0`` type
+  (``-ctk tbq4_0 -ctv tbq4_0``), flash attention is on.
+* Section "Liczby": 4.125 bpv and about 4.1 GiB at 262144 tokens.
+
+The page does not fix the rotation's sign vector, the codebook, the scale
+statistic, the rounding rules or the nibble order.  The readings taken here
+(each one is listed with its reason in the design notes of the repository):
+
+* rotation   u = R x,  R = H D / sqrt(128): D = diag(s) with s a +-1 vector
+               drawn from SplitMix64(seed), H the natural-order Sylvester
+               Hadamard matrix (H_ij = (-1)^popcount(i&j)); signs first.
+* scale      d = the binary16 value nearest the exact square root of the mean
+               square of u, ties to even, saturating at 65504.
+* codebook   16 sign-symmetric levels: of all sign-symmetric 16-level
+               codebooks whose levels have at most 4 significant bits, the one
+               with least mean-square error on N(0,1) under nearest-level
+               decisions (the 16-level Lloyd-Max quantiser held to a grid on
+               which every level is exact in fp16, bf16 and fp8 e4m3).
+* index      idx_i = #{k in 0..14 : d * t_k < u_i} with t_k the midpoints of
+               adjacent levels (nearest level, ties to the lower index).
+* pack       bytes 0-1 = d (binary16, little endian); byte 2+j holds
+               idx_{2j} in its low nibble and idx_{2j+1} in its high nibble.
+* attention  plain softmax attention on the dequantised cache; query head h
+               reads KV head floor(h / G), G = H_q / H_kv; a prefill query at
+               absolute position n_past+i attends keys 0..n_past+i inclusive.
+
+Every floating-point step of the quantiser is an IEEE-754 fp64 operation in a
+stated order, so the packed bytes are a deterministic function of the input.
+"""
+
+import numpy as np
+
+HEAD_DIM = 128
+BLOCK_BYTES = 66
+_MASK64 = (1 << 64) - 1
+
+# --------------------------------------------------------------------------
+# Codebook: the least-MSE sign-symmetric 16-level quantiser of N(0,1) whose
+# levels have at most four significant bits (it sits next to the 16-level
+# Lloyd-Max levels 0.1284 ... 2.733); thresholds are midpoints of adjacent
+# levels.  Ascending order; c[15-k] == -c[k].
+# --------------------------------------------------------------------------
+_POS_LEVELS = (0.125, 0.375, 0.625, 0.9375, 1.25, 1.625, 2.0, 2.75)
+CODEBOOK = np.array([-v for v in reversed(_POS_LEVELS)] + list(_POS_LEVELS),
+                    dtype=np.float64)
+THRESHOLDS = (CODEBOOK[:-1] + CODEBOOK[1:]) / 2.0      # 15 values, exact
+
+# fl64(1/sqrt(128)) -- the normalisation of the 128-point transform.
+INV_SQRT128 = float.fromhex("0x1.6a09e667f3bccp-4")
+
+
+# --------------------------------------------------------------------------
+# Sign vector: SplitMix64 (Steele, Lea and Flood, "Fast splittable
+# pseudorandom number generators", OOPSLA 2014).
+# --------------------------------------------------------------------------
+def splitmix64(seed, n):
+    """First ``n`` outputs of SplitMix64 started from ``seed`` (ints < 2**64)."""
+    state = seed & _MASK64
+    out = []
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & _MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def sign_bits(seed):
+    """The 16 bytes of the sign vector: bit i (little endian) set <=> s_i = -1."""
+    w0, w1 = splitmix64(seed, 2)
+    return w0.to_bytes(8, "little") + w1.to_bytes(8, "little")
+
+
+def sign_vector(seed):
+    """s in {+1,-1}^128: s_i = -1 iff bit (i mod 64) of word floor(i/64) is 1."""
+    w = splitmix64(seed, 2)
+    s = np.ones(HEAD_DIM, dtype=np.float64)
+    for i in range(HEAD_DIM):
+        if (w[i // 64] >> (i % 64)) & 1:
+            s[i] = -1.0
+    return s
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard transform (natural order), fp64 butterflies.
+# --------------------------------------------------------------------------
+def _butterfly(v):
+    """In order h = 1, 2, ..., 64: (v_i, v_{i+h}) <- (v_i + v_{i+h}, v_i - v_{i+h})
+    for every i with (i & h) == 0.  Returns H v (unnormalised)."""
+    v = np.array(v, dtype=np.float64, copy=True)
+    lead = v.shape[:-1]
+    h = 1
+    while h < HEAD_DIM:
+        w = v.reshape(lead + (HEAD_DIM // (2 * h), 2, h))
+        a = w[..., 0, :]
+        b = w[..., 1, :]
+        v = np.stack((a + b, a - b), axis=-2).reshape(lead + (HEAD_DIM,))
+        h *= 2
+    return v
+
+
+def rotate(x, signs):
+    """u = R x = H (s * x) * fl64(1/sqrt(128)), along the last axis, in fp64."""
+    v = np.asarray(x, dtype=np.float64) * signs
+    return _butterfly(v) * INV_SQRT128
+
+
+def unrotate(y, signs):
+    """x = R^T y = s * (H y) * fl64(1/sqrt(128)); R^T R = I because H H = 128 I."""
+    return signs * (_butterfly(np.asarray(y, dtype=np.float64)) * INV_SQRT128)
+
+
+# --------------------------------------------------------------------------
+# binary16 helpers
+# --------------------------------------------------------------------------
+def _half_values():
+    bits = np.arange(0x7C00, dtype=np.uint16)          # +0 ... 65504
+    return bits.view(np.float16).astype(np.float64)
+
+
+_HALF_VALUES = _half_values()
+# mid2[h-1] = ((value(h-1) + value(h)) / 2)^2 for h = 1..0x7BFF.  A midpoint
+# has at most 12 significant bits, so its square is exact in fp64.
+_MID2 = ((_HALF_VALUES[:-1] + _HALF_VALUES[1:]) / 2.0) ** 2
+
+
+def half_nearest_sqrt(ms):
+    """binary16 bit pattern of the value nearest sqrt(ms) (exact real root),
+    ties to even, saturating at 65504 (0x7BFF).  ``ms`` is an fp64 array >= 0.
+
+    The pattern h is the number of midpoints below sqrt(ms) -- counting a
+    midpoint equal to sqrt(ms) only when the pattern above it is even -- so
+    the comparison is between exact squares and never takes a square root."""
+    ms = np.asarray(ms, dtype=np.float64)
+    n_lt = np.searchsorted(_MID2, ms, side="left")
+    n_le = np.searchsorted(_MID2, ms, side="right")
+    tie = n_le > n_lt                       # sqrt(ms) is exactly midpoint n_lt+1
+    take_tie = tie & (((n_lt + 1) % 2) == 0)
+    return (n_lt + take_tie).astype(np.uint16)
+
+
+def half_bits_to_float(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Quantiser
+# --------------------------------------------------------------------------
+def quantize_blocks(x, seed=0):
+    """Quantise blocks of 128 values to TBQ4.
+
+    x: array (..., 128) in fp32 / fp16 / fp64 (converted to fp64 exactly).
+    Returns (packed uint8 (..., 66), idx uint8 (..., 128), d_bits uint16 (...)).
+    """
+    signs = sign_vector(seed)
+    x = np.asarray(x)
+    if x.shape[-1] != HEAD_DIM:
+        raise ValueError("last axis must be 128")
+    u = rotate(x.astype(np.float64), signs)
+
+    # mean square: p_i = u_i*u_i, then the tree p_i += p_{i+h} for
+    # h = 64, 32, ..., 1 and i < h; S = p_0; ms = S * 2^-7 (exact).
+    p = u * u
+    h = HEAD_DIM // 2
+    while h >= 1:
+        p = p.copy()
+        p[..., :h] = p[..., :h] + p[..., h:2 * h]
+        h //= 2
+    ms = p[..., 0] * (2.0 ** -7)
+
+    d_bits = half_nearest_sqrt(ms)
+    d = half_bits_to_float(d_bits)
+
+    # idx = number of scaled thresholds strictly below u (d*t_k is exact).
+    thr = d[..., None] * THRESHOLDS                       # (..., 15)
+    idx = (thr[..., None, :] < u[..., :, None]).sum(axis=-1).astype(np.uint8)
+
+    packed = np.empty(x.shape[:-1] + (BLOCK_BYTES,), dtype=np.uint8)
+    packed[..., 0] = (d_bits & 0xFF).astype(np.uint8)
+    packed[..., 1] = (d_bits >> 8).astype(np.uint8)
+    packed[..., 2:] = idx[..., 0::2] | (idx[..., 1::2] << 4)
+    return packed, idx, d_bits
+
+
+def unpack_blocks(packed):
+    """Inverse of the byte layout: returns (idx uint8 (..., 128), d fp64 (...))."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.shape[-1] != BLOCK_BYTES:
+        raise ValueError("last axis must be 66 bytes")
+    d_bits = packed[..., 0].astype(np.uint16) | (packed[..., 1].astype(np.uint16) << 8)
+    q = packed[..., 2:]
+    idx = np.empty(packed.shape[:-1] + (HEAD_DIM,), dtype=np.uint8)
+    idx[..., 0::2] = q & 0x0F
+    idx[..., 1::2] = q >> 4
+    return idx, half_bits_to_float(d_bits)
+
+
+def dequantize_rotated(packed):
+    """y = d * c[idx]: the block's values in the rotated domain (fp64, exact)."""
+    idx, d = unpack_blocks(packed)
+    return d[..., None] * CODEBOOK[idx]
+
+
+def dequantize_blocks(packed, seed=0):
+    """x_hat = R^T (d * c[idx]) in fp64: the block in the original domain."""
+    return unrotate(dequantize_rotated(packed), sign_vector(seed))
+
+
+# --------------------------------------------------------------------------
+# Attention on the dequantised cache (plain softmax attention, fp64)
+# --------------------------------------------------------------------------
+def _softmax_rows(s):
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attn_decode_ref(q, k_cache, v_cache, n_ctx, softmax_scale, seed=0):
+    """One decode query per (sequence, head).
+
+    q:       (B, H_q, 128) float
+    k_cache: (B, H_kv, cap, 66) uint8 packed TBQ4 blocks (same for v_cache)
+    Returns o: (B, H_q, 128) fp64.  Query head h reads KV head h // (H_q/H_kv);
+    keys 0..n_ctx-1 are attended.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            K = dequantize_blocks(k_cache[b, g, :n_ctx], seed)     # (n_ctx, 128)
+            V = dequantize_blocks(v_cache[b, g, :n_ctx], seed)
+            Q = q[b, g * G:(g + 1) * G]                            # (G, 128)
+            p = _softmax_rows(softmax_scale * (Q @ K.T))
+            out[b, g * G:(g + 1) * G] = p @ V
+    return out
+
+
+def attn_decode_rotated_ref(q, k_cache, v_cache, n_ctx, softmax_scale, seed=0):
+    """The same decode attention taken in the rotated domain:
+    q' = R q;  s_j = scale * (q' . y^K_j);  o' = sum_j p_j y^V_j;  o = R^T o'."""
+    signs = sign_vector(seed)
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            Yk = dequantize_rotated(k_cache[b, g, :n_ctx])
+            Yv = dequantize_rotated(v_cache[b, g, :n_ctx])
+            Qr = rotate(q[b, g * G:(g + 1) * G], signs)
+            p = _softmax_rows(softmax_scale * (Qr @ Yk.T))
+            out[b, g * G:(g + 1) * G] = unrotate(p @ Yv, signs)
+    return out
+
+
+def attn_decode_rows_ref(q_rows, K, V, softmax_scale):
+    """Decode attention for a few query rows against dequantised K, V (fp64):
+    q_rows (r, 128), K and V (n, 128).  Used when only some heads are checked."""
+    p = _softmax_rows(softmax_scale * (np.asarray(q_rows, np.float64) @ K.T))
+    return p @ V
+
+
+def attn_prefill_ref(q, k_cache, v_cache, n_past, softmax_scale, seed=0,
+                     rows=None, kv_heads=None):
+    """Causal prefill-chunk attention.
+
+    q: (B, n_q, H_q, 128).  Query i sits at absolute position n_past + i and
+    attends keys 0..n_past+i of its KV head (the chunk's own K/V must already
+    be in the cache).  ``rows`` optionally restricts the query indices and
+    ``kv_heads`` the KV heads that are computed (others are left NaN).
+    Returns (B, n_q, H_q, 128) fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    rows = np.arange(n_q) if rows is None else np.asarray(rows)
+    kv_heads = range(Hkv) if kv_heads is None else kv_heads
+    n_tot = n_past + n_q
+    out = np.full((B, n_q, Hq, D), np.nan)
+    for b in range(B):
+        for g in kv_heads:
+            K = dequantize_blocks(k_cache[b, g, :n_tot], seed)
+            V = dequantize_blocks(v_cache[b, g, :n_tot], seed)
+            for i in rows:
+                n_keys = n_past + int(i) + 1
+                Q = q[b, i, g * G:(g + 1) * G]                     # (G, 128)
+                p = _softmax_rows(softmax_scale * (Q @ K[:n_keys].T))
+                out[b, i, g * G:(g + 1) * G] = p @ V[:n_keys]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Split-K (flash-decoding) partials and their log-sum-exp merge.
+# --------------------------------------------------------------------------
+def split_partials(s, V, bounds):
+    """Partial softmax state per key range: for each [a, b) in ``bounds``
+    returns (m, l, acc) with m = max s, l = sum exp(s - m), acc = sum exp(s - m) V."""
+    parts = []
+    for a, b in bounds:
+        m = s[a:b].max()
+        e = np.exp(s[a:b] - m)
+        parts.append((m, e.sum(), e @ V[a:b]))
+    return parts
+
+
+def merge_partials(parts):
+    """o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p, M = max_p m_p."""
+    M = max(m for m, _, _ in parts)
+    l = sum(np.exp(m - M) * lp for m, lp, _ in parts)
+    acc = sum(np.exp(m - M) * ap for m, _, ap in parts)
+    return acc / l
