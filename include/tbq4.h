@@ -1,0 +1,167 @@
+/*
+ * tbq4.h -- C ABI of libtbq4: flash attention read directly from a TBQ4 KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the page "Kontekst 262K na jednej RTX 4090: co
+ * dodałem do llama.cpp-turboq" (trefon.com notes).
+ *   - section "Od czego zacząłem": a TBQ4 block stores 128 values in 66 bytes,
+ *     a 2-byte scale followed by 64 bytes of 4-bit indices (4.125 bits per
+ *     value); the flash-attention kernel reads raw TBQ4 blocks from global
+ *     memory and dequantises them in its inner loop; attention works in the
+ *     rotated (Hadamard) domain, so there is no separate dequantisation pass
+ *     and no F16 buffer.
+ *   - section "Konfiguracja": the K and the V cache each get their own type
+ *     (-ctk tbq4_0 -ctv tbq4_0); flash attention on; the context length is
+ *     fixed up front (-c 262144).
+ *   - section "4. Poprawność w długich sesjach": a full context must be
+ *     handled gracefully rather than crash -- here every capacity overflow is
+ *     an error code returned before anything is launched.
+ *
+ * Block format (one block = one head vector of one token, head_dim 128):
+ *   u = R x with R = H D / sqrt(128): D = diag(s), s in {+1,-1}^128 drawn from
+ *   SplitMix64(sign_seed) (bit i of the two 64-bit outputs, little endian,
+ *   set means s_i = -1), H the natural-order Sylvester Hadamard matrix.
+ *   bytes 0-1   d = binary16 nearest sqrt(mean(u_i^2)), ties to even,
+ *               saturating at 65504, little endian
+ *   bytes 2-65  4-bit indices, element 2j in the low nibble of byte 2+j and
+ *               element 2j+1 in the high nibble; idx_i = number of thresholds
+ *               t_k (midpoints of adjacent codebook levels) with d*t_k < u_i
+ *   codebook    -2.75 -2 -1.625 -1.25 -0.9375 -0.625 -0.375 -0.125
+ *               +0.125 +0.375 +0.625 +0.9375 +1.25 +1.625 +2 +2.75
+ *   Dequantised value in the rotated domain: d * c[idx]; x_hat = R^T (d c).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument named as device memory is caller-owned device
+ *     memory; the library never allocates, frees or caches device memory and
+ *     keeps no mutable global state (calls are re-entrant and thread-safe).
+ *   - All work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises.  Order appends before attention on the
+ *     same stream.
+ *   - Every argument check runs on the host before any launch; a failing
+ *     call returns a negative status and touches no memory.  A launch failure
+ *     reported by the HIP runtime returns TBQ4_ERR_HIP.
+ *   - Non-finite inputs give undefined (but memory-safe) results.
+ */
+#ifndef TBQ4_H
+#define TBQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TBQ4_HEAD_DIM 128
+#define TBQ4_BLOCK_BYTES 66
+#define TBQ4_MAX_SPLITS 1024
+
+typedef enum {
+  TBQ4_OK = 0,
+  TBQ4_ERR_INVALID_ARG = -1, /* null pointer, bad count, bad dtype, ...   */
+  TBQ4_ERR_UNSUPPORTED = -2, /* head_dim != 128, n_q_heads % n_kv_heads   */
+  TBQ4_ERR_CAPACITY = -3,    /* a token range runs past the capacity      */
+  TBQ4_ERR_ALIGNMENT = -4,   /* pointer not 16-byte aligned, capacity % 8 */
+  TBQ4_ERR_WORKSPACE = -5,   /* workspace missing or too small            */
+  TBQ4_ERR_HIP = -6          /* the HIP runtime reported a launch error   */
+} tbq4_status;
+
+typedef enum { TBQ4_F32 = 0, TBQ4_F16 = 1, TBQ4_BF16 = 2 } tbq4_dtype;
+
+/* One layer's K and V caches.
+ *   k, v        device memory, caller-owned, layout [batch][n_kv_heads]
+ *               [capacity][66] bytes each (tbq4_cache_bytes() bytes), 16-byte
+ *               aligned.  Blocks are position independent, so a caller can
+ *               checkpoint or copy any byte range.
+ *   head_dim    must be 128.
+ *   capacity    tokens per sequence; a multiple of 8 (keeps every head's
+ *               row of blocks 16-byte aligned).
+ *   sign_seed   seeds the sign vector shared by K, V, Q and the output. */
+typedef struct {
+  uint8_t *k;
+  uint8_t *v;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  uint64_t sign_seed;
+} tbq4_cache;
+
+/* Bytes of ONE of the two caches: batch * n_kv_heads * capacity * 66.
+ * Returns 0 for a negative argument. */
+size_t tbq4_cache_bytes(int32_t batch, int32_t n_kv_heads, int32_t capacity);
+
+/* Split count tbq4_attn_decode uses when given n_splits = 0 (depends only on
+ * the shapes), so callers can size the workspace.  Returns 0 on bad input. */
+int32_t tbq4_decode_auto_splits(int32_t batch, int32_t n_kv_heads, int32_t n_ctx);
+
+/* Workspace bytes tbq4_attn_decode needs for `n_splits` splits (n_splits = 0
+ * means the automatic count for these shapes):
+ * batch * n_q_heads * n_splits * 130 * 4 (fp32 max, sum and 128 partial
+ * outputs per split), rounded up to 256.  Returns 0 on bad input. */
+size_t tbq4_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                   int32_t n_ctx, int32_t n_splits);
+
+/* The 16 bytes of the sign vector for `seed` (host memory, caller-owned):
+ * the first two SplitMix64 outputs, little endian. */
+tbq4_status tbq4_sign_vector(uint64_t seed, uint8_t out_bits[16]);
+
+/* Quantise and append new K and V rows (the write side of the cache).
+ *   k_new, v_new  device, [batch][n_new][n_kv_heads][128] in src_dtype,
+ *                 16-byte aligned.
+ *   Writes the blocks of token slots [pos, pos + n_new) of every sequence of
+ *   both caches; other slots are untouched.  pos >= 0 and pos + n_new <=
+ *   capacity, else TBQ4_ERR_CAPACITY.  n_new = 0 is a no-op.
+ *   The packed bytes are a pure function of the input values and sign_seed
+ *   (fp64 arithmetic throughout). */
+tbq4_status tbq4_quantize_append(const tbq4_cache *cache, const void *k_new,
+                                 const void *v_new, tbq4_dtype src_dtype,
+                                 int32_t pos, int32_t n_new, void *hip_stream);
+
+/* Quantise a flat array of n_blocks blocks of 128 values (device, src_dtype)
+ * into n_blocks * 66 bytes at `out` (device).  Same arithmetic as
+ * tbq4_quantize_append; for callers that keep their own cache layout. */
+tbq4_status tbq4_quantize_blocks(const void *x, tbq4_dtype src_dtype, int64_t n_blocks,
+                                 uint64_t sign_seed, uint8_t *out, void *hip_stream);
+
+/* Decode attention: one query per (sequence, query head) against cached
+ * slots [0, n_ctx) of its KV head (kv head = h / (n_q_heads / n_kv_heads)).
+ *   q            device, [batch][n_q_heads][128], q_dtype (F32 or F16)
+ *   out          device, [batch][n_q_heads][128], out_dtype (F16 or F32)
+ *   softmax_scale multiplies q.k before the softmax
+ *   n_splits     split-K partition count in [1, 1024], or 0 for automatic
+ *   workspace    device, >= tbq4_decode_workspace_bytes(...) bytes, 16-byte
+ *                aligned; scratch for the per-split partial softmax states.
+ * Errors: 1 <= n_ctx <= capacity else TBQ4_ERR_CAPACITY; n_q_heads a positive
+ * multiple of n_kv_heads with n_q_heads / n_kv_heads <= 16, else
+ * TBQ4_ERR_UNSUPPORTED. */
+tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                             int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
+                             void *out, tbq4_dtype out_dtype, int32_t n_splits,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Prefill-chunk attention: n_q new queries per sequence; query i sits at
+ * absolute position n_past + i and attends slots [0, n_past + i] (causal
+ * inside the chunk, full over the cached prefix).  Slots [n_past, n_past +
+ * n_q) must already hold the chunk's own K/V (tbq4_quantize_append first).
+ *   q, out   device, [batch][n_q][n_q_heads][128]; q_dtype F32 or F16,
+ *            out_dtype F16 or F32.
+ * Errors: n_past >= 0, n_q >= 1, n_past + n_q <= capacity else
+ * TBQ4_ERR_CAPACITY; n_q_heads / n_kv_heads must be 8, else
+ * TBQ4_ERR_UNSUPPORTED. */
+tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                    int32_t n_q_heads, int32_t n_past, int32_t n_q,
+                                    float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                    void *hip_stream);
+
+/* Static description of a status code. */
+const char *tbq4_status_str(tbq4_status s);
+
+/* Library version as "major.minor.patch". */
+const char *tbq4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TBQ4_H */

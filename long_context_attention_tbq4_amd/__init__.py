@@ -1,0 +1,173 @@
+"""TBQ4 fused long-context attention for AMD Instinct MI355X (gfx950).
+
+Python binding of libtbq4.so: argument marshalling only.  Every step of the
+hot path -- quantise-append, split-K decode attention, prefill-chunk
+attention -- runs in the library's HIP kernels; torch supplies device memory
+and the current stream.
+
+Method: page "Kontekst 262K na jednej RTX 4090: co dodałem do
+llama.cpp-turboq", section "Od czego zacząłem" -- flash attention reads raw
+TBQ4 blocks (128 values in 66 bytes: 2-byte scale + 64 bytes of 4-bit
+indices) and dequantises them in its inner loop, in the rotated Hadamard
+domain, with no dequantisation pass and no F16 buffer.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS
+
+__all__ = [
+    "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
+    "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
+    "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
+]
+
+_DT = {torch.float32: _lib.F32, torch.float16: _lib.F16, torch.bfloat16: _lib.BF16}
+
+
+class TBQ4Error(RuntimeError):
+    def __init__(self, status, what):
+        msg = _lib.lib().tbq4_status_str(status).decode()
+        super().__init__(f"{what}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status, what):
+    if status != _lib.OK:
+        raise TBQ4Error(status, what)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t):
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _require(t, name, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class KVCache:
+    """One layer's TBQ4 K and V caches: uint8 device tensors of shape
+    [batch][n_kv_heads][capacity][66] (head-major rows of 66-byte blocks)."""
+
+    def __init__(self, batch, n_kv_heads, capacity, sign_seed=0, device="cuda"):
+        if capacity % 8:
+            raise ValueError("capacity must be a multiple of 8")
+        shape = (batch, n_kv_heads, capacity, BLOCK_BYTES)
+        self.k = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.v = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
+        self.sign_seed = sign_seed
+
+    @property
+    def device(self):
+        return self.k.device
+
+    def descriptor(self):
+        return _lib.Cache(self.k.data_ptr(), self.v.data_ptr(), self.batch, self.n_kv_heads,
+                          HEAD_DIM, self.capacity, self.sign_seed)
+
+
+def quantize_append(cache, k_new, v_new, pos):
+    """Quantise k_new, v_new ([batch][n_new][n_kv_heads][128], fp32/fp16/bf16)
+    into token slots [pos, pos + n_new) of every sequence."""
+    _require(k_new, "k_new")
+    _require(v_new, "v_new", k_new.shape)
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    B, n_new, H, D = k_new.shape
+    if (B, H, D) != (cache.batch, cache.n_kv_heads, HEAD_DIM):
+        raise ValueError("k_new shape does not match the cache")
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_quantize_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new),
+                                           _dtype(k_new), pos, n_new, _stream(cache.device)),
+           "tbq4_quantize_append")
+
+
+def quantize_blocks(x, sign_seed=0, out=None):
+    """Quantise a contiguous (..., 128) tensor into (..., 66) uint8 blocks."""
+    _require(x, "x")
+    if x.shape[-1] != HEAD_DIM:
+        raise ValueError("last dimension must be 128")
+    n = x.numel() // HEAD_DIM
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (BLOCK_BYTES,), dtype=torch.uint8, device=x.device)
+    _require(out, "out", tuple(x.shape[:-1]) + (BLOCK_BYTES,))
+    _check(_lib.lib().tbq4_quantize_blocks(_ptr(x), _dtype(x), n, sign_seed, _ptr(out),
+                                           _stream(x.device)), "tbq4_quantize_blocks")
+    return out
+
+
+def decode_auto_splits(batch, n_kv_heads, n_ctx):
+    return _lib.lib().tbq4_decode_auto_splits(batch, n_kv_heads, n_ctx)
+
+
+def decode_workspace_bytes(batch, n_kv_heads, n_q_heads, n_ctx, n_splits=0):
+    return _lib.lib().tbq4_decode_workspace_bytes(batch, n_kv_heads, n_q_heads, n_ctx, n_splits)
+
+
+def attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None, out_dtype=torch.float16,
+                workspace=None):
+    """Decode attention of q ([batch][n_q_heads][128], fp32/fp16) against
+    cached slots [0, n_ctx).  Returns out ([batch][n_q_heads][128])."""
+    _require(q, "q")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, Hq, D))
+    need = decode_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, n_ctx, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_attn_decode(ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx,
+                                       float(softmax_scale), _ptr(out), _dtype(out), n_splits,
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(q.device)), "tbq4_attn_decode")
+    return out
+
+
+def attn_prefill_chunk(cache, q, n_past, softmax_scale, out=None, out_dtype=torch.float16):
+    """Causal prefill-chunk attention of q ([batch][n_q][n_q_heads][128]):
+    query i attends slots [0, n_past + i]."""
+    _require(q, "q")
+    B, n_q, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, n_q, Hq, D))
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_attn_prefill_chunk(ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_past,
+                                              n_q, float(softmax_scale), _ptr(out), _dtype(out),
+                                              _stream(q.device)), "tbq4_attn_prefill_chunk")
+    return out
+
+
+def sign_vector(seed):
+    """The 16 sign bytes for ``seed`` (bit i set means s_i = -1)."""
+    buf = (ctypes.c_uint8 * 16)()
+    _check(_lib.lib().tbq4_sign_vector(seed, buf), "tbq4_sign_vector")
+    return bytes(buf)
+
+
+def cache_bytes(batch, n_kv_heads, capacity):
+    return _lib.lib().tbq4_cache_bytes(batch, n_kv_heads, capacity)
+
+
+def version():
+    return _lib.lib().tbq4_version().decode()

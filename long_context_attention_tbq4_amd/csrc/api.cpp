@@ -1,0 +1,243 @@
+// C ABI of libtbq4 (declared in include/tbq4.h): argument checks on the host,
+// then kernel launches on the caller's stream.  No device memory is allocated
+// here and no call synchronises.
+//
+// Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq":
+// section "Konfiguracja" (K and V caches typed separately, context fixed up
+// front) and section "4. Poprawność w długich sesjach" (a full context must be
+// handled gracefully instead of crashing): every shape, capacity and pointer
+// problem is a negative status returned before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "../../include/tbq4.h"
+#include "tbq4_launch.h"
+
+namespace {
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): state += golden gamma,
+// then two xor-shift-multiply rounds and a final xor-shift.
+uint64_t splitmix64_next(uint64_t &state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+void sign_words(uint64_t seed, uint32_t out[4]) {
+  uint64_t st = seed;
+  const uint64_t w0 = splitmix64_next(st);
+  const uint64_t w1 = splitmix64_next(st);
+  out[0] = (uint32_t)w0;
+  out[1] = (uint32_t)(w0 >> 32);
+  out[2] = (uint32_t)w1;
+  out[3] = (uint32_t)(w1 >> 32);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+tbq4_status check_cache(const tbq4_cache *c) {
+  if (!c) return TBQ4_ERR_INVALID_ARG;
+  if (!c->k || !c->v) return TBQ4_ERR_INVALID_ARG;
+  if (c->batch <= 0 || c->n_kv_heads <= 0 || c->capacity <= 0) return TBQ4_ERR_INVALID_ARG;
+  if (c->head_dim != TBQ4_HEAD_DIM) return TBQ4_ERR_UNSUPPORTED;
+  if (c->capacity % 8 != 0) return TBQ4_ERR_ALIGNMENT;
+  // one (sequence, head) row must stay addressable with 32-bit offsets
+  if ((int64_t)c->capacity * TBQ4_BLOCK_BYTES > 0x7FFFFFF0ll) return TBQ4_ERR_UNSUPPORTED;
+  if (!aligned16(c->k) || !aligned16(c->v)) return TBQ4_ERR_ALIGNMENT;
+  return TBQ4_OK;
+}
+
+bool valid_dtype(int d) { return d == TBQ4_F32 || d == TBQ4_F16 || d == TBQ4_BF16; }
+
+tbq4_status from_hip(hipError_t e) { return e == hipSuccess ? TBQ4_OK : TBQ4_ERR_HIP; }
+
+int32_t auto_splits(int32_t batch, int32_t n_kv_heads, int32_t n_ctx) {
+  // enough wavefronts for ~8 per compute unit on a 256-CU part, but never
+  // fewer than 4 tiles per split
+  const int64_t n_tiles = (n_ctx + tbq4::kDecodeTile - 1) / tbq4::kDecodeTile;
+  const int64_t rows = (int64_t)batch * n_kv_heads;
+  int64_t p = (2048 + rows - 1) / rows;
+  const int64_t max_by_len = (n_tiles + 3) / 4;
+  if (p > max_by_len) p = max_by_len;
+  if (p < 1) p = 1;
+  if (p > TBQ4_MAX_SPLITS) p = TBQ4_MAX_SPLITS;
+  return (int32_t)p;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+size_t tbq4_cache_bytes(int32_t batch, int32_t n_kv_heads, int32_t capacity) {
+  if (batch < 0 || n_kv_heads < 0 || capacity < 0) return 0;
+  return (size_t)batch * (size_t)n_kv_heads * (size_t)capacity * TBQ4_BLOCK_BYTES;
+}
+
+int32_t tbq4_decode_auto_splits(int32_t batch, int32_t n_kv_heads, int32_t n_ctx) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_ctx <= 0) return 0;
+  return auto_splits(batch, n_kv_heads, n_ctx);
+}
+
+size_t tbq4_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                   int32_t n_ctx, int32_t n_splits) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_ctx <= 0) return 0;
+  if (n_splits < 0 || n_splits > TBQ4_MAX_SPLITS) return 0;
+  const int32_t p = n_splits == 0 ? auto_splits(batch, n_kv_heads, n_ctx) : n_splits;
+  return round256((size_t)batch * n_q_heads * p * 130 * sizeof(float));
+}
+
+tbq4_status tbq4_sign_vector(uint64_t seed, uint8_t out_bits[16]) {
+  if (!out_bits) return TBQ4_ERR_INVALID_ARG;
+  uint32_t w[4];
+  sign_words(seed, w);
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) out_bits[4 * i + j] = (uint8_t)(w[i] >> (8 * j));
+  return TBQ4_OK;
+}
+
+tbq4_status tbq4_quantize_append(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                                 tbq4_dtype src_dtype, int32_t pos, int32_t n_new,
+                                 void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  if (!valid_dtype(src_dtype)) return TBQ4_ERR_INVALID_ARG;
+  if (n_new < 0 || pos < 0) return TBQ4_ERR_INVALID_ARG;
+  if ((int64_t)pos + n_new > cache->capacity) return TBQ4_ERR_CAPACITY;
+  if (n_new == 0) return TBQ4_OK;
+  if (!k_new || !v_new) return TBQ4_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TBQ4_ERR_ALIGNMENT;
+  tbq4::QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.dst[0] = cache->k;
+  a.dst[1] = cache->v;
+  a.blocks_per_tensor = (int64_t)cache->batch * n_new * cache->n_kv_heads;
+  a.n_new = n_new;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.capacity = cache->capacity;
+  a.pos = pos;
+  a.flat = 0;
+  uint32_t w[4];
+  sign_words(cache->sign_seed, w);
+  a.sign_lo = w[0]; a.sign_hi = w[1]; a.sign_lo2 = w[2]; a.sign_hi2 = w[3];
+  return from_hip(tbq4::launch_quantize(a, (int)src_dtype, 2, (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_quantize_blocks(const void *x, tbq4_dtype src_dtype, int64_t n_blocks,
+                                 uint64_t sign_seed, uint8_t *out, void *hip_stream) {
+  if (!valid_dtype(src_dtype)) return TBQ4_ERR_INVALID_ARG;
+  if (n_blocks < 0) return TBQ4_ERR_INVALID_ARG;
+  if (n_blocks == 0) return TBQ4_OK;
+  if (!x || !out) return TBQ4_ERR_INVALID_ARG;
+  if (n_blocks > ((int64_t)1 << 36)) return TBQ4_ERR_UNSUPPORTED;
+  tbq4::QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src[0] = x;
+  a.dst[0] = out;
+  a.blocks_per_tensor = n_blocks;
+  a.flat = 1;
+  uint32_t w[4];
+  sign_words(sign_seed, w);
+  a.sign_lo = w[0]; a.sign_hi = w[1]; a.sign_lo2 = w[2]; a.sign_hi2 = w[3];
+  return from_hip(tbq4::launch_quantize(a, (int)src_dtype, 1, (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                             int32_t n_q_heads, int32_t n_ctx, float softmax_scale, void *out,
+                             tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                             size_t workspace_bytes, void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  if (!q || !out) return TBQ4_ERR_INVALID_ARG;
+  if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;
+  const int32_t G = n_q_heads / cache->n_kv_heads;
+  if (G > 8) return TBQ4_ERR_UNSUPPORTED;
+  if (n_ctx < 1 || n_ctx > cache->capacity) return TBQ4_ERR_CAPACITY;
+  if (n_splits < 0 || n_splits > TBQ4_MAX_SPLITS) return TBQ4_ERR_INVALID_ARG;
+  if (cache->batch > 65535 || cache->n_kv_heads > 65535) return TBQ4_ERR_UNSUPPORTED;
+  const int32_t P = n_splits == 0 ? auto_splits(cache->batch, cache->n_kv_heads, n_ctx) : n_splits;
+  const size_t need = tbq4_decode_workspace_bytes(cache->batch, cache->n_kv_heads, n_q_heads,
+                                                  n_ctx, P);
+  if (!workspace || workspace_bytes < need) return TBQ4_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(q) || !aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+
+  tbq4::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = cache->k;
+  a.v = cache->v;
+  a.q = q;
+  a.ws = (float *)workspace;
+  a.out = out;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group = G;
+  a.capacity = cache->capacity;
+  a.n_ctx = n_ctx;
+  a.n_splits = P;
+  const int32_t n_tiles = (n_ctx + tbq4::kDecodeTile - 1) / tbq4::kDecodeTile;
+  a.tiles_per_split = (n_tiles + P - 1) / P;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  sign_words(cache->sign_seed, a.sign);
+  return from_hip(tbq4::launch_decode(a, cache->batch, (int)q_dtype, (int)out_dtype,
+                                      (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                    int32_t n_q_heads, int32_t n_past, int32_t n_q,
+                                    float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                    void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  if (!q || !out) return TBQ4_ERR_INVALID_ARG;
+  if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;
+  const int32_t G = n_q_heads / cache->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16 && G != 32) return TBQ4_ERR_UNSUPPORTED;
+  if (n_past < 0 || n_q < 1) return TBQ4_ERR_CAPACITY;
+  if ((int64_t)n_past + n_q > cache->capacity) return TBQ4_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  tbq4::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = cache->k;
+  a.v = cache->v;
+  a.q = q;
+  a.out = out;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group = G;
+  a.capacity = cache->capacity;
+  a.n_past = n_past;
+  a.n_q = n_q;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  sign_words(cache->sign_seed, a.sign);
+  return from_hip(tbq4::launch_prefill(a, cache->batch, (int)q_dtype, (int)out_dtype,
+                                       (hipStream_t)hip_stream));
+}
+
+const char *tbq4_status_str(tbq4_status s) {
+  switch (s) {
+    case TBQ4_OK: return "ok";
+    case TBQ4_ERR_INVALID_ARG: return "invalid argument";
+    case TBQ4_ERR_UNSUPPORTED: return "unsupported shape";
+    case TBQ4_ERR_CAPACITY: return "token range exceeds cache capacity";
+    case TBQ4_ERR_ALIGNMENT: return "pointer or capacity not aligned";
+    case TBQ4_ERR_WORKSPACE: return "workspace missing or too small";
+    case TBQ4_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char *tbq4_version(void) { return "0.1.0"; }
+
+}  // extern "C"

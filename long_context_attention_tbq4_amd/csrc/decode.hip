@@ -1,0 +1,346 @@
+// TBQ4 split-K decode attention for gfx950.
+//
+// Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+// section "Od czego zacząłem": the flash-attention kernel reads raw TBQ4
+// blocks from global memory and dequantises them in its inner loop, in the
+// rotated (Hadamard) domain, so there is no dequantisation pass and no F16
+// buffer.  Rotated-domain attention: q' = R q, s_j = scale d^K_j (q' . c^K_j),
+// o' = sum_j p_j d^V_j c^V_j, o = R^T o' (R orthogonal).
+//
+// Work split (flash decoding): one wavefront per (sequence, KV head, split)
+// streams a contiguous run of 64-token tiles and writes a partial softmax
+// state (m, l, o'[128]) for each of the G query heads of that KV head; a
+// second kernel merges the splits, normalises, applies R^T and stores.
+//
+// Per 64-token tile a wavefront
+//   * fetches 4 x 16 tokens of K and V with 16-byte-per-lane buffer loads
+//     (lane = token x 32-dimension quarter; a 16-token group is one
+//     contiguous 1056-byte run, so every fetched line is fully used),
+//   * S^T = K Q'^T on v_mfma_f32_16x16x32_f16: K nibbles go straight from
+//     registers to fp16 operands (byte-permute LUT -> e4m3 -> fp16); the 16
+//     MFMA columns hold the G <= 8 query heads twice, as an fp16 high part
+//     and the fp16 residual, so the scores carry ~22 bits of q,
+//   * stages the V index bytes in LDS and reads them back transposed with
+//     ds_read_b64_tr_b8 (8 tokens x 1 byte per lane), dequantises them the
+//     same way and runs O'^T += P~ V on MFMA, with P~ = p d^V again split
+//     into fp16 high and residual rows,
+//   * keeps the online-softmax state in the log2 domain.
+#include "tbq4_device.h"
+#include "tbq4_launch.h"
+
+namespace tbq4 {
+
+constexpr int kTile = kDecodeTile;  // tokens per loop iteration
+constexpr int kVRow = 80;        // LDS bytes per staged V row (64 + pad)
+
+
+__device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+
+// 16-lane row rotation by 8: lane j receives lane (j + 8) mod 16 of its row.
+__device__ __forceinline__ float row_ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            0x128, 0xF, 0xF, false));
+}
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT *p);
+template <> __device__ __forceinline__ float load_q<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_q<_Float16>(const _Float16 *p) { return (float)*p; }
+
+template <typename QT>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[kTile];
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int quarter = lane >> 4;       // 32-dimension quarter / token sub-group
+  const int col = lane & 15;           // MFMA column: query head (col & 7), part col >> 3
+  const int head = col & 7;
+  const bool lo_part = col >= 8;
+
+  // ---------------- q' = R q * scale * log2(e), split into fp16 hi + residual
+  float qv[32];
+  {
+    const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim +
+                   quarter * 32;
+    const uint32_t sw = a.sign[quarter];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float x = head < G ? load_q<QT>(qp + i) : 0.0f;
+      qv[i] = ((sw >> i) & 1u) ? -x : x;
+    }
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & h) == 0) {
+          const float x = qv[i], y = qv[i + h];
+          qv[i] = x + y;
+          qv[i + h] = x - y;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 16; h <= 32; h <<= 1) {   // dims 32 and 64 apart: lanes 16 / 32 apart
+      const bool upper = (lane & h) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float o = __shfl_xor(qv[i], h, 64);
+        qv[i] = upper ? (o - qv[i]) : (qv[i] + o);
+      }
+    }
+  }
+  const float f = 0.08838834764831845f * a.qscale;
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    qv[i] *= f;
+    mx = fmaxf(mx, fabsf(qv[i]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // power-of-two normalisation: max |q| in [2^13, 2^14) keeps hi and
+  // residual well inside the fp16 range
+  int ex = 0;
+  if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
+  ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+  const float qs_inv = ldexpf(1.0f, -ex);
+  half8 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int el = 0; el < 8; ++el) {
+      const int i = 8 * c + (el < 4 ? 2 * el : 2 * el - 7);
+      const float x = ldexpf(qv[i], ex);
+      const _Float16 hi = (_Float16)x;
+      const _Float16 lo = (_Float16)(x - (float)hi);
+      qop[c][el] = lo_part ? lo : hi;
+    }
+  }
+
+  // ---------------- token range of this split
+  const int n_tiles = (a.n_ctx + kTile - 1) / kTile;
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(t_begin + a.tiles_per_split, n_tiles);
+
+  const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
+  const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
+  const rsrc_t rk = make_rsrc(a.k + row, row_bytes);
+  const rsrc_t rv = make_rsrc(a.v + row, row_bytes);
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4v o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // transposed-read source addresses (fixed per lane): lane s of 16-lane group
+  // G4 points at token tau(G4, s/2), byte 8*(s&1) of a 16-byte column group
+  int tr_off[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int e = col >> 1;
+    const int tok = 32 * kk + 16 * (e >> 2) + 4 * quarter + (e & 3);
+    tr_off[kk] = tok * kVRow + 8 * (col & 1);
+  }
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int tok0 = t * kTile;
+    // ---- fetch
+    uint32_t kw[4][4], vw[4][4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const uint32_t start = (uint32_t)(tok0 + 16 * blk + col) * kBlockBytes + 2 + 16 * quarter;
+      load16_unaligned(rk, start, kw[blk]);
+      load16_unaligned(rv, start, vw[blk]);
+    }
+    const uint16_t skv = buf_load_u16(rk, (uint32_t)(tok0 + lane) * kBlockBytes);
+    const uint16_t svv = buf_load_u16(rv, (uint32_t)(tok0 + lane) * kBlockBytes);
+
+    __syncthreads();   // previous tile's LDS reads are done
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      u32x4 w = {vw[blk][0], vw[blk][1], vw[blk][2], vw[blk][3]};
+      *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = w;
+    }
+    sk[lane] = skv;
+    sv[lane] = svv;
+
+    // ---- scores S^T[token][col] = K . q'
+    float s[4][4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(word_to_half8(kw[blk][c]), qop[c], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[blk][e] = acc[e] + row_ror8(acc[e]);
+    }
+    __syncthreads();   // staged V rows and scales are visible
+
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int tl = 16 * blk + 4 * quarter;
+      const uint2 kd = *(const uint2 *)(sk + tl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hb = (e < 2 ? kd.x : kd.y) >> (16 * (e & 1));
+        const float dk = half_bits_to_float(hb & 0xFFFF);
+        const bool valid = tok0 + tl + e < a.n_ctx;
+        const float x = valid ? s[blk][e] * (dk * qs_inv) : -INFINITY;
+        s[blk][e] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+
+    // rescale the accumulators when some head's running max moved
+    if (__any(alpha != 1.0f)) {
+      float al[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, (4 * quarter + e) & 7, 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[i][e] *= al[e];
+    }
+
+    // ---- probabilities, folded V scale, fp16 hi / residual operands
+    float psum = 0.0f;
+    half8 pa[2];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int tl = 16 * blk + 4 * quarter;
+      const uint2 vd = *(const uint2 *)(sv + tl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = exp2f(s[blk][e] - m_new);
+        psum += p;
+        const uint32_t hb = (e < 2 ? vd.x : vd.y) >> (16 * (e & 1));
+        const float pt = p * half_bits_to_float(hb & 0xFFFF);
+        const _Float16 hi = (_Float16)pt;
+        const _Float16 lo = (_Float16)(pt - (float)hi);
+        pa[blk >> 1][4 * (blk & 1) + e] = lo_part ? lo : hi;
+      }
+    }
+    l_run = l_run * alpha + psum;
+
+    // ---- O'^T += P~ V  (V read back transposed: 8 tokens x 1 byte per lane)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        typedef __attribute__((address_space(3))) int2v lds_i2;
+        const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i2 *)(vlds + tr_off[kk] + 16 * cg));
+        const uint32_t w0 = (uint32_t)r[0], w1 = (uint32_t)r[1];
+        const half8 ve = lo_nibbles_to_half8(w0, w1);
+        const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
+        o[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], ve, o[2 * cg], 0, 0, 0);
+        o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---------------- partial state of this split
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[i][e] += __shfl_xor(o[i][e], 32, 64);
+
+  const int P = a.n_splits;
+  float *wsb = a.ws + ((size_t)b * a.n_q_heads + (size_t)g * G) * P * 130 + (size_t)split * 130;
+  if (lane < G) {
+    wsb[(size_t)lane * P * 130 + 0] = m_run;
+    wsb[(size_t)lane * P * 130 + 1] = l_run;
+  }
+  if (lane < 32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * quarter + e;   // query head within the group
+      if (r < G) {
+        float *dst = wsb + (size_t)r * P * 130 + 2;
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) {
+          dst[32 * cg + 2 * col] = o[2 * cg][e];
+          dst[32 * cg + 2 * col + 1] = o[2 * cg + 1][e];
+        }
+      }
+    }
+  }
+}
+
+// Merge: o = R^T (sum_p 2^(m_p - M) o'_p / sum_p 2^(m_p - M) l_p), one
+// wavefront per (sequence, query head); lane holds dims lane and lane + 64.
+template <typename OT>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int P = a.n_splits;
+  const float *base = a.ws + ((size_t)b * a.n_q_heads + h) * P * 130;
+  float M = -INFINITY;
+  for (int p = lane; p < P; p += 64) M = fmaxf(M, base[(size_t)p * 130]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int p = 0; p < P; ++p) {
+    const float* bp = base + (size_t)p * 130;
+    const float w = exp2f(bp[0] - M);
+    L += w * bp[1];
+    o0 += w * bp[2 + lane];
+    o1 += w * bp[2 + 64 + lane];
+  }
+  const float inv = 1.0f / L;
+  o0 *= inv;
+  o1 *= inv;
+  // o = s * (H o') / sqrt(128)
+#pragma unroll
+  for (int hh = 1; hh < 64; hh <<= 1) {
+    const float p0 = __shfl_xor(o0, hh, 64), p1 = __shfl_xor(o1, hh, 64);
+    const bool upper = (lane & hh) != 0;
+    o0 = upper ? (p0 - o0) : (o0 + p0);
+    o1 = upper ? (p1 - o1) : (o1 + p1);
+  }
+  {
+    const float x = o0, y = o1;
+    o0 = x + y;
+    o1 = x - y;
+  }
+  const float r = 0.08838834764831845f;
+  const bool n0 = (a.sign[lane >> 5] >> (lane & 31)) & 1u;
+  const bool n1 = (a.sign[2 + (lane >> 5)] >> (lane & 31)) & 1u;
+  o0 = n0 ? -o0 * r : o0 * r;
+  o1 = n1 ? -o1 * r : o1 * r;
+  OT *dst = (OT *)a.out + ((size_t)b * a.n_q_heads + h) * kHeadDim;
+  dst[lane] = (OT)o0;
+  dst[lane + 64] = (OT)o1;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, int batch, int q_dtype, int out_dtype,
+                         hipStream_t stream) {
+  dim3 g1(a.n_splits, a.n_kv_heads, batch);
+  if (q_dtype == 0)
+    hipLaunchKernelGGL(decode_split_kernel<float>, g1, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<_Float16>, g1, dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(a.n_q_heads, batch);
+  if (out_dtype == 0)
+    hipLaunchKernelGGL(decode_merge_kernel<float>, g2, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<_Float16>, g2, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tbq4

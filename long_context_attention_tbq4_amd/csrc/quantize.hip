@@ -1,0 +1,169 @@
+// TBQ4 quantise-and-pack kernel (the write side of the cache).
+//
+// Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+// section "Od czego zacząłem": a block is 128 values stored in 66 bytes, a
+// 2-byte scale then 64 bytes of 4-bit indices, in the rotated Hadamard domain.
+// The page does not describe how blocks are written; this kernel fixes every
+// step as an IEEE fp64 operation in a stated order so that the bytes are a
+// pure function of the input (bit-exact against an independent fp64
+// implementation of the same steps):
+//   v = s * x                           (s = +-1 from SplitMix64(seed))
+//   butterflies h = 1,2,...,64:  (v_i, v_{i+h}) <- (v_i + v_{i+h}, v_i - v_{i+h})
+//   u = v * fl64(1/sqrt(128))
+//   p = u*u; tree p_i += p_{i+h} for h = 64..1; ms = p_0 * 2^-7
+//   d = binary16 nearest sqrt(ms) (exact comparison with squared midpoints,
+//       ties to even, saturating at 65504)
+//   idx_i = #{k : d * t_k < u_i}, t_k midpoints of adjacent codebook levels
+//   bytes: d (LE) then idx_{2j} | idx_{2j+1} << 4
+//
+// One wavefront quantises one block: lane l holds elements l and l+64.
+#include "tbq4_device.h"
+#include "tbq4_launch.h"
+
+namespace tbq4 {
+
+#pragma clang fp contract(off)
+
+// fl64(1/sqrt(128)) = 0x1.6a09e667f3bccp-4
+__device__ __forceinline__ double inv_sqrt128() { return __longlong_as_double(0x3FB6A09E667F3BCCll); }
+
+// exact value of binary16 pattern h (0 <= h <= 0x7C00)
+__device__ __forceinline__ double half_value(int h) {
+  const int e = h >> 10, m = h & 0x3FF;
+  return e == 0 ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+}
+
+// Pattern of the binary16 value nearest sqrt(ms): the largest h in
+// [0, 0x7BFF] whose lower midpoint mid(h) = (value(h-1)+value(h))/2 lies
+// below sqrt(ms) -- or equals it with h even.  mid(h) has <= 12 significant
+// bits, so mid(h)^2 is exact and the test never takes a square root.
+__device__ __forceinline__ int half_round_sqrt(double ms) {
+  int lo = 0, hi = 0x7BFF;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const double m = (half_value(mid - 1) + half_value(mid)) * 0.5;
+    const double m2 = m * m;
+    const bool ok = (m2 < ms) || (m2 == ms && (mid & 1) == 0);
+    if (ok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T> __device__ __forceinline__ double load_exact(const T *p);
+template <> __device__ __forceinline__ double load_exact<float>(const float *p) { return (double)*p; }
+template <> __device__ __forceinline__ double load_exact<_Float16>(const _Float16 *p) { return (double)*p; }
+template <> __device__ __forceinline__ double load_exact<uint16_t>(const uint16_t *p) {
+  // bf16: the upper half of an fp32
+  return (double)__uint_as_float(((uint32_t)*p) << 16);
+}
+
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gblock = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int tensor = gblock >= a.blocks_per_tensor ? 1 : 0;
+  const int64_t i = gblock - (int64_t)tensor * a.blocks_per_tensor;
+  if (tensor == 1 && a.flat) return;
+  if (i >= a.blocks_per_tensor) return;
+
+  const T *src;
+  uint8_t *dst;
+  if (a.flat) {
+    src = (const T *)a.src[0] + i * kHeadDim;
+    dst = a.dst[0] + i * kBlockBytes;
+  } else {
+    // source [batch][n_new][n_kv_heads][128]; cache [batch][n_kv_heads][capacity][66]
+    const int64_t h = i % a.n_kv_heads;
+    const int64_t t = (i / a.n_kv_heads) % a.n_new;
+    const int64_t b = i / ((int64_t)a.n_kv_heads * a.n_new);
+    src = (const T *)a.src[tensor] + i * kHeadDim;
+    dst = a.dst[tensor] + ((b * a.n_kv_heads + h) * a.capacity + a.pos + t) * kBlockBytes;
+  }
+
+  // signs of elements lane and lane+64
+  const uint32_t w_a = lane < 32 ? a.sign_lo : a.sign_hi;
+  const uint32_t w_b = lane < 32 ? a.sign_lo2 : a.sign_hi2;
+  const bool neg0 = (w_a >> (lane & 31)) & 1u;
+  const bool neg1 = (w_b >> (lane & 31)) & 1u;
+  double v0 = load_exact<T>(src + lane);
+  double v1 = load_exact<T>(src + lane + 64);
+  if (neg0) v0 = -v0;
+  if (neg1) v1 = -v1;
+
+  // butterflies h = 1..32 across lanes, then h = 64 inside the lane
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const double p0 = __shfl_xor(v0, h, 64);
+    const double p1 = __shfl_xor(v1, h, 64);
+    const bool upper = (lane & h) != 0;
+    v0 = upper ? (p0 - v0) : (v0 + p0);
+    v1 = upper ? (p1 - v1) : (v1 + p1);
+  }
+  {
+    const double a0 = v0, b0 = v1;
+    v0 = a0 + b0;
+    v1 = a0 - b0;
+  }
+  const double R = inv_sqrt128();
+  const double u0 = v0 * R;
+  const double u1 = v1 * R;
+
+  // mean square: p_l = u_l^2 + u_{l+64}^2, then p_l += p_{l+h}, h = 32..1
+  const double q0 = u0 * u0;
+  const double q1 = u1 * u1;
+  double p = q0 + q1;
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const double o = __shfl_down(p, h, 64);
+    p = p + o;
+  }
+  const double S = __shfl(p, 0, 64);
+  const double ms = S * 0x1p-7;
+  const int dbits = half_round_sqrt(ms);
+  const double d = half_value(dbits);
+
+  // idx = number of scaled thresholds strictly below u
+  const double thr[15] = {-2.375, -1.8125, -1.4375, -1.09375, -0.78125, -0.5, -0.25, 0.0,
+                          0.25, 0.5, 0.78125, 1.09375, 1.4375, 1.8125, 2.375};
+  int i0 = 0, i1 = 0;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    const double dt = d * thr[k];
+    i0 += dt < u0 ? 1 : 0;
+    i1 += dt < u1 ? 1 : 0;
+  }
+
+  // byte m = idx[2m] | idx[2m+1] << 4; elements 2m, 2m+1 live in lanes
+  // (2m)&63 and (2m+1)&63, first element for m < 32, second for m >= 32
+  const int both = i0 | (i1 << 8);
+  const int srcl = (2 * lane) & 63;
+  const int e_a = __shfl(both, srcl, 64);
+  const int e_b = __shfl(both, srcl + 1, 64);
+  const int sh = lane < 32 ? 0 : 8;
+  const uint32_t byte = (uint32_t)(((e_a >> sh) & 15) | (((e_b >> sh) & 15) << 4));
+  const uint32_t next = (uint32_t)__shfl_down((int)byte, 1, 64);
+  if ((lane & 1) == 0) {
+    *(uint16_t *)(dst + 2 + lane) = (uint16_t)(byte | (next << 8));
+  }
+  if (lane == 0) *(uint16_t *)dst = (uint16_t)dbits;
+}
+
+template __global__ void quantize_kernel<float>(QuantArgs);
+template __global__ void quantize_kernel<_Float16>(QuantArgs);
+template __global__ void quantize_kernel<uint16_t>(QuantArgs);
+
+hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream) {
+  const int64_t blocks = a.blocks_per_tensor * tensors;
+  const int64_t grid = (blocks + 3) / 4;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(quantize_kernel<float>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(quantize_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tbq4

@@ -1,0 +1,138 @@
+// Device-side helpers shared by the TBQ4 kernels (gfx950 / CDNA4 only).
+//
+// Block format (page "Kontekst 262K na jednej RTX 4090: co dodałem do
+// llama.cpp-turboq", section "Od czego zacząłem"): 128 values -> 66 bytes, a
+// binary16 scale d followed by 64 bytes of 4-bit indices (element 2j in the
+// low nibble of byte 2+j).  Index k selects level c_k of the 16-entry codebook
+//   -2.75 -2 -1.625 -1.25 -0.9375 -0.625 -0.375 -0.125
+//   +0.125 +0.375 +0.625 +0.9375 +1.25 +1.625 +2 +2.75
+// Every level has four significant bits, so each is exact as an fp8 e4m3
+// byte, as fp16 and as the integer 16*c_k; the kernels never form a
+// dequantised tensor -- they turn nibbles into MFMA operands in registers or
+// LDS and apply d once per token.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tbq4 {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlockBytes = 66;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Codebook as byte tables for v_perm_b32.  A perm selector byte 0..3 picks a
+// byte of the second source, 4..7 a byte of the first.
+//   e4m3 bytes of c_8..c_15 (positive): 20 2C 32 37 | 3A 3D 40 43
+//   e4m3 bytes of c_0..c_7  (negative): C3 C0 BD BA | B7 B2 AC A0
+//   int8 16*c_8..16*c_15:  2  6 10 15 | 20 26 32 44
+//   int8 16*c_0..16*c_7: -44 -32 -26 -20 | -15 -10 -6 -2
+// ---------------------------------------------------------------------------
+constexpr uint32_t kE4PosLo = 0x37322C20u, kE4PosHi = 0x43403D3Au;
+constexpr uint32_t kE4NegLo = 0xBABDC0C3u, kE4NegHi = 0xA0ACB2B7u;
+constexpr uint32_t kI8PosLo = 0x0F0A0602u, kI8PosHi = 0x2C201A14u;
+constexpr uint32_t kI8NegLo = 0xECE6E0D4u, kI8NegHi = 0xFEFAF6F1u;
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Four nibbles, one per byte of `t` (the high nibble of each byte is
+// ignored), -> four codebook bytes from the tables (posHi:posLo, negHi:negLo).
+__device__ __forceinline__ uint32_t lut4(uint32_t t, uint32_t posHi, uint32_t posLo,
+                                         uint32_t negHi, uint32_t negLo) {
+  const uint32_t s7 = t & 0x07070707u;
+  const uint32_t p = perm(posHi, posLo, s7);
+  const uint32_t n = perm(negHi, negLo, s7);
+  // byte i of the result: byte i of p if bit 3 of nibble i is set, else of n
+  const uint32_t sel = ((t >> 1) & 0x04040404u) | 0x03020100u;
+  return perm(p, n, sel);
+}
+
+// Four nibbles -> four fp16 codebook values (two fp16x2 words).
+__device__ __forceinline__ void nib4_to_f16(uint32_t t, uint32_t &w01, uint32_t &w23) {
+  const uint32_t e = lut4(t, kE4PosHi, kE4PosLo, kE4NegHi, kE4NegLo);
+  fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, 1.0f, false);
+  fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, 1.0f, true);
+  w01 = __builtin_bit_cast(uint32_t, a);
+  w23 = __builtin_bit_cast(uint32_t, b);
+}
+
+// One word of 8 nibbles (elements in nibble order 0..7) -> 8 fp16 values as an
+// MFMA operand, in the order (n0 n2 n4 n6 n1 n3 n5 n7): low nibbles first.
+__device__ __forceinline__ half8 word_to_half8(uint32_t w) {
+  uint32_t r0, r1, r2, r3;
+  nib4_to_f16(w, r0, r1);
+  nib4_to_f16(w >> 4, r2, r3);
+  u32x4 v = {r0, r1, r2, r3};
+  return __builtin_bit_cast(half8, v);
+}
+
+// Low nibbles of two words (8 values) -> one half8 operand; likewise high.
+__device__ __forceinline__ half8 lo_nibbles_to_half8(uint32_t w0, uint32_t w1) {
+  uint32_t r0, r1, r2, r3;
+  nib4_to_f16(w0, r0, r1);
+  nib4_to_f16(w1, r2, r3);
+  u32x4 v = {r0, r1, r2, r3};
+  return __builtin_bit_cast(half8, v);
+}
+
+// Four nibbles -> four int8 codes 16*c_k.
+__device__ __forceinline__ uint32_t nib4_to_i8(uint32_t t) {
+  return lut4(t, kI8PosHi, kI8PosLo, kI8NegHi, kI8NegLo);
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources: loads through a V# are range checked by the hardware --
+// bytes past num_records read as zero -- so a wave may over-fetch a few bytes
+// at the end of a row without touching memory outside it.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+  // word 3 for CDNA: DST_SEL_XYZW + 32-bit data format, raw (untyped) access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load_x4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_x1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t alignbyte(uint32_t hi, uint32_t lo, uint32_t shift) {
+  return __builtin_amdgcn_alignbyte(hi, lo, shift);
+}
+
+// Sixteen index bytes that start at byte offset `start` of a row (any even
+// offset), as four little-endian words, from a 5-word aligned fetch.
+__device__ __forceinline__ void load16_unaligned(rsrc_t r, uint32_t start, uint32_t out[4]) {
+  const uint32_t a = start & ~3u;
+  const u32x4 w = buf_load_x4(r, a);
+  const uint32_t w4 = buf_load_x1(r, a + 16);
+  const uint32_t s = start & 3u;
+  out[0] = alignbyte(w[1], w[0], s);
+  out[1] = alignbyte(w[2], w[1], s);
+  out[2] = alignbyte(w[3], w[2], s);
+  out[3] = alignbyte(w4, w[3], s);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+}  // namespace tbq4

@@ -1,0 +1,47 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tbq4 {
+
+struct QuantArgs {
+  const void *src[2];          // K and V sources (V unused in flat mode)
+  uint8_t *dst[2];             // K and V caches (or the flat output)
+  int64_t blocks_per_tensor;   // blocks per source tensor
+  int32_t n_new, n_kv_heads, capacity, pos;
+  int32_t flat;                // 1: block i -> src + 128 i, dst + 66 i
+  uint32_t sign_lo, sign_hi;   // sign bits 0..31, 32..63
+  uint32_t sign_lo2, sign_hi2; // sign bits 64..95, 96..127
+};
+
+struct DecodeArgs {
+  const uint8_t *k;
+  const uint8_t *v;
+  const void *q;         // [B][Hq][128]
+  float *ws;             // [B][Hq][P][130]
+  void *out;             // [B][Hq][128]
+  int32_t n_kv_heads, n_q_heads, group, capacity, n_ctx, n_splits, tiles_per_split;
+  float qscale;          // softmax_scale * log2(e)
+  uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
+};
+
+struct PrefillArgs {
+  const uint8_t *k;
+  const uint8_t *v;
+  const void *q;         // [B][n_q][Hq][128]
+  void *out;             // [B][n_q][Hq][128]
+  int32_t n_kv_heads, n_q_heads, group, capacity, n_past, n_q;
+  float qscale;          // softmax_scale * log2(e)
+  uint32_t sign[4];
+};
+
+constexpr int kDecodeTile = 64;
+
+hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int batch, int q_dtype, int out_dtype,
+                         hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
+                          hipStream_t stream);
+
+}  // namespace tbq4

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed; no kernel is launched).
+
+Every argument check of include/tbq4.h runs on the host before any launch,
+so invalid calls can be exercised here; each must return its status code.
+Capacity overflow must be an error, not a crash (page "Kontekst 262K na jednej
+RTX 4090: co dodałem do llama.cpp-turboq", section "4. Poprawność w długich
+sesjach": a full context is handled gracefully).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_tbq4_amd import _lib
+from oracle import tbq4_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    with open(os.path.join(ROOT, "include", "tbq4.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(tbq4_[a-z_0-9]+)\s*\(", header))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.tbq4_version().decode().count(".") == 2
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert L.tbq4_status_str(s)
+    assert L.tbq4_status_str(-99) == b"unknown status"
+
+
+def test_cache_bytes_reproduces_page_footprint(L):
+    # 262144 tokens, 128 (layer, kv head) pairs, K and V: 4.125 GiB (printed
+    # as about 4.1 GiB), against 16 GiB for an FP16 cache.
+    per = L.tbq4_cache_bytes(1, 128, 262144)
+    assert per == 262144 * 128 * 66
+    assert 2 * per / 2 ** 30 == 4.125
+    assert L.tbq4_cache_bytes(-1, 1, 8) == 0
+
+
+def test_sign_vector_matches_oracle(L):
+    for seed in (0, 1, 2, 12345, 2 ** 64 - 1):
+        buf = (ctypes.c_uint8 * 16)()
+        assert L.tbq4_sign_vector(seed, buf) == 0
+        assert bytes(buf) == o.sign_bits(seed)
+    assert L.tbq4_sign_vector(0, None) == _lib.ERR_INVALID_ARG
+
+
+def test_workspace_and_splits(L):
+    p = L.tbq4_decode_auto_splits(4, 8, 131072)
+    assert 1 <= p <= 1024
+    assert L.tbq4_decode_workspace_bytes(4, 8, 64, 131072, 0) >= 4 * 64 * p * 130 * 4
+    assert L.tbq4_decode_workspace_bytes(4, 8, 64, 131072, 16) == 4 * 64 * 16 * 130 * 4
+    assert L.tbq4_decode_workspace_bytes(4, 8, 64, 131072, 1025) == 0
+    assert L.tbq4_decode_auto_splits(0, 8, 100) == 0
+
+
+FAKE = 0x10000  # a 16-byte aligned, never dereferenced address
+
+
+def _cache(batch=1, heads=2, head_dim=128, cap=64, k=FAKE, v=FAKE, seed=0):
+    return _lib.Cache(k, v, batch, heads, head_dim, cap, seed)
+
+
+def test_append_argument_errors(L):
+    c = _cache()
+    app = L.tbq4_quantize_append
+    assert app(None, FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(_cache(head_dim=64)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_UNSUPPORTED
+    assert app(ctypes.byref(_cache(cap=60)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_ALIGNMENT
+    assert app(ctypes.byref(_cache(k=FAKE + 2)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_ALIGNMENT
+    assert app(ctypes.byref(_cache(k=0)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(c), FAKE, FAKE, 7, 0, 1, None) == _lib.ERR_INVALID_ARG    # dtype
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, 60, 5, None) == _lib.ERR_CAPACITY      # 65 > 64
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, 64, 1, None) == _lib.ERR_CAPACITY
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, -1, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(c), None, FAKE, 0, 0, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(c), FAKE + 4, FAKE, 0, 0, 1, None) == _lib.ERR_ALIGNMENT
+    # n_new = 0 is a valid no-op that launches nothing
+    assert app(ctypes.byref(c), None, None, 0, 64, 0, None) == _lib.OK
+
+
+def test_decode_argument_errors(L):
+    c = _cache(heads=2, cap=64)
+    ws = 1 << 20
+
+    def dec(cache=c, q=FAKE, qdt=0, hq=8, n_ctx=10, scale=1.0, out=FAKE, odt=1, p=0,
+            w=FAKE, wb=ws):
+        return L.tbq4_attn_decode(ctypes.byref(cache) if cache is not None else None, q, qdt, hq,
+                                  n_ctx, scale, out, odt, p, w, wb, None)
+    assert dec(cache=None) == _lib.ERR_INVALID_ARG
+    assert dec(q=None) == _lib.ERR_INVALID_ARG
+    assert dec(qdt=2) == _lib.ERR_INVALID_ARG          # bf16 queries not accepted
+    assert dec(odt=2) == _lib.ERR_INVALID_ARG
+    assert dec(hq=7) == _lib.ERR_UNSUPPORTED            # not a multiple of 2 kv heads
+    assert dec(hq=18) == _lib.ERR_UNSUPPORTED           # group of 9 > 8
+    assert dec(n_ctx=0) == _lib.ERR_CAPACITY
+    assert dec(n_ctx=65) == _lib.ERR_CAPACITY
+    assert dec(p=1025) == _lib.ERR_INVALID_ARG
+    assert dec(p=-1) == _lib.ERR_INVALID_ARG
+    assert dec(w=None) == _lib.ERR_WORKSPACE
+    assert dec(wb=16) == _lib.ERR_WORKSPACE
+    assert dec(scale=float("nan")) == _lib.ERR_INVALID_ARG
+    assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
+
+
+def test_prefill_argument_errors(L):
+    c = _cache(heads=2, cap=64)
+
+    def pre(cache=c, q=FAKE, qdt=0, hq=16, n_past=10, n_q=4, out=FAKE, odt=1):
+        return L.tbq4_attn_prefill_chunk(ctypes.byref(cache), q, qdt, hq, n_past, n_q, 0.1, out,
+                                         odt, None)
+    assert pre(hq=6) == _lib.ERR_UNSUPPORTED            # group of 3
+    assert pre(n_past=60, n_q=5) == _lib.ERR_CAPACITY
+    assert pre(n_q=0) == _lib.ERR_CAPACITY
+    assert pre(n_past=-1) == _lib.ERR_CAPACITY
+    assert pre(q=None) == _lib.ERR_INVALID_ARG
+    assert pre(cache=_cache(head_dim=256)) == _lib.ERR_UNSUPPORTED
+
+
+def test_quantize_blocks_argument_errors(L):
+    q = L.tbq4_quantize_blocks
+    assert q(FAKE, 0, -1, 0, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert q(FAKE, 5, 1, 0, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert q(None, 0, 1, 0, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert q(FAKE, 0, 0, 0, None, None) == _lib.OK

@@ -1,0 +1,170 @@
+"""GPU split-K decode attention against the fp64 oracle.
+
+Method: page "Kontekst 262K na jednej RTX 4090: co dodałem do
+llama.cpp-turboq", section "Od czego zacząłem" (flash attention straight on
+TBQ4 blocks, dequantised in the inner loop, in the rotated domain).  Bar:
+packed caches byte-identical to the oracle's; outputs within max-abs 2e-3 and
+relative L2 1e-3 (plus half an fp16 ulp of the reference for fp16 output).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_tbq4_amd as tb
+from oracle import tbq4_oracle as o
+from workloads import WORKLOADS, kv_rows, kv_tensor, q_decode, tiny_inputs
+from _util import check_attn
+
+pytestmark = pytest.mark.gpu
+
+
+def _fill(cache, k, v, chunk=16384):
+    """Append host fp32 [B][T][H][128] K/V into the cache in chunks."""
+    T = k.shape[1]
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        tb.quantize_append(cache, torch.from_numpy(np.ascontiguousarray(k[:, t0:t1])).cuda(),
+                           torch.from_numpy(np.ascontiguousarray(v[:, t0:t1])).cuda(), t0)
+
+
+def _oracle_cache(k, v, seed=0):
+    # [B][T][H][128] -> [B][H][T][66]
+    return (o.quantize_blocks(k.transpose(0, 2, 1, 3), seed)[0],
+            o.quantize_blocks(v.transpose(0, 2, 1, 3), seed)[0])
+
+
+def _run_small(B, Hkv, G, T, cap, n_ctx, scale, seed, P, q_dtype=torch.float32,
+               out_dtype=torch.float16, rng_seed=0, kscale=1.0):
+    rng = np.random.default_rng(rng_seed)
+    k = (rng.standard_normal((B, T, Hkv, 128)) * kscale).astype(np.float32)
+    v = rng.standard_normal((B, T, Hkv, 128)).astype(np.float32)
+    q = rng.standard_normal((B, Hkv * G, 128)).astype(np.float32)
+    cache = tb.KVCache(B, Hkv, cap, sign_seed=seed)
+    _fill(cache, k, v)
+    kc, vc = _oracle_cache(k, v, seed)
+    assert np.array_equal(cache.k[:, :, :T].cpu().numpy(), kc)
+    assert np.array_equal(cache.v[:, :, :T].cpu().numpy(), vc)
+    qt = torch.from_numpy(q).to(q_dtype).cuda()
+    out = tb.attn_decode(cache, qt, n_ctx, scale, n_splits=P, out_dtype=out_dtype)
+    ref = o.attn_decode_ref(qt.float().cpu().numpy(), kc, vc, n_ctx, scale, seed)
+    return out.float().cpu().numpy(), ref
+
+
+def test_tiny_workload_full():
+    """Tiny decode: batch 1, 1 KV / 4 Q heads, 1024 tokens, one key channel x20."""
+    w = WORKLOADS["tiny"]
+    k, v, q, _ = tiny_inputs()
+    cache = tb.KVCache(1, 1, 1024)
+    _fill(cache, k, v)
+    kc, vc = _oracle_cache(k, v)
+    assert np.array_equal(cache.k.cpu().numpy(), kc)
+    assert np.array_equal(cache.v.cpu().numpy(), vc)
+    ref = o.attn_decode_ref(q, kc, vc, 1024, w.softmax_scale)
+    for P in (0, 1, 2, 4, 16):
+        for od in (torch.float16, torch.float32):
+            out = tb.attn_decode(cache, torch.from_numpy(q).cuda(), 1024, w.softmax_scale,
+                                 n_splits=P, out_dtype=od)
+            check_attn(out.float().cpu().numpy(), ref, od == torch.float16, f"tiny P={P} {od}")
+
+
+@pytest.mark.parametrize("n_ctx", [1, 2, 7, 63, 64, 65, 129, 200, 1000])
+def test_ragged_lengths(n_ctx):
+    cap = ((n_ctx + 7) // 8) * 8 + 8
+    out, ref = _run_small(1, 2, 8, n_ctx, cap, n_ctx, 1 / math.sqrt(128), seed=3, P=0, rng_seed=n_ctx)
+    check_attn(out, ref, True, f"n_ctx={n_ctx}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 8])
+def test_group_sizes(G):
+    out, ref = _run_small(2, 3, G, 300, 304, 300, 0.2, seed=11, P=3, rng_seed=G)
+    check_attn(out, ref, True, f"G={G}")
+
+
+def test_n_ctx_shorter_than_filled():
+    out, ref = _run_small(2, 2, 4, 512, 512, 333, 0.1, seed=0, P=5)
+    check_attn(out, ref, True, "n_ctx < filled")
+
+
+def test_fp16_queries_and_fp32_output():
+    out, ref = _run_small(1, 2, 8, 777, 784, 777, 0.09, seed=1, P=4, q_dtype=torch.float16,
+                          out_dtype=torch.float32)
+    check_attn(out, ref, False, "fp16 q")
+
+
+def test_large_scores_peaky_softmax():
+    # keys x30 -> very peaky softmax; the online max must stay exact
+    out, ref = _run_small(1, 1, 8, 2048, 2048, 2048, 1 / math.sqrt(128), seed=2, P=8,
+                          out_dtype=torch.float32, kscale=30.0)
+    check_attn(out, ref, False, "peaky")
+
+
+@pytest.mark.parametrize("P", [1, 3, 16, 64, 256, 1024])
+def test_split_counts_agree(P):
+    out, ref = _run_small(1, 1, 8, 4096, 4096, 4096, 0.1, seed=4, P=P, out_dtype=torch.float32)
+    check_attn(out, ref, False, f"P={P}")
+
+
+def test_deterministic():
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((1, 3000, 2, 128)).astype(np.float32)
+    cache = tb.KVCache(1, 2, 3000)
+    _fill(cache, k, k)
+    q = torch.from_numpy(rng.standard_normal((1, 16, 128)).astype(np.float32)).cuda()
+    a = tb.attn_decode(cache, q, 3000, 0.1, n_splits=7)
+    b = tb.attn_decode(cache, q, 3000, 0.1, n_splits=7)
+    assert torch.equal(a, b)
+
+
+def test_decode16k_workload_full():
+    """Decode at 16384: batch 1, 8 KV / 64 Q heads, 2 outlier channels x15,
+    Q ~ N(0,1)/sqrt(128) with scale 1.0 (and again with scale 1/sqrt(128))."""
+    w = WORKLOADS["decode16k"]
+    T = w.n_ctx
+    k = kv_tensor(w, 0, 0, 0, T)
+    v = kv_tensor(w, 0, 1, 0, T)
+    cache = tb.KVCache(1, 8, T)
+    _fill(cache, k, v)
+    kc, vc = _oracle_cache(k, v)
+    assert np.array_equal(cache.k.cpu().numpy(), kc)
+    assert np.array_equal(cache.v.cpu().numpy(), vc)
+    q = q_decode(w)
+    for scale in (w.softmax_scale, 1 / math.sqrt(128)):
+        ref = o.attn_decode_ref(q, kc, vc, T, scale)
+        for P in (0, 16, 64):
+            out = tb.attn_decode(cache, torch.from_numpy(q).cuda(), T, scale, n_splits=P)
+            check_attn(out.float().cpu().numpy(), ref, True, f"16k scale={scale} P={P}")
+
+
+@pytest.mark.slow
+def test_decode128k_workload_sampled():
+    """Decode at 131072, batch 4, Student-t KV with channel scales: the whole
+    cache is filled on the GPU; two (sequence, KV head) rows are re-quantised
+    by the oracle (bytes compared) and their 16 query heads checked, for the
+    split counts the benchmark sweeps."""
+    w = WORKLOADS["decode128k"]
+    T = w.n_ctx
+    cache = tb.KVCache(w.batch, w.n_kv_heads, T)
+    for t0 in range(0, T, 32768):
+        t1 = t0 + 32768
+        k = kv_tensor(w, 0, 0, t0, t1)
+        v = kv_tensor(w, 0, 1, t0, t1)
+        tb.quantize_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), t0)
+    q = q_decode(w)
+    qt = torch.from_numpy(q).cuda()
+    outs = {P: tb.attn_decode(cache, qt, T, w.softmax_scale, n_splits=P).float().cpu().numpy()
+            for P in (0, 16, 32, 64, 128, 256)}
+    G = w.n_q_heads // w.n_kv_heads
+    for (b, g) in ((0, 0), (3, 5)):
+        K = kv_rows(w, 0, 0, b, g, 0, T)
+        V = kv_rows(w, 0, 1, b, g, 0, T)
+        kc = o.quantize_blocks(K)[0]
+        vc = o.quantize_blocks(V)[0]
+        assert np.array_equal(cache.k[b, g].cpu().numpy(), kc)
+        assert np.array_equal(cache.v[b, g].cpu().numpy(), vc)
+        ref = o.attn_decode_rows_ref(q[b, g * G:(g + 1) * G], o.dequantize_blocks(kc),
+                                     o.dequantize_blocks(vc), w.softmax_scale)
+        for P, out in outs.items():
+            check_attn(out[b, g * G:(g + 1) * G], ref, True, f"128k b={b} g={g} P={P}")
