@@ -1,0 +1,266 @@
+"""Benchmark of the TBQ4 attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--splits P]
+                    [--no-prefill] [--no-cpu-baseline]
+
+One step = one pass of the whole decode hot path over the decode128k workload
+(batch 4 independent sequences, 8 KV / 64 query heads, head_dim 128, 131072
+cached tokens in TBQ4 K and V caches resident in HBM): quantise-append the new
+token's K and V for every sequence, then split-K decode attention over all
+131072 slots (partial kernel + merge kernel).  The headline value is the
+step's algorithmic HBM bytes (packed K+V read, q read, output written, appended
+rows) divided by the step time, in GB/s.  The prefill-chunk workload (2048
+queries on 131072 cached tokens, 8 KV / 64 query heads, append of the chunk's
+K/V then causal attention) is timed in the same run and reported under
+"prefill" in TFLOP/s (4 * 128 * 64 FLOPs per unmasked (query, key) pair).
+
+The dominant kernel's roofline entry uses HIP events recorded on the stream
+the kernels run on, around every decode-partial launch of the timed region.
+The CPU oracle is timed on a bounded sample of the same workload (rows of the
+decode cache, fp64 dequantise + attention) on the host's cores.
+
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--prefill-steps", type=int, default=0)
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768):
+    from workloads import K, V, kv_tensor
+    for a in range(t0, t1, chunk):
+        log(f"{w.name}: filling tokens {a}..{min(t1, a + chunk)}")
+        b = min(t1, a + chunk)
+        k = torch.from_numpy(kv_tensor(w, 0, K, a, b)).cuda()
+        v = torch.from_numpy(kv_tensor(w, 0, V, a, b)).cuda()
+        tb.quantize_append(cache, k, v, a)
+        del k, v
+    torch.cuda.synchronize()
+
+
+def bench_decode(tb, torch, args):
+    from workloads import WORKLOADS, q_decode
+    w = WORKLOADS["decode128k"]
+    B, Hkv, Hq, T = w.batch, w.n_kv_heads, w.n_q_heads, w.n_ctx
+    cache = tb.KVCache(B, Hkv, T)
+    fill_cache(tb, torch, cache, w, 0, T - 1)
+    rng = np.random.default_rng([0, 99])
+    k_new = torch.from_numpy(rng.standard_t(5, size=(B, 1, Hkv, 128)).astype(np.float32)).cuda()
+    v_new = torch.from_numpy(rng.standard_t(5, size=(B, 1, Hkv, 128)).astype(np.float32)).cuda()
+    q = torch.from_numpy(q_decode(w)).cuda()
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    P = args.splits or tb.decode_auto_splits(B, Hkv, T)
+    ws = torch.empty(tb.decode_workspace_bytes(B, Hkv, Hq, T, P), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        tb.quantize_append(cache, k_new, v_new, T - 1)
+        if ev is not None:
+            ev[0].record(stream)
+        tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        tb.attn_decode_merge(ws, B, Hq, P, cache.sign_seed, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the dominant kernel alone: the same partial launch repeated back to
+    # back between two events (single-launch events add the marker gap)
+    kb = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    kb[0].record(stream)
+    for _ in range(args.steps):
+        tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
+    kb[1].record(stream)
+    torch.cuda.synchronize()
+    kern_back_to_back = kb[0].elapsed_time(kb[1]) / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kv_bytes = B * T * Hkv * 2 * 66
+    q_bytes = B * Hq * 128 * 4
+    out_bytes = B * Hq * 128 * 2
+    append_bytes = 2 * B * Hkv * 128 * 4 + 2 * B * Hkv * 66
+    step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
+    ms = wall * 1e3 / args.steps
+    kern_avg = kern_back_to_back
+    achieved = (kv_bytes + q_bytes) / (kern_avg * 1e-3) / 1e9
+    assert torch.isfinite(out.float()).all()
+    return {
+        "P": P, "ms": ms, "value": step_bytes / (ms * 1e-3) / 1e9,
+        "kernel_ms": kern_avg, "kernel_ms_in_step": float(np.mean(kern_ms)),
+        "kernel_ms_in_step_p90": float(np.percentile(kern_ms, 90)),
+        "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
+        "tokens_per_s": B * T / (ms * 1e-3),
+    }
+
+
+def bench_prefill(tb, torch, args):
+    from workloads import WORKLOADS, K, V, kv_tensor, q_prefill
+    w = WORKLOADS["prefill"]
+    n_past, n_q, Hkv, Hq = w.n_ctx, w.n_q, w.n_kv_heads, w.n_q_heads
+    cache = tb.KVCache(1, Hkv, n_past + n_q)
+    fill_cache(tb, torch, cache, w, 0, n_past)
+    k_new = torch.from_numpy(kv_tensor(w, 0, K, n_past, n_past + n_q)).cuda()
+    v_new = torch.from_numpy(kv_tensor(w, 0, V, n_past, n_past + n_q)).cuda()
+    q = torch.from_numpy(q_prefill(w)).cuda()
+    out = torch.empty((1, n_q, Hq, 128), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    steps = args.prefill_steps or max(3, args.steps // 4)
+
+    def step(ev=None):
+        tb.quantize_append(cache, k_new, v_new, n_past)
+        if ev is not None:
+            ev[0].record(stream)
+        tb.attn_prefill_chunk(cache, q, n_past, w.softmax_scale, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    att_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pairs = sum(n_past + i + 1 for i in range(n_q))
+    flops = 4 * 128 * Hq * pairs
+    assert torch.isfinite(out.float()).all()
+    return {
+        "workload": "prefill: 2048 new queries on 131072 cached tokens, batch 1, 8 KV / 64 Q "
+                    "heads, head_dim 128; step = append of the chunk's K/V + causal attention",
+        "steps": steps, "ms_per_step": wall * 1e3 / steps, "attention_ms": att_ms,
+        "tflops": flops / (att_ms * 1e-3) / 1e12,
+        "frac_of_mfma_peak": flops / (att_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "algorithmic_tflop": flops / 1e12, "query_tokens_per_s": n_q / (att_ms * 1e-3),
+    }
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle, untuned, on whole (sequence, KV head) rows of the decode128k
+    workload: fp64 dequantise of the 131072 K and V blocks + attention of the
+    8 query heads.  Rate in GB/s of packed K+V consumed."""
+    from oracle import tbq4_oracle as o
+    from workloads import WORKLOADS, K, V, kv_rows, q_decode
+    w = WORKLOADS["decode128k"]
+    T, G = w.n_ctx, w.n_q_heads // w.n_kv_heads
+    q = q_decode(w)
+    done, spent, rows = 0, 0.0, []
+    for (b, g) in [(0, 0), (1, 3), (2, 5), (3, 7), (0, 4), (1, 1)]:
+        kc = o.quantize_blocks(kv_rows(w, 0, K, b, g, 0, T))[0]
+        vc = o.quantize_blocks(kv_rows(w, 0, V, b, g, 0, T))[0]
+        t0 = time.perf_counter()
+        o.attn_decode_rows_ref(q[b, g * G:(g + 1) * G], o.dequantize_blocks(kc),
+                               o.dequantize_blocks(vc), w.softmax_scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        log(f"cpu baseline: row {done} done, {spent:.1f} s")
+        rows.append((b, g))
+        if spent >= budget_s:
+            break
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+    except Exception:
+        pass
+    gbs = done * T * 132 / spent / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of 32 (sequence, KV head) rows of decode128k (131072 tokens x "
+                      f"8 query heads each), fp64 dequantise + attention; {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_attention_tbq4_amd as tb
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dec = bench_decode(tb, torch, args)
+    log(f"decode: {dec['ms']:.4f} ms/step, kernel {dec['kernel_ms']:.4f} ms, "
+        f"{dec['achieved']:.0f} GB/s")
+    pre = None if args.no_prefill else bench_prefill(tb, torch, args)
+    if pre:
+        log(f"prefill: {pre['attention_ms']:.3f} ms, {pre['tflops']:.1f} TFLOP/s")
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode128k: batch 4 sequences, 8 KV / 64 query heads, head_dim 128, "
+                        "131072 cached tokens in TBQ4 K and V (Student-t nu=5 x per-channel "
+                        "scales); step = append one token per sequence + split-K decode",
+            "batch": 4, "n_ctx": 131072, "n_kv_heads": 8, "n_q_heads": 64, "n_splits": dec["P"],
+            "hbm_frac_of_step": round(dec["value"] / HBM_PEAK_GBS, 4),
+            "kv_tokens_per_s": round(dec["tokens_per_s"], 1),
+        },
+        "roofline": {
+            "kernel": "decode_split_kernel",
+            "bound": "hbm",
+            "achieved": round(dec["achieved"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_ms": round(dec["kernel_ms"], 5),
+            "kernel_ms_in_step": round(dec["kernel_ms_in_step"], 5),
+            "kernel_ms_in_step_p90": round(dec["kernel_ms_in_step_p90"], 5),
+        },
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

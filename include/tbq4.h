@@ -23,12 +23,15 @@
  *   set means s_i = -1), H the natural-order Sylvester Hadamard matrix.
  *   bytes 0-1   d = binary16 nearest sqrt(mean(u_i^2)), ties to even,
  *               saturating at 65504, little endian
- *   bytes 2-65  4-bit indices, element 2j in the low nibble of byte 2+j and
- *               element 2j+1 in the high nibble; idx_i = number of thresholds
- *               t_k (midpoints of adjacent codebook levels) with d*t_k < u_i
- *   codebook    -2.75 -2 -1.625 -1.25 -0.9375 -0.625 -0.375 -0.125
- *               +0.125 +0.375 +0.625 +0.9375 +1.25 +1.625 +2 +2.75
- *   Dequantised value in the rotated domain: d * c[idx]; x_hat = R^T (d c).
+ *   bytes 2-65  4-bit codes, element 2j in the low nibble of byte 2+j and
+ *               element 2j+1 in the high nibble.  A code is sign-magnitude
+ *               (laid out like the e2m1 4-bit float): bit 3 set for u_i < 0,
+ *               bits 0-2 = m_i = number of midpoints tau_k of adjacent
+ *               magnitudes with d*tau_k < |u_i| (nearest level, ties toward
+ *               zero, u_i = 0 -> +0.125).
+ *   magnitudes  0.125 0.375 0.625 0.9375 1.25 1.625 2 2.75  (tau_k = midpoints)
+ *   Dequantised value in the rotated domain: d * (-1)^sign * magnitude[m];
+ *   x_hat = R^T (d c).
  *
  * Conventions shared by every call
  *   - Every pointer argument named as device memory is caller-owned device
@@ -133,12 +136,39 @@ tbq4_status tbq4_quantize_blocks(const void *x, tbq4_dtype src_dtype, int64_t n_
  *   workspace    device, >= tbq4_decode_workspace_bytes(...) bytes, 16-byte
  *                aligned; scratch for the per-split partial softmax states.
  * Errors: 1 <= n_ctx <= capacity else TBQ4_ERR_CAPACITY; n_q_heads a positive
- * multiple of n_kv_heads with n_q_heads / n_kv_heads <= 16, else
- * TBQ4_ERR_UNSUPPORTED. */
+ * multiple of n_kv_heads with n_q_heads / n_kv_heads <= 8, else
+ * TBQ4_ERR_UNSUPPORTED.  Two launches (split kernel, merge kernel). */
 tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
                              int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
                              void *out, tbq4_dtype out_dtype, int32_t n_splits,
                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* The two phases of tbq4_attn_decode, for callers that produce or combine
+ * split-K partial states themselves (for example partials computed over
+ * different token ranges, or on different devices, then merged).
+ *
+ * tbq4_attn_decode_partial: same arguments and checks as tbq4_attn_decode
+ * minus the output; writes, for every (sequence b, query head h, split p),
+ * 130 fp32 values at workspace + ((b * n_q_heads + h) * n_splits + p) * 130:
+ *   [0] m  = max over the split's keys of the score, in log2 units
+ *          (softmax_scale * log2(e) * q.k); -inf for an empty split
+ *   [1] l  = sum over the split's keys of 2^(score - m)
+ *   [2 + i] = sum over the split's keys of 2^(score - m) * v'_i, i = 0..127,
+ *          in the ROTATED domain (v' = R v, unnormalised).
+ * Split p covers the 64-token tiles [p * T, (p + 1) * T), T = ceil(ceil(n_ctx
+ * / 64) / n_splits); with n_splits = 0 the automatic count is used and
+ * returned through *n_splits_used (may be NULL).
+ *
+ * tbq4_attn_decode_merge: out[b][h] = R^T (sum_p 2^(m_p - M) o_p / sum_p
+ * 2^(m_p - M) l_p), M = max_p m_p, from a workspace laid out as above with
+ * n_splits partial states per (b, h).  sign_seed must be the cache's. */
+tbq4_status tbq4_attn_decode_partial(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                     int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
+                                     int32_t n_splits, int32_t *n_splits_used, void *workspace,
+                                     size_t workspace_bytes, void *hip_stream);
+tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes, int32_t batch,
+                                   int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
+                                   void *out, tbq4_dtype out_dtype, void *hip_stream);
 
 /* Prefill-chunk attention: n_q new queries per sequence; query i sits at
  * absolute position n_past + i and attends slots [0, n_past + i] (causal
@@ -147,8 +177,8 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
  *   q, out   device, [batch][n_q][n_q_heads][128]; q_dtype F32 or F16,
  *            out_dtype F16 or F32.
  * Errors: n_past >= 0, n_q >= 1, n_past + n_q <= capacity else
- * TBQ4_ERR_CAPACITY; n_q_heads / n_kv_heads must be 8, else
- * TBQ4_ERR_UNSUPPORTED. */
+ * TBQ4_ERR_CAPACITY; n_q_heads / n_kv_heads must be 1, 2, 4, 8, 16 or 32,
+ * else TBQ4_ERR_UNSUPPORTED. */
 tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
                                     int32_t n_q_heads, int32_t n_past, int32_t n_q,
                                     float softmax_scale, void *out, tbq4_dtype out_dtype,

@@ -21,6 +21,7 @@ from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS
 
 __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
+    "attn_decode_partial", "attn_decode_merge",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
     "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
 ]
@@ -140,6 +141,36 @@ def attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None, out_dtype=
                                        float(softmax_scale), _ptr(out), _dtype(out), n_splits,
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(q.device)), "tbq4_attn_decode")
+    return out
+
+
+def attn_decode_partial(cache, q, n_ctx, softmax_scale, n_splits=0, workspace=None):
+    """First decode phase: per-split partial softmax states into `workspace`
+    (layout in include/tbq4.h).  Returns (workspace, n_splits_used)."""
+    _require(q, "q")
+    B, Hq, D = q.shape
+    need = decode_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, n_ctx, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    used = ctypes.c_int32(0)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_attn_decode_partial(
+        ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx, float(softmax_scale), n_splits,
+        ctypes.byref(used), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device)), "tbq4_attn_decode_partial")
+    return workspace, used.value
+
+
+def attn_decode_merge(workspace, batch, n_q_heads, n_splits, sign_seed=0, out=None,
+                      out_dtype=torch.float16):
+    """Second decode phase: merge `n_splits` partial states per (sequence,
+    head), normalise and rotate back.  Returns out ([batch][n_q_heads][128])."""
+    if out is None:
+        out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=out_dtype, device=workspace.device)
+    _require(out, "out", (batch, n_q_heads, HEAD_DIM))
+    _check(_lib.lib().tbq4_attn_decode_merge(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), batch, n_q_heads, n_splits,
+        sign_seed, _ptr(out), _dtype(out), _stream(out.device)), "tbq4_attn_decode_merge")
     return out
 
 

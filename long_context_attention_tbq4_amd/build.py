@@ -18,6 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtbq4.so")
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "prefill.hip"]
+# per-source options: the decode loop keeps its MFMA accumulators in
+# ordinary VGPRs (its conditional rescale then needs no register copies)
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():
@@ -37,7 +40,8 @@ def build(verbose=False):
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc()] + common + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc()] + common + EXTRA.get(src, []) +
+               ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -148,15 +148,16 @@ tbq4_status tbq4_quantize_blocks(const void *x, tbq4_dtype src_dtype, int64_t n_
   return from_hip(tbq4::launch_quantize(a, (int)src_dtype, 1, (hipStream_t)hip_stream));
 }
 
-tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
-                             int32_t n_q_heads, int32_t n_ctx, float softmax_scale, void *out,
-                             tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
-                             size_t workspace_bytes, void *hip_stream) {
+// Checks shared by the decode calls; fills `a` (all but out) and returns the
+// split count through *P.
+static tbq4_status prepare_decode(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                  int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
+                                  int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                  tbq4::DecodeArgs &a) {
   tbq4_status s = check_cache(cache);
   if (s != TBQ4_OK) return s;
-  if (!q || !out) return TBQ4_ERR_INVALID_ARG;
+  if (!q) return TBQ4_ERR_INVALID_ARG;
   if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
-  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;
   const int32_t G = n_q_heads / cache->n_kv_heads;
@@ -168,15 +169,12 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
   const size_t need = tbq4_decode_workspace_bytes(cache->batch, cache->n_kv_heads, n_q_heads,
                                                   n_ctx, P);
   if (!workspace || workspace_bytes < need) return TBQ4_ERR_WORKSPACE;
-  if (!aligned16(workspace) || !aligned16(q) || !aligned16(out)) return TBQ4_ERR_ALIGNMENT;
-
-  tbq4::DecodeArgs a;
+  if (!aligned16(workspace) || !aligned16(q)) return TBQ4_ERR_ALIGNMENT;
   memset(&a, 0, sizeof(a));
   a.k = cache->k;
   a.v = cache->v;
   a.q = q;
   a.ws = (float *)workspace;
-  a.out = out;
   a.n_kv_heads = cache->n_kv_heads;
   a.n_q_heads = n_q_heads;
   a.group = G;
@@ -187,8 +185,59 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
   a.tiles_per_split = (n_tiles + P - 1) / P;
   a.qscale = softmax_scale * 1.4426950408889634f;
   sign_words(cache->sign_seed, a.sign);
-  return from_hip(tbq4::launch_decode(a, cache->batch, (int)q_dtype, (int)out_dtype,
-                                      (hipStream_t)hip_stream));
+  return TBQ4_OK;
+}
+
+tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                             int32_t n_q_heads, int32_t n_ctx, float softmax_scale, void *out,
+                             tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                             size_t workspace_bytes, void *hip_stream) {
+  if (!out) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  tbq4::DecodeArgs a;
+  tbq4_status s = prepare_decode(cache, q, q_dtype, n_q_heads, n_ctx, softmax_scale, n_splits,
+                                 workspace, workspace_bytes, a);
+  if (s != TBQ4_OK) return s;
+  if (!aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  a.out = out;
+  hipStream_t st = (hipStream_t)hip_stream;
+  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
+  if (s != TBQ4_OK) return s;
+  return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
+}
+
+tbq4_status tbq4_attn_decode_partial(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                     int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
+                                     int32_t n_splits, int32_t *n_splits_used, void *workspace,
+                                     size_t workspace_bytes, void *hip_stream) {
+  tbq4::DecodeArgs a;
+  tbq4_status s = prepare_decode(cache, q, q_dtype, n_q_heads, n_ctx, softmax_scale, n_splits,
+                                 workspace, workspace_bytes, a);
+  if (s != TBQ4_OK) return s;
+  if (n_splits_used) *n_splits_used = a.n_splits;
+  return from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype,
+                                              (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes, int32_t batch,
+                                   int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
+                                   void *out, tbq4_dtype out_dtype, void *hip_stream) {
+  if (!workspace || !out) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (batch <= 0 || n_q_heads <= 0 || batch > 65535 || n_q_heads > 65535)
+    return TBQ4_ERR_INVALID_ARG;
+  if (n_splits < 1 || n_splits > TBQ4_MAX_SPLITS) return TBQ4_ERR_INVALID_ARG;
+  const size_t need = round256((size_t)batch * n_q_heads * n_splits * 130 * sizeof(float));
+  if (workspace_bytes < need) return TBQ4_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  tbq4::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.ws = (float *)workspace;
+  a.out = out;
+  a.n_q_heads = n_q_heads;
+  a.n_splits = n_splits;
+  sign_words(sign_seed, a.sign);
+  return from_hip(tbq4::launch_decode_merge(a, batch, (int)out_dtype, (hipStream_t)hip_stream));
 }
 
 tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,

@@ -38,8 +38,8 @@ __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b;
 
 // 16-lane row rotation by 8: lane j receives lane (j + 8) mod 16 of its row.
 __device__ __forceinline__ float row_ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
-                                                            0x128, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x128, 0xF, 0xF, true));
 }
 
 template <typename QT>
@@ -50,8 +50,8 @@ template <> __device__ __forceinline__ float load_q<_Float16>(const _Float16 *p)
 template <typename QT>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[kTile];
+  __shared__ __attribute__((aligned(16))) float sk[kTile];   // d^K * 2^-ex per token
+  __shared__ __attribute__((aligned(16))) float sv[kTile];   // d^V per token
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -100,10 +100,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     qv[i] *= f;
     mx = fmaxf(mx, fabsf(qv[i]));
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  // power-of-two normalisation: max |q| in [2^13, 2^14) keeps hi and
-  // residual well inside the fp16 range
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  // one power-of-two normalisation for the whole group: max |q'| in
+  // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
+  // range, and 2^-ex folds into the per-token key scale
   int ex = 0;
   if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
   ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
@@ -146,27 +147,57 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     tr_off[kk] = tok * kVRow + 8 * (col & 1);
   }
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int tok0 = t * kTile;
-    // ---- fetch
-    uint32_t kw[4][4], vw[4][4];
+  // Raw fetch of one 64-token tile: per 16-token group, 5 words of K and of V
+  // covering this lane's 16 index bytes (start offsets are even, so the words
+  // are realigned by 0 or 2 bytes -- a per-lane constant), plus the scales of
+  // token `lane`.  Two fetch buffers alternate: the next tile's fetch is in
+  // flight while the current tile is processed.  A tile past the end of the
+  // split is fetched at an offset beyond the buffer range, which the hardware
+  // turns into zeros without a memory access, so every fetch is issued
+  // unconditionally and the wait counts stay exact.
+  struct Raw {
+    u32x4 k4[4], v4[4];
+    uint32_t k1[4], v1[4];
+    uint16_t sk, sv;
+  };
+  const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
+  const uint32_t shift = lane_off & 3u;
+  auto fetch = [&](Raw &r, int t) {
+    const uint32_t base = t < t_end ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const uint32_t start = (uint32_t)(tok0 + 16 * blk + col) * kBlockBytes + 2 + 16 * quarter;
-      load16_unaligned(rk, start, kw[blk]);
-      load16_unaligned(rv, start, vw[blk]);
+      const uint32_t a = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
+      r.k4[blk] = buf_load_x4(rk, a);
+      r.k1[blk] = buf_load_x1(rk, a + 16);
+      r.v4[blk] = buf_load_x4(rv, a);
+      r.v1[blk] = buf_load_x1(rv, a + 16);
     }
-    const uint16_t skv = buf_load_u16(rk, (uint32_t)(tok0 + lane) * kBlockBytes);
-    const uint16_t svv = buf_load_u16(rv, (uint32_t)(tok0 + lane) * kBlockBytes);
+    r.sk = buf_load_u16(rk, base + (uint32_t)lane * kBlockBytes);
+    r.sv = buf_load_u16(rv, base + (uint32_t)lane * kBlockBytes);
+  };
+
+  auto process = [&](const Raw &r, int t) {
+    const int tok0 = t * kTile;
+    uint32_t kw[4][4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const u32x4 w = r.k4[blk];
+      kw[blk][0] = alignbyte(w[1], w[0], shift);
+      kw[blk][1] = alignbyte(w[2], w[1], shift);
+      kw[blk][2] = alignbyte(w[3], w[2], shift);
+      kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+    }
 
     __syncthreads();   // previous tile's LDS reads are done
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      u32x4 w = {vw[blk][0], vw[blk][1], vw[blk][2], vw[blk][3]};
-      *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = w;
+      const u32x4 w = r.v4[blk];
+      const u32x4 a = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
+                       alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
+      *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
     }
-    sk[lane] = skv;
-    sv[lane] = svv;
+    sk[lane] = half_bits_to_float(r.sk) * qs_inv;
+    sv[lane] = half_bits_to_float(r.sv);
 
     // ---- scores S^T[token][col] = K . q'
     float s[4][4];
@@ -181,25 +212,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     __syncthreads();   // staged V rows and scales are visible
 
-    float tmax = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const int tl = 16 * blk + 4 * quarter;
-      const uint2 kd = *(const uint2 *)(sk + tl);
+      const float4v kd = *(const float4v *)(sk + 16 * blk + 4 * quarter);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t hb = (e < 2 ? kd.x : kd.y) >> (16 * (e & 1));
-        const float dk = half_bits_to_float(hb & 0xFFFF);
-        const bool valid = tok0 + tl + e < a.n_ctx;
-        const float x = valid ? s[blk][e] * (dk * qs_inv) : -INFINITY;
-        s[blk][e] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int e = 0; e < 4; ++e) s[blk][e] *= kd[e];
     }
+    if (tok0 + kTile > a.n_ctx) {        // only the last tile holds tokens >= n_ctx
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[blk][e] += (tok0 + 16 * blk + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s[blk][e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
 
     // rescale the accumulators when some head's running max moved
@@ -218,14 +252,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     half8 pa[2];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const int tl = 16 * blk + 4 * quarter;
-      const uint2 vd = *(const uint2 *)(sv + tl);
+      const float4v vd = *(const float4v *)(sv + 16 * blk + 4 * quarter);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(s[blk][e] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[blk][e] - m_new);
         psum += p;
-        const uint32_t hb = (e < 2 ? vd.x : vd.y) >> (16 * (e & 1));
-        const float pt = p * half_bits_to_float(hb & 0xFFFF);
+        const float pt = p * vd[e];
         const _Float16 hi = (_Float16)pt;
         const _Float16 lo = (_Float16)(pt - (float)hi);
         pa[blk >> 1][4 * (blk & 1) + e] = lo_part ? lo : hi;
@@ -248,6 +280,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
       }
     }
+  };
+
+  Raw ra, rb;
+  fetch(ra, t_begin);
+  for (int t = t_begin; t < t_end; t += 2) {
+    fetch(rb, t + 1);
+    process(ra, t);
+    fetch(ra, t + 2);
+    if (t + 1 < t_end) process(rb, t + 1);
   }
 
   // ---------------- partial state of this split
@@ -281,25 +322,62 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge: o = R^T (sum_p 2^(m_p - M) o'_p / sum_p 2^(m_p - M) l_p), one
-// wavefront per (sequence, query head); lane holds dims lane and lane + 64.
+// 256-thread workgroup per (sequence, query head).  The four wavefronts take
+// every fourth split (lane holds dims lane and lane + 64), several splits in
+// flight at once; the partial sums meet in LDS and wavefront 0 normalises,
+// applies the inverse rotation and stores.
 template <typename OT>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float red[4][130];
+  __shared__ float smax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int P = a.n_splits;
   const float *base = a.ws + ((size_t)b * a.n_q_heads + h) * P * 130;
+
   float M = -INFINITY;
-  for (int p = lane; p < P; p += 64) M = fmaxf(M, base[(size_t)p * 130]);
+  for (int p = tid; p < P; p += 256) M = fmaxf(M, base[(size_t)p * 130]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if (lane == 0) smax[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+
   float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int p = 0; p < P; ++p) {
-    const float* bp = base + (size_t)p * 130;
-    const float w = exp2f(bp[0] - M);
-    L += w * bp[1];
-    o0 += w * bp[2 + lane];
-    o1 += w * bp[2 + 64 + lane];
+  int p = wave;
+  for (; p + 12 < P; p += 16) {
+    float w[4], lp[4], x0[4], x1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float *bp = base + (size_t)(p + 4 * u) * 130;
+      w[u] = bp[0];
+      lp[u] = bp[1];
+      x0[u] = bp[2 + lane];
+      x1[u] = bp[66 + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wt = __builtin_amdgcn_exp2f(w[u] - M);
+      L += wt * lp[u];
+      o0 += wt * x0[u];
+      o1 += wt * x1[u];
+    }
   }
+  for (; p < P; p += 4) {
+    const float *bp = base + (size_t)p * 130;
+    const float wt = __builtin_amdgcn_exp2f(bp[0] - M);
+    L += wt * bp[1];
+    o0 += wt * bp[2 + lane];
+    o1 += wt * bp[66 + lane];
+  }
+  red[wave][lane] = o0;
+  red[wave][64 + lane] = o1;
+  if (lane == 0) red[wave][128] = L;
+  __syncthreads();
+  if (wave != 0) return;
+  o0 = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+  o1 = red[0][64 + lane] + red[1][64 + lane] + red[2][64 + lane] + red[3][64 + lane];
+  L = red[0][128] + red[1][128] + red[2][128] + red[3][128];
   const float inv = 1.0f / L;
   o0 *= inv;
   o1 *= inv;
@@ -326,20 +404,21 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   dst[lane + 64] = (OT)o1;
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int batch, int q_dtype, int out_dtype,
-                         hipStream_t stream) {
-  dim3 g1(a.n_splits, a.n_kv_heads, batch);
+hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream) {
+  dim3 grid(a.n_splits, a.n_kv_heads, batch);
   if (q_dtype == 0)
-    hipLaunchKernelGGL(decode_split_kernel<float>, g1, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_split_kernel<_Float16>, g1, dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 g2(a.n_q_heads, batch);
+    hipLaunchKernelGGL(decode_split_kernel<_Float16>, grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream) {
+  dim3 grid(a.n_q_heads, batch);
   if (out_dtype == 0)
-    hipLaunchKernelGGL(decode_merge_kernel<float>, g2, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_merge_kernel<float>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<_Float16>, g2, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_merge_kernel<_Float16>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

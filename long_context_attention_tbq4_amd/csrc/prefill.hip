@@ -1,6 +1,360 @@
-// placeholder replaced by the prefill kernel
+// TBQ4 prefill-chunk attention for gfx950.
+//
+// Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+// section "Od czego zacząłem": flash attention reads raw TBQ4 blocks and
+// dequantises them in its inner loop, in the rotated (Hadamard) domain, with
+// no F16 buffer in memory.  A prefill chunk: query i of the chunk sits at
+// absolute position n_past + i and attends keys 0 .. n_past + i.
+//
+// A workgroup owns one KV head and a tile of 128/G queries x G heads = 128
+// rows (4 wavefronts x 32 rows); blockIdx.x % n_kv_heads is the KV head, so
+// on an 8-XCD part each XCD streams the cache of its own head.  Per 64-key
+// tile the workgroup
+//   * fetches the next tile's packed K and V rows (coalesced 16-byte-per-lane
+//     loads) before it computes on the current one, and dequantises them into
+//     the other half of a double-buffered LDS tile: fp16 codebook values, one
+//     fp32 scale per key and tensor,
+//   * S^T = K Q'^T on v_mfma_f32_32x32x16_f16, with q' split into an fp16
+//     high part and the fp16 residual that both accumulate into the same
+//     fp32 scores (~22 bits of q'), then scales by d^K per key,
+//   * online softmax in the log2 domain, P~ = p d^V in fp16,
+//   * O'^T += V^T P~^T on v_mfma_f32_32x32x16_f16 with V^T read straight out
+//     of the row-major LDS tile by ds_read_b64_tr_b16.
+// The epilogue divides by the row sum, applies R^T and stores.
+//
+// LDS rows keep each 8-dimension group in nibble order (d0 d2 d4 d6 d1 d3 d5
+// d7); q' uses the same order, and since the Walsh-Hadamard matrix is
+// invariant under a permutation of index bits, the output transform runs in
+// that order too, mapping positions back to dimensions only at the store.
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
+
 namespace tbq4 {
-hipError_t launch_prefill(const PrefillArgs &, int, int, int, hipStream_t) { return hipErrorNotSupported; }
+
+constexpr int kKT = 64;             // keys per tile
+constexpr int kRowB = 272;          // LDS bytes per fp16 row (256 + pad)
+constexpr int kTileB = kKT * kRowB; // bytes of one K (or V) tile
+
+struct __attribute__((aligned(16))) PrefillLds {
+  uint8_t k[2][kTileB];
+  uint8_t v[2][kTileB];
+  float sk[2][kKT];
+  float sv[2][kKT];
+};
+
+// dimension held at row position p (8-dimension groups in nibble order)
+__device__ __forceinline__ int pos_to_dim(int p) {
+  const int r = p & 7;
+  return (p & ~7) | (r < 4 ? 2 * r : 2 * (r - 4) + 1);
 }
+
+template <typename T> __device__ __forceinline__ float ld(const T *p);
+template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float ld<_Float16>(const _Float16 *p) { return (float)*p; }
+
+// One thread's share of a tile fetch: 16 index bytes of K and V for one key
+// and quarter (5 raw words each), and the key's two scales (quarter 0).
+struct TileRaw {
+  u32x4 k4, v4;
+  uint32_t k1, v1;
+  uint16_t sk, sv;
+};
+
+template <typename QT, typename OT>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+  __shared__ PrefillLds L;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int G = a.group;
+  const int qpw = 32 / G;                        // queries per wavefront
+  const int qpwg = 4 * qpw;                      // queries per workgroup
+  const int g = blockIdx.x % a.n_kv_heads;
+  const int qt = blockIdx.x / a.n_kv_heads;
+  const int b = blockIdx.y;
+
+  const int row = lane & 31, half = lane >> 5;
+  const int qi = qt * qpwg + wave * qpw + row / G;          // query index in the chunk
+  const int hq = g * G + row % G;                           // query head
+  const bool row_valid = qi < a.n_q;
+  const int qi_c = row_valid ? qi : a.n_q - 1;
+  const int key_limit = a.n_past + qi_c;                    // last key this row sees
+  const int wave_q0 = min(qt * qpwg + wave * qpw, a.n_q - 1);
+  const int wave_min_limit = a.n_past + wave_q0;            // smallest limit in the wave
+
+  // ---------------- q' = R q * scale * log2(e): fp16 high part + residual
+  // lane holds positions 16 c + 8 half + e (c = 0..7, e = 0..7)
+  half8 qh[8], ql[8];
+  float rowscale;
+  {
+    float x[64];
+    const QT *qp = (const QT *)a.q + (((size_t)b * a.n_q + qi_c) * a.n_q_heads + hq) * kHeadDim;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = pos_to_dim(16 * c + 8 * half + e);
+        const float v = ld<QT>(qp + d);
+        x[8 * c + e] = ((a.sign[d >> 5] >> (d & 31)) & 1u) ? -v : v;
+      }
+    // Walsh-Hadamard over the 7 position bits: bits 0-2 = e, bit 3 = half
+    // (lanes 32 apart), bits 4-6 = c
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        if ((i & h) == 0) {
+          const float u = x[i], w = x[i + h];
+          x[i] = u + w;
+          x[i + h] = u - w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float o = __shfl_xor(x[i], 32, 64);
+      x[i] = half ? (o - x[i]) : (x[i] + o);
+    }
+    const float f = 0.08838834764831845f * a.qscale;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      x[i] *= f;
+      mx = fmaxf(mx, fabsf(x[i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // power-of-two normalisation: max |q'| in [2^13, 2^14)
+    int ex = 0;
+    if (mx > 0.0f) {
+      int e2;
+      frexpf(mx, &e2);
+      ex = 14 - e2;
+    }
+    ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+    rowscale = ldexpf(1.0f, -ex);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = ldexpf(x[8 * c + e], ex);
+        const _Float16 hi = (_Float16)y;
+        qh[c][e] = hi;
+        ql[c][e] = (_Float16)(y - (float)hi);
+      }
+  }
+
+  const int q_last = min(qt * qpwg + qpwg, a.n_q) - 1;
+  const int kv_end = a.n_past + q_last + 1;                  // keys the workgroup needs
+  const int n_tiles = (kv_end + kKT - 1) / kKT;
+
+  const size_t rowoff = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
+  const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
+  const rsrc_t rk = make_rsrc(a.k + rowoff, row_bytes);
+  const rsrc_t rv = make_rsrc(a.v + rowoff, row_bytes);
+
+  // fetch mapping: thread -> (key, quarter); start offsets are even, so the
+  // realignment shift is 0 or 2 (a per-thread constant)
+  const int fkey = tid >> 2, fq = tid & 3;
+  const uint32_t foff = (uint32_t)fkey * kBlockBytes + 2 + 16 * fq;
+  const uint32_t fshift = foff & 3u;
+  auto fetch = [&](TileRaw &r, int t) {
+    const uint32_t base = (uint32_t)t * kKT * kBlockBytes;
+    const uint32_t a0 = (base + foff) & ~3u;
+    r.k4 = buf_load_x4(rk, a0);
+    r.k1 = buf_load_x1(rk, a0 + 16);
+    r.v4 = buf_load_x4(rv, a0);
+    r.v1 = buf_load_x1(rv, a0 + 16);
+    r.sk = 0;
+    r.sv = 0;
+    if (fq == 0) {
+      r.sk = buf_load_u16(rk, base + (uint32_t)fkey * kBlockBytes);
+      r.sv = buf_load_u16(rv, base + (uint32_t)fkey * kBlockBytes);
+    }
+  };
+  // dequantise a fetched share into LDS buffer `buf`: 32 fp16 codebook
+  // values of K and of V at row fkey, positions 32 fq .. 32 fq + 31
+  auto stage = [&](const TileRaw &r, int buf) {
+    const uint32_t kw[4] = {alignbyte(r.k4[1], r.k4[0], fshift), alignbyte(r.k4[2], r.k4[1], fshift),
+                            alignbyte(r.k4[3], r.k4[2], fshift), alignbyte(r.k1, r.k4[3], fshift)};
+    const uint32_t vw[4] = {alignbyte(r.v4[1], r.v4[0], fshift), alignbyte(r.v4[2], r.v4[1], fshift),
+                            alignbyte(r.v4[3], r.v4[2], fshift), alignbyte(r.v1, r.v4[3], fshift)};
+    uint8_t *kr = L.k[buf] + fkey * kRowB + 64 * fq;
+    uint8_t *vr = L.v[buf] + fkey * kRowB + 64 * fq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t r0, r1, r2, r3;
+      nib4_to_f16(kw[c], r0, r1);
+      nib4_to_f16(kw[c] >> 4, r2, r3);
+      *(u32x4 *)(kr + 16 * c) = u32x4{r0, r1, r2, r3};
+      nib4_to_f16(vw[c], r0, r1);
+      nib4_to_f16(vw[c] >> 4, r2, r3);
+      *(u32x4 *)(vr + 16 * c) = u32x4{r0, r1, r2, r3};
+    }
+    if (fq == 0) {
+      L.sk[buf][fkey] = half_bits_to_float(r.sk);
+      L.sv[buf][fkey] = half_bits_to_float(r.sv);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float16v o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
+
+  // transposed V reads: lane s of a 16-lane group points at key 4*half + s/4
+  // (+ 8 for the second read) and position 16*((lane>>4)&1) + 4*(s&3)
+  const int s16 = lane & 15;
+  const int tr_base = (4 * half + (s16 >> 2)) * kRowB + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+
+  {
+    TileRaw r0;
+    fetch(r0, 0);
+    stage(r0, 0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    const int key0 = kt * kKT;
+    TileRaw nxt;
+    const bool more = kt + 1 < n_tiles;
+    if (more) fetch(nxt, kt + 1);
+
+    const uint8_t *kb = L.k[buf];
+    const uint8_t *vb = L.v[buf];
+    const bool masked = key0 + kKT - 1 > wave_min_limit;   // tile crosses the diagonal
+
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kb0 = 32 * sub;              // first key of this 32-key block in the tile
+      // ---- S^T[key][row] = K (q'_hi + q'_lo)
+      float16v sacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const half8 ka = *(const half8 *)(kb + (kb0 + row) * kRowB + 32 * c + 16 * half);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[c], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[c], sacc, 0, 0, 0);
+      }
+      // element e holds key kb0 + 8 (e/4) + 4 half + e%4
+      float s[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4v dk4 = *(const float4v *)(&L.sk[buf][kb0 + 8 * m + 4 * half]);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) s[4 * m + e2] = sacc[4 * m + e2] * (rowscale * dk4[e2]);
+      }
+      if (masked) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2)
+            s[4 * m + e2] += (key0 + kb0 + 8 * m + 4 * half + e2 <= key_limit) ? 0.0f : -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      }
+      float psum = 0.0f;
+      half8 pb[2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4v dv4 = *(const float4v *)(&L.sv[buf][kb0 + 8 * m + 4 * half]);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int e = 4 * m + e2;
+          const float p = __builtin_amdgcn_exp2f(s[e] - m_new);
+          psum += p;
+          pb[e >> 3][e & 7] = (_Float16)(p * dv4[e2]);
+        }
+      }
+      l_run = l_run * alpha + psum;
+
+      // ---- O'^T[dim][row] += V^T P~^T
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint8_t *vbase = vb + (kb0 + 16 * ks) * kRowB + tr_base;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          typedef __attribute__((address_space(3))) short4v lds_s4;
+          const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 64 * db));
+          const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kRowB + 64 * db));
+          const short8v vs = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, vs), pb[ks], o[db],
+                                                         0, 0, 0);
+        }
+      }
+    }
+
+    if (more) stage(nxt, buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue: normalise, o = R^T o', store
+  l_run += __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_run;
+  float y[64];       // index 16 db + e  <->  position 32 db + 8 (e/4) + 4 half + e%4
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) y[16 * db + e] = o[db][e] * inv;
+  // position bits 0,1 = e bits 0,1; bits 3,4 = e bits 2,3; bits 5,6 = db
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if ((i & h) == 0) {
+        const float u = y[i], w = y[i + h];
+        y[i] = u + w;
+        y[i + h] = u - w;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {                 // position bit 2: lanes 32 apart
+    const float t = __shfl_xor(y[i], 32, 64);
+    y[i] = half ? (t - y[i]) : (y[i] + t);
+  }
+  if (row_valid) {
+    OT *dst = (OT *)a.out + (((size_t)b * a.n_q + qi) * a.n_q_heads + hq) * kHeadDim;
+    const float r = 0.08838834764831845f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int db = i >> 4, e = i & 15;
+      const int p = 32 * db + 8 * (e >> 2) + 4 * half + (e & 3);
+      const int d = pos_to_dim(p);
+      const float v = y[i] * r;
+      dst[d] = (OT)(((a.sign[d >> 5] >> (d & 31)) & 1u) ? -v : v);
+    }
+  }
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
+                          hipStream_t stream) {
+  const int qpwg = 4 * (32 / a.group);
+  const int n_qt = (a.n_q + qpwg - 1) / qpwg;
+  const int64_t gx = (int64_t)n_qt * a.n_kv_heads;
+  if (gx > 0x7FFFFFFF || batch > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)gx, batch);
+  if (q_dtype == 0 && out_dtype == 1)
+    hipLaunchKernelGGL((prefill_kernel<float, _Float16>), grid, dim3(256), 0, stream, a);
+  else if (q_dtype == 0)
+    hipLaunchKernelGGL((prefill_kernel<float, float>), grid, dim3(256), 0, stream, a);
+  else if (out_dtype == 1)
+    hipLaunchKernelGGL((prefill_kernel<_Float16, _Float16>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<_Float16, float>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tbq4

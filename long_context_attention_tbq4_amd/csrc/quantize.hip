@@ -13,8 +13,9 @@
 //   p = u*u; tree p_i += p_{i+h} for h = 64..1; ms = p_0 * 2^-7
 //   d = binary16 nearest sqrt(ms) (exact comparison with squared midpoints,
 //       ties to even, saturating at 65504)
-//   idx_i = #{k : d * t_k < u_i}, t_k midpoints of adjacent codebook levels
-//   bytes: d (LE) then idx_{2j} | idx_{2j+1} << 4
+//   code_i = 8*[u_i < 0] + #{k < 7 : d * tau_k < |u_i|}, tau_k midpoints of
+//       adjacent level magnitudes (nearest level, ties toward zero)
+//   bytes: d (LE) then code_{2j} | code_{2j+1} << 4
 //
 // One wavefront quantises one block: lane l holds elements l and l+64.
 #include "tbq4_device.h"
@@ -123,18 +124,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int dbits = half_round_sqrt(ms);
   const double d = half_value(dbits);
 
-  // idx = number of scaled thresholds strictly below u
-  const double thr[15] = {-2.375, -1.8125, -1.4375, -1.09375, -0.78125, -0.5, -0.25, 0.0,
-                          0.25, 0.5, 0.78125, 1.09375, 1.4375, 1.8125, 2.375};
-  int i0 = 0, i1 = 0;
+  // sign-magnitude code: bit 3 = sign of u, bits 0-2 = number of scaled
+  // magnitude midpoints strictly below |u| (d * tau_k is exact)
+  const double tau[7] = {0.25, 0.5, 0.78125, 1.09375, 1.4375, 1.8125, 2.375};
+  const double a0 = fabs(u0), a1 = fabs(u1);
+  int i0 = u0 < 0.0 ? 8 : 0, i1 = u1 < 0.0 ? 8 : 0;
 #pragma unroll
-  for (int k = 0; k < 15; ++k) {
-    const double dt = d * thr[k];
-    i0 += dt < u0 ? 1 : 0;
-    i1 += dt < u1 ? 1 : 0;
+  for (int k = 0; k < 7; ++k) {
+    const double dt = d * tau[k];
+    i0 += dt < a0 ? 1 : 0;
+    i1 += dt < a1 ? 1 : 0;
   }
 
-  // byte m = idx[2m] | idx[2m+1] << 4; elements 2m, 2m+1 live in lanes
+  // byte m = code[2m] | code[2m+1] << 4; elements 2m, 2m+1 live in lanes
   // (2m)&63 and (2m+1)&63, first element for m < 32, second for m >= 32
   const int both = i0 | (i1 << 8);
   const int srcl = (2 * lane) & 63;

@@ -2,14 +2,14 @@
 //
 // Block format (page "Kontekst 262K na jednej RTX 4090: co dodałem do
 // llama.cpp-turboq", section "Od czego zacząłem"): 128 values -> 66 bytes, a
-// binary16 scale d followed by 64 bytes of 4-bit indices (element 2j in the
-// low nibble of byte 2+j).  Index k selects level c_k of the 16-entry codebook
-//   -2.75 -2 -1.625 -1.25 -0.9375 -0.625 -0.375 -0.125
-//   +0.125 +0.375 +0.625 +0.9375 +1.25 +1.625 +2 +2.75
+// binary16 scale d followed by 64 bytes of 4-bit codes (element 2j in the low
+// nibble of byte 2+j).  A code is sign-magnitude, laid out like the 4-bit
+// e2m1 float: bit 3 = sign, bits 0-2 = rank m of the magnitude in
+//   0.125 0.375 0.625 0.9375 1.25 1.625 2 2.75
 // Every level has four significant bits, so each is exact as an fp8 e4m3
-// byte, as fp16 and as the integer 16*c_k; the kernels never form a
-// dequantised tensor -- they turn nibbles into MFMA operands in registers or
-// LDS and apply d once per token.
+// byte, as fp16 and as the integer 16*c; the kernels never form a dequantised
+// tensor -- they turn codes into MFMA operands in registers or LDS and apply d
+// once per token.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,46 +28,40 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int16v __attribute__((ext_vector_type(16)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
-// Codebook as byte tables for v_perm_b32.  A perm selector byte 0..3 picks a
-// byte of the second source, 4..7 a byte of the first.
-//   e4m3 bytes of c_8..c_15 (positive): 20 2C 32 37 | 3A 3D 40 43
-//   e4m3 bytes of c_0..c_7  (negative): C3 C0 BD BA | B7 B2 AC A0
-//   int8 16*c_8..16*c_15:  2  6 10 15 | 20 26 32 44
-//   int8 16*c_0..16*c_7: -44 -32 -26 -20 | -15 -10 -6 -2
+// Codebook as byte tables for v_perm_b32 (a selector byte 0..3 picks a byte of
+// the second source, 4..7 a byte of the first), indexed by the magnitude rank:
+//   e4m3 bytes of the magnitudes: 20 2C 32 37 | 3A 3D 40 43 (sign = bit 7)
+//   int8 16*c, positive: 2 6 10 15 | 20 26 32 44; negative: their negations
 // ---------------------------------------------------------------------------
-constexpr uint32_t kE4PosLo = 0x37322C20u, kE4PosHi = 0x43403D3Au;
-constexpr uint32_t kE4NegLo = 0xBABDC0C3u, kE4NegHi = 0xA0ACB2B7u;
+constexpr uint32_t kE4MagLo = 0x37322C20u, kE4MagHi = 0x43403D3Au;
 constexpr uint32_t kI8PosLo = 0x0F0A0602u, kI8PosHi = 0x2C201A14u;
-constexpr uint32_t kI8NegLo = 0xECE6E0D4u, kI8NegHi = 0xFEFAF6F1u;
+constexpr uint32_t kI8NegLo = 0xF1F6FAFEu, kI8NegHi = 0xD4E0E6ECu;
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Four nibbles, one per byte of `t` (the high nibble of each byte is
-// ignored), -> four codebook bytes from the tables (posHi:posLo, negHi:negLo).
-__device__ __forceinline__ uint32_t lut4(uint32_t t, uint32_t posHi, uint32_t posLo,
-                                         uint32_t negHi, uint32_t negLo) {
-  const uint32_t s7 = t & 0x07070707u;
-  const uint32_t p = perm(posHi, posLo, s7);
-  const uint32_t n = perm(negHi, negLo, s7);
-  // byte i of the result: byte i of p if bit 3 of nibble i is set, else of n
-  const uint32_t sel = ((t >> 1) & 0x04040404u) | 0x03020100u;
-  return perm(p, n, sel);
+// Four codes, one in the low nibble of each byte of `t` (high nibbles are
+// ignored) -> four e4m3 bytes: magnitude from the table, sign bit 3 -> bit 7.
+__device__ __forceinline__ uint32_t nib4_to_e4m3(uint32_t t) {
+  const uint32_t mag = perm(kE4MagHi, kE4MagLo, t & 0x07070707u);
+  return mag | ((t << 4) & 0x80808080u);
 }
 
-// Four nibbles -> four fp16 codebook values (two fp16x2 words).
+// Four codes -> four fp16 codebook values (two fp16x2 words).
 __device__ __forceinline__ void nib4_to_f16(uint32_t t, uint32_t &w01, uint32_t &w23) {
-  const uint32_t e = lut4(t, kE4PosHi, kE4PosLo, kE4NegHi, kE4NegLo);
+  const uint32_t e = nib4_to_e4m3(t);
   fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, 1.0f, false);
   fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, 1.0f, true);
   w01 = __builtin_bit_cast(uint32_t, a);
   w23 = __builtin_bit_cast(uint32_t, b);
 }
 
-// One word of 8 nibbles (elements in nibble order 0..7) -> 8 fp16 values as an
+// One word of 8 codes (elements in nibble order 0..7) -> 8 fp16 values as an
 // MFMA operand, in the order (n0 n2 n4 n6 n1 n3 n5 n7): low nibbles first.
 __device__ __forceinline__ half8 word_to_half8(uint32_t w) {
   uint32_t r0, r1, r2, r3;
@@ -77,7 +71,7 @@ __device__ __forceinline__ half8 word_to_half8(uint32_t w) {
   return __builtin_bit_cast(half8, v);
 }
 
-// Low nibbles of two words (8 values) -> one half8 operand; likewise high.
+// Low nibbles of two words (8 values) -> one half8 operand.
 __device__ __forceinline__ half8 lo_nibbles_to_half8(uint32_t w0, uint32_t w1) {
   uint32_t r0, r1, r2, r3;
   nib4_to_f16(w0, r0, r1);
@@ -86,9 +80,14 @@ __device__ __forceinline__ half8 lo_nibbles_to_half8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(half8, v);
 }
 
-// Four nibbles -> four int8 codes 16*c_k.
+// Four codes -> four int8 values 16*c: positive and negative tables looked up
+// by rank, then byte i taken from the negative one when its sign bit is set.
 __device__ __forceinline__ uint32_t nib4_to_i8(uint32_t t) {
-  return lut4(t, kI8PosHi, kI8PosLo, kI8NegHi, kI8NegLo);
+  const uint32_t s7 = t & 0x07070707u;
+  const uint32_t p = perm(kI8PosHi, kI8PosLo, s7);
+  const uint32_t n = perm(kI8NegHi, kI8NegLo, s7);
+  const uint32_t sel = ((t >> 1) & 0x04040404u) | 0x03020100u;
+  return perm(n, p, sel);
 }
 
 // ---------------------------------------------------------------------------

@@ -39,8 +39,8 @@ struct PrefillArgs {
 constexpr int kDecodeTile = 64;
 
 hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs &a, int batch, int q_dtype, int out_dtype,
-                         hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
                           hipStream_t stream);
 

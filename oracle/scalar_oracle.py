@@ -16,8 +16,7 @@ of 4-bit indices; attention in the rotated Hadamard domain).
 import math
 from fractions import Fraction
 
-_LEVELS = [-2.75, -2.0, -1.625, -1.25, -0.9375, -0.625, -0.375, -0.125,
-           0.125, 0.375, 0.625, 0.9375, 1.25, 1.625, 2.0, 2.75]
+_MAGS = [0.125, 0.375, 0.625, 0.9375, 1.25, 1.625, 2.0, 2.75]
 _R = float.fromhex("0x1.6a09e667f3bccp-4")
 _M64 = (1 << 64) - 1
 
@@ -87,8 +86,13 @@ def quantize_block(x, seed=0):
     ms = p[0] * 2.0 ** -7
     dbits = _half_round_sqrt_exact(ms)
     d = float(_half_from_bits(dbits))
-    thr = [(_LEVELS[k] + _LEVELS[k + 1]) / 2.0 for k in range(15)]
-    idx = [sum(1 for t in thr if d * t < ui) for ui in u]
+    # sign-magnitude code: sign bit 3 for negative values, magnitude rank =
+    # number of magnitude midpoints (scaled by d) strictly below |u|
+    tau = [(_MAGS[k] + _MAGS[k + 1]) / 2.0 for k in range(7)]
+    idx = []
+    for ui in u:
+        m = sum(1 for t in tau if d * t < abs(ui))
+        idx.append(m + (8 if ui < 0 else 0))
     out = [dbits & 0xFF, dbits >> 8]
     for j in range(64):
         out.append(idx[2 * j] | (idx[2 * j + 1] << 4))
@@ -104,8 +108,8 @@ def dequantize_block(block, seed=0):
     y = []
     for j in range(64):
         byte = block[2 + j]
-        y.append(d * _LEVELS[byte & 15])
-        y.append(d * _LEVELS[byte >> 4])
+        for code in (byte & 15, byte >> 4):
+            y.append(d * (-_MAGS[code - 8] if code >= 8 else _MAGS[code]))
     h = 1
     while h < 128:
         for i in range(128):

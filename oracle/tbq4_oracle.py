@@ -33,10 +33,15 @@ statistic, the rounding rules or the nibble order.  The readings taken here
                with least mean-square error on N(0,1) under nearest-level
                decisions (the 16-level Lloyd-Max quantiser held to a grid on
                which every level is exact in fp16, bf16 and fp8 e4m3).
-* index      idx_i = #{k in 0..14 : d * t_k < u_i} with t_k the midpoints of
-               adjacent levels (nearest level, ties to the lower index).
-* pack       bytes 0-1 = d (binary16, little endian); byte 2+j holds
-               idx_{2j} in its low nibble and idx_{2j+1} in its high nibble.
+* code       each value becomes a 4-bit sign-magnitude code, laid out like
+               the 4-bit e2m1 float: bit 3 = sign (set for u_i < 0), bits 0-2
+               = m_i = #{k in 0..6 : d * tau_k < |u_i|}, tau_k the midpoints of
+               adjacent magnitudes.  This picks the nearest level; a value
+               exactly between two magnitudes takes the smaller one, and
+               u_i = 0 takes +0.125 d (so an all-zero block packs to zeros).
+* pack       bytes 0-1 = d (binary16, little endian); byte 2+j holds the code
+               of element 2j in its low nibble and of element 2j+1 in its high
+               nibble.
 * attention  plain softmax attention on the dequantised cache; query head h
                reads KV head floor(h / G), G = H_q / H_kv; a prefill query at
                absolute position n_past+i attends keys 0..n_past+i inclusive.
@@ -54,13 +59,15 @@ _MASK64 = (1 << 64) - 1
 # --------------------------------------------------------------------------
 # Codebook: the least-MSE sign-symmetric 16-level quantiser of N(0,1) whose
 # levels have at most four significant bits (it sits next to the 16-level
-# Lloyd-Max levels 0.1284 ... 2.733); thresholds are midpoints of adjacent
-# levels.  Ascending order; c[15-k] == -c[k].
+# Lloyd-Max levels 0.1284 ... 2.733).  CODEBOOK lists the levels in ascending
+# order; a 4-bit code (s, m) stands for (-1)^s * MAGNITUDES[m].
 # --------------------------------------------------------------------------
-_POS_LEVELS = (0.125, 0.375, 0.625, 0.9375, 1.25, 1.625, 2.0, 2.75)
-CODEBOOK = np.array([-v for v in reversed(_POS_LEVELS)] + list(_POS_LEVELS),
-                    dtype=np.float64)
-THRESHOLDS = (CODEBOOK[:-1] + CODEBOOK[1:]) / 2.0      # 15 values, exact
+MAGNITUDES = np.array([0.125, 0.375, 0.625, 0.9375, 1.25, 1.625, 2.0, 2.75], dtype=np.float64)
+CODEBOOK = np.concatenate([-MAGNITUDES[::-1], MAGNITUDES])
+THRESHOLDS = (CODEBOOK[:-1] + CODEBOOK[1:]) / 2.0          # 15 values, exact
+MAG_THRESHOLDS = (MAGNITUDES[:-1] + MAGNITUDES[1:]) / 2.0  # 7 values, exact
+# value of each 4-bit code 0..15
+CODE_VALUES = np.concatenate([MAGNITUDES, -MAGNITUDES])
 
 # fl64(1/sqrt(128)) -- the normalisation of the 128-point transform.
 INV_SQRT128 = float.fromhex("0x1.6a09e667f3bccp-4")
@@ -168,7 +175,7 @@ def quantize_blocks(x, seed=0):
     """Quantise blocks of 128 values to TBQ4.
 
     x: array (..., 128) in fp32 / fp16 / fp64 (converted to fp64 exactly).
-    Returns (packed uint8 (..., 66), idx uint8 (..., 128), d_bits uint16 (...)).
+    Returns (packed uint8 (..., 66), codes uint8 (..., 128), d_bits uint16 (...)).
     """
     signs = sign_vector(seed)
     x = np.asarray(x)
@@ -189,9 +196,11 @@ def quantize_blocks(x, seed=0):
     d_bits = half_nearest_sqrt(ms)
     d = half_bits_to_float(d_bits)
 
-    # idx = number of scaled thresholds strictly below u (d*t_k is exact).
-    thr = d[..., None] * THRESHOLDS                       # (..., 15)
-    idx = (thr[..., None, :] < u[..., :, None]).sum(axis=-1).astype(np.uint8)
+    # code = sign bit | number of scaled magnitude thresholds below |u|
+    # (d * tau_k is exact in fp64)
+    thr = d[..., None] * MAG_THRESHOLDS                   # (..., 7)
+    mag = (thr[..., None, :] < np.abs(u)[..., :, None]).sum(axis=-1)
+    idx = (mag + 8 * (u < 0)).astype(np.uint8)
 
     packed = np.empty(x.shape[:-1] + (BLOCK_BYTES,), dtype=np.uint8)
     packed[..., 0] = (d_bits & 0xFF).astype(np.uint8)
@@ -201,7 +210,7 @@ def quantize_blocks(x, seed=0):
 
 
 def unpack_blocks(packed):
-    """Inverse of the byte layout: returns (idx uint8 (..., 128), d fp64 (...))."""
+    """Inverse of the byte layout: returns (codes uint8 (..., 128), d fp64 (...))."""
     packed = np.asarray(packed, dtype=np.uint8)
     if packed.shape[-1] != BLOCK_BYTES:
         raise ValueError("last axis must be 66 bytes")
@@ -214,9 +223,9 @@ def unpack_blocks(packed):
 
 
 def dequantize_rotated(packed):
-    """y = d * c[idx]: the block's values in the rotated domain (fp64, exact)."""
+    """y = d * value(code): the block's values in the rotated domain (fp64, exact)."""
     idx, d = unpack_blocks(packed)
-    return d[..., None] * CODEBOOK[idx]
+    return d[..., None] * CODE_VALUES[idx]
 
 
 def dequantize_blocks(packed, seed=0):

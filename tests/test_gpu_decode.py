@@ -168,3 +168,25 @@ def test_decode128k_workload_sampled():
                                      o.dequantize_blocks(vc), w.softmax_scale)
         for P, out in outs.items():
             check_attn(out[b, g * G:(g + 1) * G], ref, True, f"128k b={b} g={g} P={P}")
+
+
+def test_two_phase_equals_one_call():
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((2, 1500, 2, 128)).astype(np.float32)
+    cache = tb.KVCache(2, 2, 1504, sign_seed=4)
+    _fill(cache, k, k)
+    q = torch.from_numpy(rng.standard_normal((2, 16, 128)).astype(np.float32)).cuda()
+    one = tb.attn_decode(cache, q, 1500, 0.1, n_splits=6)
+    ws, used = tb.attn_decode_partial(cache, q, 1500, 0.1, n_splits=6)
+    assert used == 6
+    two = tb.attn_decode_merge(ws, 2, 16, used, sign_seed=4)
+    assert torch.equal(one, two)
+    # the partial states follow the documented layout: merging them on the
+    # host reproduces the output
+    wsf = ws[:2 * 16 * 6 * 130 * 4].view(torch.float32).view(2, 16, 6, 130).cpu().double().numpy()
+    M = wsf[..., 0].max(axis=2, keepdims=True)
+    wgt = np.exp2(wsf[..., 0:1] - M[..., None])
+    L = (wgt[..., 0] * wsf[..., 1]).sum(axis=2)
+    Or = (wgt * wsf[..., 2:]).sum(axis=2) / L[..., None]
+    host = o.unrotate(Or, o.sign_vector(4))
+    np.testing.assert_allclose(host, one.float().cpu().numpy(), atol=2e-3)

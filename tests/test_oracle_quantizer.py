@@ -203,23 +203,43 @@ def test_codebook_is_best_four_significant_bit_codebook():
     assert g["mse"] < _gauss_mse(o.CODEBOOK) < 1.03 * g["mse"]
 
 
-# ---------------------------------------------------------------- index rule
-def test_index_is_nearest_level_lowest_on_ties():
+# ---------------------------------------------------------------- code rule
+def _levels_toward_zero_first():
+    """Levels ordered (+0.125, -0.125, +0.375, -0.375, ...): argmin over this
+    order breaks distance ties toward the smaller magnitude, and at 0 toward +."""
+    lv = []
+    for m in o.MAGNITUDES:
+        lv += [m, -m]
+    return np.array(lv)
+
+
+def test_code_is_nearest_level_ties_toward_zero():
     rng = np.random.default_rng(4)
     x = rng.standard_normal((300, 128)) * rng.uniform(0.01, 100, size=(300, 1))
-    _, idx, d_bits = o.quantize_blocks(x.astype(np.float32))
+    _, codes, d_bits = o.quantize_blocks(x.astype(np.float32))
     u = o.rotate(x.astype(np.float32).astype(np.float64), o.sign_vector(0))
     d = o.half_bits_to_float(d_bits)
-    dist = np.abs(u[..., None] - d[:, None, None] * o.CODEBOOK)
-    assert np.array_equal(idx, np.argmin(dist, axis=-1))
+    lv = _levels_toward_zero_first()
+    nearest = lv[np.argmin(np.abs(u[..., None] - d[:, None, None] * lv), axis=-1)]
+    assert np.array_equal(o.CODE_VALUES[codes] * d[:, None], nearest * d[:, None])
+    # the code's sign bit is the sign of u; its magnitude rank is the level's
+    assert np.array_equal(codes >= 8, u < 0)
+    assert np.array_equal(o.MAGNITUDES[codes & 7], np.abs(nearest))
 
 
-def test_index_exact_threshold_goes_low():
-    # u exactly on a threshold (u = d * t_k) must take index k (the lower level).
+def test_code_exact_ties_and_zero():
+    # |u| exactly on the midpoint between magnitudes m and m+1 takes m, for
+    # either sign; u = 0 takes +0.125 (code 0).
     d = 0.5
-    for k, t in enumerate(o.THRESHOLDS):
+    for k, t in enumerate(o.MAG_THRESHOLDS):
         u = d * t
-        assert int((d * o.THRESHOLDS < u).sum()) == k
+        assert int((d * o.MAG_THRESHOLDS < abs(u)).sum()) == k
+        assert int((d * o.MAG_THRESHOLDS < abs(-u)).sum()) == k
+    packed, codes, d_bits = o.quantize_blocks(np.zeros((1, 128)))
+    assert np.all(codes == 0) and np.all(packed == 0)
+    assert np.array_equal(o.CODE_VALUES, np.concatenate([o.MAGNITUDES, -o.MAGNITUDES]))
+    assert np.array_equal(np.sort(o.CODE_VALUES), o.CODEBOOK)
+    assert np.array_equal(o.MAG_THRESHOLDS, o.THRESHOLDS[8:])
 
 
 # ---------------------------------------------------------------- known blocks
@@ -294,4 +314,4 @@ def test_unpack_inverts_pack():
     y = o.dequantize_rotated(packed)
     for r in range(3):
         for i in range(128):
-            assert y[r, i] == float(Fraction(d[r]) * Fraction(o.CODEBOOK[idx[r, i]]))
+            assert y[r, i] == float(Fraction(d[r]) * Fraction(o.CODE_VALUES[idx[r, i]]))

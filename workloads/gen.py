@@ -136,9 +136,12 @@ def kv_tensor(w, layer, tensor, t0, t1, workers=None):
         for j in jobs:
             out[j[3], :, j[4]] = _rows_job(j)
     else:
+        # worker processes are stopped by a sentinel, not a signal, so the
+        # pool also shuts down cleanly under a profiler
         import multiprocessing as mp
-        with mp.get_context("spawn").Pool(n) as pool:
-            for j, rows in zip(jobs, pool.imap(_rows_job, jobs)):
+        from concurrent.futures import ProcessPoolExecutor
+        with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn")) as ex:
+            for j, rows in zip(jobs, ex.map(_rows_job, jobs)):
                 out[j[3], :, j[4]] = rows
     return out
 
