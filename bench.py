@@ -14,8 +14,9 @@ queries on 131072 cached tokens, 8 KV / 64 query heads, append of the chunk's
 K/V then causal attention) is timed in the same run and reported under
 "prefill" in TFLOP/s (4 * 128 * 64 FLOPs per unmasked (query, key) pair).
 
-The dominant kernel's roofline entry uses HIP events recorded on the stream
-the kernels run on, around every decode-partial launch of the timed region.
+The dominant kernel's roofline entry uses HIP events on the stream the kernels
+run on, recorded by the dispatch of every decode-partial launch of the timed
+region (start and end of that kernel's execution).
 The CPU oracle is timed on a bounded sample of the same workload (rows of the
 decode cache, fp64 dequantise + attention) on the host's cores.
 
@@ -32,6 +33,31 @@ import time
 import numpy as np
 
 METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
+
+# HBM bytes per decode_split_kernel launch on this workload (64 splits), from
+# two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch)
+# scaled by what the same counters read for a plain 256 MiB device copy
+# (FETCH_SIZE reads half the copied bytes -> x2.0; WRITE_SIZE reads them all
+# -> x1.0).  Reported only while the kernel's sources hash to the version the
+# counters were taken on; otherwise the traffic is unknown (null).
+KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
+TRAFFIC = {"sources_sha256": "0a83bf0e2e61626cac8607faa4d79482a25b086b97c4d88084ed1bb443631222",
+           "n_splits": 64, "fetch_kib": 271359.6, "fetch_factor": 2.0,
+           "write_kib": 8704.0, "write_factor": 1.0}
+
+
+def measured_traffic(n_splits):
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                       "long_context_attention_tbq4_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != TRAFFIC["sources_sha256"] or n_splits != TRAFFIC["n_splits"]:
+        return None
+    return round(1024 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_factor"]
+                         + TRAFFIC["write_kib"] * TRAFFIC["write_factor"]))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 
@@ -45,11 +71,52 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB five times "
+                        "(reference for the profiler's byte counters) and exit")
     return p.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Timing events of the HIP runtime torch already loaded, handed to the
+    library so that the kernel dispatch itself records them."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def pair(self, i):
+        return self.ev[2 * i], self.ev[2 * i + 1]
+
+    def elapsed_ms(self):
+        out = []
+        for i in range(len(self.ev) // 2):
+            ms = self.ct.c_float()
+            rc = self.rt.hipEventElapsedTime(self.ct.byref(ms), self.ev[2 * i], self.ev[2 * i + 1])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            out.append(ms.value)
+        return out
+
+    def destroy(self):
+        for e in self.ev:
+            self.rt.hipEventDestroy(e)
+        self.ev = []
 
 
 def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768):
@@ -77,50 +144,38 @@ def bench_decode(tb, torch, args):
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
     P = args.splits or tb.decode_auto_splits(B, Hkv, T)
     ws = torch.empty(tb.decode_workspace_bytes(B, Hkv, Hq, T, P), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    hip = HipEvents(args.steps)
+
+    def step(i=None):
         tb.quantize_append(cache, k_new, v_new, T - 1)
-        if ev is not None:
-            ev[0].record(stream)
-        tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+        tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws,
+                               events=None if i is None else hip.pair(i))
         tb.attn_decode_merge(ws, B, Hq, P, cache.sign_seed, out=out)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the dominant kernel alone: the same partial launch repeated back to
-    # back between two events (single-launch events add the marker gap)
-    kb = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    kb[0].record(stream)
-    for _ in range(args.steps):
-        tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
-    kb[1].record(stream)
-    torch.cuda.synchronize()
-    kern_back_to_back = kb[0].elapsed_time(kb[1]) / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = hip.elapsed_ms()
+    hip.destroy()
     kv_bytes = B * T * Hkv * 2 * 66
     q_bytes = B * Hq * 128 * 4
     out_bytes = B * Hq * 128 * 2
     append_bytes = 2 * B * Hkv * 128 * 4 + 2 * B * Hkv * 66
     step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
     ms = wall * 1e3 / args.steps
-    kern_avg = kern_back_to_back
+    kern_avg = float(np.mean(kern_ms))
     achieved = (kv_bytes + q_bytes) / (kern_avg * 1e-3) / 1e9
     assert torch.isfinite(out.float()).all()
     return {
         "P": P, "ms": ms, "value": step_bytes / (ms * 1e-3) / 1e9,
-        "kernel_ms": kern_avg, "kernel_ms_in_step": float(np.mean(kern_ms)),
-        "kernel_ms_in_step_p90": float(np.percentile(kern_ms, 90)),
+        "kernel_ms": kern_avg, "kernel_ms_min": float(np.min(kern_ms)),
+        "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
         "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
         "tokens_per_s": B * T / (ms * 1e-3),
     }
@@ -216,6 +271,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
     dec = bench_decode(tb, torch, args)
     log(f"decode: {dec['ms']:.4f} ms/step, kernel {dec['kernel_ms']:.4f} ms, "
         f"{dec['achieved']:.0f} GB/s")
@@ -251,10 +315,12 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dec["P"]),
             "kernel_ms": round(dec["kernel_ms"], 5),
-            "kernel_ms_in_step": round(dec["kernel_ms_in_step"], 5),
-            "kernel_ms_in_step_p90": round(dec["kernel_ms_in_step_p90"], 5),
+            "kernel_ms_min": round(dec["kernel_ms_min"], 5),
+            "kernel_ms_p90": round(dec["kernel_ms_p90"], 5),
+            "timing": "HIP events recorded by the split kernel's own dispatch "
+                      "(hipExtLaunchKernel) on every timed step",
         },
         "cpu_baseline": cpu,
         "prefill": pre,

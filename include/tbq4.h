@@ -166,6 +166,18 @@ tbq4_status tbq4_attn_decode_partial(const tbq4_cache *cache, const void *q, tbq
                                      int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
                                      int32_t n_splits, int32_t *n_splits_used, void *workspace,
                                      size_t workspace_bytes, void *hip_stream);
+/* tbq4_attn_decode_partial_timed: tbq4_attn_decode_partial plus two optional
+ * HIP events (hipEvent_t, created by the caller with timing enabled; either
+ * may be NULL).  The split kernel's own dispatch records them at the start and
+ * at the end of its execution, so hipEventElapsedTime on the pair gives the
+ * kernel's duration without the latency of separate event markers.  For
+ * callers that time the kernel in production without a profiler. */
+tbq4_status tbq4_attn_decode_partial_timed(const tbq4_cache *cache, const void *q,
+                                           tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_ctx,
+                                           float softmax_scale, int32_t n_splits,
+                                           int32_t *n_splits_used, void *workspace,
+                                           size_t workspace_bytes, void *hip_stream,
+                                           void *start_event, void *stop_event);
 tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes, int32_t batch,
                                    int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
                                    void *out, tbq4_dtype out_dtype, void *hip_stream);

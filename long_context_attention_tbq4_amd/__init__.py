@@ -144,9 +144,13 @@ def attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None, out_dtype=
     return out
 
 
-def attn_decode_partial(cache, q, n_ctx, softmax_scale, n_splits=0, workspace=None):
+def attn_decode_partial(cache, q, n_ctx, softmax_scale, n_splits=0, workspace=None,
+                        events=None):
     """First decode phase: per-split partial softmax states into `workspace`
-    (layout in include/tbq4.h).  Returns (workspace, n_splits_used)."""
+    (layout in include/tbq4.h).  Returns (workspace, n_splits_used).
+
+    ``events``: optional (start, stop) raw hipEvent_t handles (ints); the split
+    kernel's dispatch records them at its start and end."""
     _require(q, "q")
     B, Hq, D = q.shape
     need = decode_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, n_ctx, n_splits)
@@ -154,10 +158,18 @@ def attn_decode_partial(cache, q, n_ctx, softmax_scale, n_splits=0, workspace=No
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     used = ctypes.c_int32(0)
     d = cache.descriptor()
-    _check(_lib.lib().tbq4_attn_decode_partial(
-        ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx, float(softmax_scale), n_splits,
-        ctypes.byref(used), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(q.device)), "tbq4_attn_decode_partial")
+    nbytes = workspace.numel() * workspace.element_size()
+    if events is None:
+        _check(_lib.lib().tbq4_attn_decode_partial(
+            ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx, float(softmax_scale), n_splits,
+            ctypes.byref(used), _ptr(workspace), nbytes, _stream(q.device)),
+            "tbq4_attn_decode_partial")
+    else:
+        _check(_lib.lib().tbq4_attn_decode_partial_timed(
+            ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx, float(softmax_scale), n_splits,
+            ctypes.byref(used), _ptr(workspace), nbytes, _stream(q.device),
+            ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1])),
+            "tbq4_attn_decode_partial_timed")
     return workspace, used.value
 
 

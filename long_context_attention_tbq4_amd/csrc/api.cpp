@@ -219,6 +219,22 @@ tbq4_status tbq4_attn_decode_partial(const tbq4_cache *cache, const void *q, tbq
                                               (hipStream_t)hip_stream));
 }
 
+tbq4_status tbq4_attn_decode_partial_timed(const tbq4_cache *cache, const void *q,
+                                           tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_ctx,
+                                           float softmax_scale, int32_t n_splits,
+                                           int32_t *n_splits_used, void *workspace,
+                                           size_t workspace_bytes, void *hip_stream,
+                                           void *start_event, void *stop_event) {
+  tbq4::DecodeArgs a;
+  tbq4_status s = prepare_decode(cache, q, q_dtype, n_q_heads, n_ctx, softmax_scale, n_splits,
+                                 workspace, workspace_bytes, a);
+  if (s != TBQ4_OK) return s;
+  if (n_splits_used) *n_splits_used = a.n_splits;
+  return from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype,
+                                              (hipStream_t)hip_stream, (hipEvent_t)start_event,
+                                              (hipEvent_t)stop_event));
+}
+
 tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes, int32_t batch,
                                    int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
                                    void *out, tbq4_dtype out_dtype, void *hip_stream) {

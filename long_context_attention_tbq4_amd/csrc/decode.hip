@@ -28,6 +28,8 @@
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
 
+#include <hip/hip_ext.h>
+
 namespace tbq4 {
 
 constexpr int kTile = kDecodeTile;  // tokens per loop iteration
@@ -60,6 +62,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int col = lane & 15;           // MFMA column: query head (col & 7), part col >> 3
   const int head = col & 7;
   const bool lo_part = col >= 8;
+  const float lo_mask = lo_part ? 1.0f : 0.0f;
 
   // ---------------- q' = R q * scale * log2(e), split into fp16 hi + residual
   float qv[32];
@@ -150,8 +153,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // Raw fetch of one 64-token tile: per 16-token group, 5 words of K and of V
   // covering this lane's 16 index bytes (start offsets are even, so the words
   // are realigned by 0 or 2 bytes -- a per-lane constant), plus the scales of
-  // token `lane`.  Two fetch buffers alternate: the next tile's fetch is in
-  // flight while the current tile is processed.  A tile past the end of the
+  // token `lane`.  The next tile is fetched into the same registers as soon as
+  // the current tile's raw words are consumed (K realigned into registers, V
+  // and the scales staged in LDS), so it is in flight during the scores,
+  // softmax and PV work of the current tile.  A tile past the end of the
   // split is fetched at an offset beyond the buffer range, which the hardware
   // turns into zeros without a memory access, so every fetch is issued
   // unconditionally and the wait counts stay exact.
@@ -176,7 +181,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     r.sv = buf_load_u16(rv, base + (uint32_t)lane * kBlockBytes);
   };
 
-  auto process = [&](const Raw &r, int t) {
+  auto process = [&](Raw &r, int t) {
     const int tok0 = t * kTile;
     uint32_t kw[4][4];
 #pragma unroll
@@ -198,9 +203,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     sk[lane] = half_bits_to_float(r.sk) * qs_inv;
     sv[lane] = half_bits_to_float(r.sv);
+    fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
 
-    // ---- scores S^T[token][col] = K . q'
-    float s[4][4];
+    // ---- scores S^T[token][col] = K . q' (fp16 high + residual columns
+    // added back together by a 16-lane rotation)
+    float acc_s[4][4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       float4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -208,36 +215,44 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       for (int c = 0; c < 4; ++c)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(word_to_half8(kw[blk][c]), qop[c], acc, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[blk][e] = acc[e] + row_ror8(acc[e]);
+      for (int e = 0; e < 4; ++e) acc_s[blk][e] = acc[e] + row_ror8(acc[e]);
     }
     __syncthreads();   // staged V rows and scales are visible
 
+    // t = score - m_ref with the running max updated lazily: m_ref is the
+    // running max (0 before the first tile), and only a tile holding a score
+    // above it -- and the first tile -- takes the rescaling path, which
+    // recovers the scores as t + m_ref.
+    const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
+    float t4[4][4];
+    float tmax = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const float4v kd = *(const float4v *)(sk + 16 * blk + 4 * quarter);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[blk][e] *= kd[e];
+      for (int e = 0; e < 4; ++e) {
+        t4[blk][e] = fmaf(acc_s[blk][e], kd[e], -m_ref);
+        tmax = fmaxf(tmax, t4[blk][e]);
+      }
     }
     if (tok0 + kTile > a.n_ctx) {        // only the last tile holds tokens >= n_ctx
+      tmax = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s[blk][e] += (tok0 + 16 * blk + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          t4[blk][e] += (tok0 + 16 * blk + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
+          tmax = fmaxf(tmax, t4[blk][e]);
+        }
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s[blk][e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // rescale the accumulators when some head's running max moved
-    if (__any(alpha != 1.0f)) {
+    if (__any(tmax > 0.0f || m_run == -INFINITY)) {
+      float smax = tmax + m_ref;
+      smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+      const float m_new = fmaxf(m_run, smax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
       float al[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, (4 * quarter + e) & 7, 64);
@@ -245,25 +260,40 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[i][e] *= al[e];
+      const float shift_t = m_ref - m_new;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t4[blk][e] += shift_t;
     }
 
-    // ---- probabilities, folded V scale, fp16 hi / residual operands
+    // ---- probabilities, folded V scale, fp16 high part (columns 0-7) or
+    // fp16 residual (columns 8-15): x - lo_mask * hi, rounded toward zero
     float psum = 0.0f;
-    half8 pa[2];
+    uint32_t pw[2][4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const float4v vd = *(const float4v *)(sv + 16 * blk + 4 * quarter);
+      float pt[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[blk][e] - m_new);
+        const float p = __builtin_amdgcn_exp2f(t4[blk][e]);
         psum += p;
-        const float pt = p * vd[e];
-        const _Float16 hi = (_Float16)pt;
-        const _Float16 lo = (_Float16)(pt - (float)hi);
-        pa[blk >> 1][4 * (blk & 1) + e] = lo_part ? lo : hi;
+        pt[e] = p * vd[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(pt[e], pt[e + 1]);
+        const float r0 = fmaf(-(float)h[0], lo_mask, pt[e]);
+        const float r1 = fmaf(-(float)h[1], lo_mask, pt[e + 1]);
+        pw[blk >> 1][2 * (blk & 1) + (e >> 1)] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
       }
     }
-    l_run = l_run * alpha + psum;
+    l_run += psum;
+    half8 pa[2];
+    pa[0] = __builtin_bit_cast(half8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
+    pa[1] = __builtin_bit_cast(half8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
 
     // ---- O'^T += P~ V  (V read back transposed: 8 tokens x 1 byte per lane)
 #pragma unroll
@@ -282,14 +312,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  Raw ra, rb;
-  fetch(ra, t_begin);
-  for (int t = t_begin; t < t_end; t += 2) {
-    fetch(rb, t + 1);
-    process(ra, t);
-    fetch(ra, t + 2);
-    if (t + 1 < t_end) process(rb, t + 1);
-  }
+  Raw r;
+  fetch(r, t_begin);
+  for (int t = t_begin; t < t_end; ++t) process(r, t);
 
   // ---------------- partial state of this split
   l_run += __shfl_xor(l_run, 16, 64);
@@ -404,13 +429,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   dst[lane + 64] = (OT)o1;
 }
 
-hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream) {
+hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
+                                 hipEvent_t start, hipEvent_t stop) {
   dim3 grid(a.n_splits, a.n_kv_heads, batch);
-  if (q_dtype == 0)
-    hipLaunchKernelGGL(decode_split_kernel<float>, grid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<_Float16>, grid, dim3(64), 0, stream, a);
-  return hipGetLastError();
+  const void *fn = q_dtype == 0 ? reinterpret_cast<const void *>(&decode_split_kernel<float>)
+                                : reinterpret_cast<const void *>(&decode_split_kernel<_Float16>);
+  DecodeArgs arg = a;
+  void *params[] = {&arg};
+  if (start || stop)
+    return hipExtLaunchKernel(fn, grid, dim3(64), params, 0, stream, start, stop, 0);
+  return hipLaunchKernel(fn, grid, dim3(64), params, 0, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream) {

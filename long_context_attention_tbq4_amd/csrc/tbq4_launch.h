@@ -39,7 +39,9 @@ struct PrefillArgs {
 constexpr int kDecodeTile = 64;
 
 hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream);
-hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream);
+// With start/stop events the dispatch itself records them (hipExtLaunchKernel).
+hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
+                                 hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
                           hipStream_t stream);

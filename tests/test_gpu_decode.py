@@ -190,3 +190,34 @@ def test_two_phase_equals_one_call():
     Or = (wgt * wsf[..., 2:]).sum(axis=2) / L[..., None]
     host = o.unrotate(Or, o.sign_vector(4))
     np.testing.assert_allclose(host, one.float().cpu().numpy(), atol=2e-3)
+
+
+def test_timed_partial_matches_and_records_events():
+    """The timed variant writes the same partial states and its dispatch
+    records both events (elapsed time positive and finite)."""
+    import ctypes
+    rt = ctypes.CDLL("libamdhip64.so.7")
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal((1, 2000, 2, 128)).astype(np.float32)
+    cache = tb.KVCache(1, 2, 2000)
+    _fill(cache, k, k)
+    q = torch.from_numpy(rng.standard_normal((1, 16, 128)).astype(np.float32)).cuda()
+    ws0, used0 = tb.attn_decode_partial(cache, q, 2000, 0.1, n_splits=5)
+    ws1, used1 = tb.attn_decode_partial(cache, q, 2000, 0.1, n_splits=5,
+                                        events=(ev[0].value, ev[1].value))
+    torch.cuda.synchronize()
+    n = 1 * 16 * 5 * 130 * 4
+    assert used0 == used1 == 5
+    assert torch.equal(ws0[:n], ws1[:n])
+    ms = ctypes.c_float()
+    assert rt.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    assert 0.0 < ms.value < 1000.0
+    for e in ev:
+        rt.hipEventDestroy(e)
