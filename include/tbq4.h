@@ -155,8 +155,8 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
  *   [1] l  = sum over the split's keys of 2^(score - m)
  *   [2 + i] = sum over the split's keys of 2^(score - m) * v'_i, i = 0..127,
  *          in the ROTATED domain (v' = R v, unnormalised).
- * Split p covers the 64-token tiles [p * T, (p + 1) * T), T = ceil(ceil(n_ctx
- * / 64) / n_splits); with n_splits = 0 the automatic count is used and
+ * Split p covers the 32-token tiles [p * T, (p + 1) * T), T = ceil(ceil(n_ctx
+ * / 32) / n_splits); with n_splits = 0 the automatic count is used and
  * returned through *n_splits_used (may be NULL).
  *
  * tbq4_attn_decode_merge: out[b][h] = R^T (sum_p 2^(m_p - M) o_p / sum_p

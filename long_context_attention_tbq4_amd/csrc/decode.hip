@@ -8,12 +8,12 @@
 // o' = sum_j p_j d^V_j c^V_j, o = R^T o' (R orthogonal).
 //
 // Work split (flash decoding): one wavefront per (sequence, KV head, split)
-// streams a contiguous run of 64-token tiles and writes a partial softmax
+// streams a contiguous run of 32-token tiles and writes a partial softmax
 // state (m, l, o'[128]) for each of the G query heads of that KV head; a
 // second kernel merges the splits, normalises, applies R^T and stores.
 //
-// Per 64-token tile a wavefront
-//   * fetches 4 x 16 tokens of K and V with 16-byte-per-lane buffer loads
+// Per 32-token tile a wavefront
+//   * fetches 2 x 16 tokens of K and V with 16-byte-per-lane buffer loads
 //     (lane = token x 32-dimension quarter; a 16-token group is one
 //     contiguous 1056-byte run, so every fetched line is fully used),
 //   * S^T = K Q'^T on v_mfma_f32_16x16x32_f16: K nibbles go straight from
@@ -33,7 +33,8 @@
 namespace tbq4 {
 
 constexpr int kTile = kDecodeTile;  // tokens per loop iteration
-constexpr int kVRow = 80;        // LDS bytes per staged V row (64 + pad)
+constexpr int kBlk = kTile / 16;    // 16-token MFMA row blocks per tile
+constexpr int kVRow = 80;           // LDS bytes per staged V row (64 + pad)
 
 
 __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
@@ -140,17 +141,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // transposed-read source addresses (fixed per lane): lane s of 16-lane group
+  // transposed-read source address (fixed per lane): lane s of 16-lane group
   // G4 points at token tau(G4, s/2), byte 8*(s&1) of a 16-byte column group
-  int tr_off[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  int tr_off;
+  {
     const int e = col >> 1;
-    const int tok = 32 * kk + 16 * (e >> 2) + 4 * quarter + (e & 3);
-    tr_off[kk] = tok * kVRow + 8 * (col & 1);
+    const int tok = 16 * (e >> 2) + 4 * quarter + (e & 3);
+    tr_off = tok * kVRow + 8 * (col & 1);
   }
 
-  // Raw fetch of one 64-token tile: per 16-token group, 5 words of K and of V
+  // Raw fetch of one 32-token tile: per 16-token group, 5 words of K and of V
   // covering this lane's 16 index bytes (start offsets are even, so the words
   // are realigned by 0 or 2 bytes -- a per-lane constant), plus the scales of
   // token `lane`.  The next tile is fetched into the same registers as soon as
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // turns into zeros without a memory access, so every fetch is issued
   // unconditionally and the wait counts stay exact.
   struct Raw {
-    u32x4 k4[4], v4[4];
-    uint32_t k1[4], v1[4];
+    u32x4 k4[kBlk], v4[kBlk];
+    uint32_t k1[kBlk], v1[kBlk];
     uint16_t sk, sv;
   };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
@@ -170,22 +170,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   auto fetch = [&](Raw &r, int t) {
     const uint32_t base = t < t_end ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < kBlk; ++blk) {
       const uint32_t a = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
       r.k4[blk] = buf_load_x4(rk, a);
       r.k1[blk] = buf_load_x1(rk, a + 16);
       r.v4[blk] = buf_load_x4(rv, a);
       r.v1[blk] = buf_load_x1(rv, a + 16);
     }
-    r.sk = buf_load_u16(rk, base + (uint32_t)lane * kBlockBytes);
-    r.sv = buf_load_u16(rv, base + (uint32_t)lane * kBlockBytes);
+    const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
+    r.sk = buf_load_u16(rk, soff);
+    r.sv = buf_load_u16(rv, soff);
   };
 
   auto process = [&](Raw &r, int t) {
     const int tok0 = t * kTile;
-    uint32_t kw[4][4];
+    uint32_t kw[kBlk][4];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < kBlk; ++blk) {
       const u32x4 w = r.k4[blk];
       kw[blk][0] = alignbyte(w[1], w[0], shift);
       kw[blk][1] = alignbyte(w[2], w[1], shift);
@@ -195,21 +196,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
     __syncthreads();   // previous tile's LDS reads are done
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < kBlk; ++blk) {
       const u32x4 w = r.v4[blk];
       const u32x4 a = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
                        alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
       *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
     }
-    sk[lane] = half_bits_to_float(r.sk) * qs_inv;
-    sv[lane] = half_bits_to_float(r.sv);
+    if (lane < kTile) {
+      sk[lane] = half_bits_to_float(r.sk) * qs_inv;
+      sv[lane] = half_bits_to_float(r.sv);
+    }
     fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
 
     // ---- scores S^T[token][col] = K . q' (fp16 high + residual columns
     // added back together by a 16-lane rotation)
-    float acc_s[4][4];
+    float acc_s[kBlk][4];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < kBlk; ++blk) {
       float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -224,10 +227,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // above it -- and the first tile -- takes the rescaling path, which
     // recovers the scores as t + m_ref.
     const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
-    float t4[4][4];
+    float t4[kBlk][4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < kBlk; ++blk) {
       const float4v kd = *(const float4v *)(sk + 16 * blk + 4 * quarter);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (tok0 + kTile > a.n_ctx) {        // only the last tile holds tokens >= n_ctx
       tmax = -INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int blk = 0; blk < kBlk; ++blk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           t4[blk][e] += (tok0 + 16 * blk + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) o[i][e] *= al[e];
       const float shift_t = m_ref - m_new;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int blk = 0; blk < kBlk; ++blk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) t4[blk][e] += shift_t;
     }
@@ -270,9 +273,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // ---- probabilities, folded V scale, fp16 high part (columns 0-7) or
     // fp16 residual (columns 8-15): x - lo_mask * hi, rounded toward zero
     float psum = 0.0f;
-    uint32_t pw[2][4];
+    uint32_t pw[kBlk / 2][4];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < kBlk; ++blk) {
       const float4v vd = *(const float4v *)(sv + 16 * blk + 4 * quarter);
       float pt[4];
 #pragma unroll
@@ -291,18 +294,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
     l_run += psum;
-    half8 pa[2];
-    pa[0] = __builtin_bit_cast(half8, u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]});
-    pa[1] = __builtin_bit_cast(half8, u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]});
+    half8 pa[kBlk / 2];
+#pragma unroll
+    for (int kk = 0; kk < kBlk / 2; ++kk)
+      pa[kk] = __builtin_bit_cast(half8, u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
 
     // ---- O'^T += P~ V  (V read back transposed: 8 tokens x 1 byte per lane)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kBlk / 2; ++kk) {
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
         typedef __attribute__((address_space(3))) int2v lds_i2;
         const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i2 *)(vlds + tr_off[kk] + 16 * cg));
+            (lds_i2 *)(vlds + tr_off + 32 * kk * kVRow + 16 * cg));
         const uint32_t w0 = (uint32_t)r[0], w1 = (uint32_t)r[1];
         const half8 ve = lo_nibbles_to_half8(w0, w1);
         const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);

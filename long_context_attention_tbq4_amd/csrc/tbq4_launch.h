@@ -36,7 +36,7 @@ struct PrefillArgs {
   uint32_t sign[4];
 };
 
-constexpr int kDecodeTile = 64;
+constexpr int kDecodeTile = 32;
 
 hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream);
 // With start/stop events the dispatch itself records them (hipExtLaunchKernel).
