@@ -20,15 +20,18 @@
 //     registers to fp16 operands (byte-permute LUT -> e4m3 -> fp16); the 16
 //     MFMA columns hold the G <= 8 query heads twice, as an fp16 high part
 //     and the fp16 residual, so the scores carry ~22 bits of q,
+//   * finishes each (head, token) score once: the lanes of MFMA columns 0-7
+//     take the first 16-token block, those of columns 8-15 the second,
 //   * stages the V index bytes in LDS and reads them back transposed with
 //     ds_read_b64_tr_b8 (8 tokens x 1 byte per lane), dequantises them the
-//     same way and runs O'^T += P~ V on MFMA, with P~ = p d^V again split
-//     into fp16 high and residual rows,
+//     same way and runs O'^T += P~ V on MFMA, with P~ = p d^V rounded to
+//     fp16 (rows 8-15 of the P~ operand are zero),
 //   * keeps the online-softmax state in the log2 domain.
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
 
 #include <hip/hip_ext.h>
+#include <type_traits>
 
 namespace tbq4 {
 
@@ -54,7 +57,7 @@ template <typename QT>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
   __shared__ __attribute__((aligned(16))) float sk[kTile];   // d^K * 2^-ex per token
-  __shared__ __attribute__((aligned(16))) float sv[kTile];   // d^V per token
+  __shared__ __attribute__((aligned(16))) float sv[kTile + 32];   // d^V per token, then zeros
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -63,7 +66,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int col = lane & 15;           // MFMA column: query head (col & 7), part col >> 3
   const int head = col & 7;
   const bool lo_part = col >= 8;
-  const float lo_mask = lo_part ? 1.0f : 0.0f;
+  static_assert(kBlk == 2, "the score split between lanes 0-7 and 8-15 pairs two blocks");
+  // lanes of P~ rows 8-15 read zero V scales
+  const float *sv_rd = lo_part ? sv + kTile : sv;
+  if (lane < 32) sv[kTile + lane] = 0.0f;
 
   // ---------------- q' = R q * scale * log2(e), split into fp16 hi + residual
   float qv[32];
@@ -182,7 +188,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     r.sv = buf_load_u16(rv, soff);
   };
 
-  auto process = [&](Raw &r, int t) {
+  // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
+  // context); full tiles carry no masking code at all
+  auto process = [&](Raw &r, int t, auto partial_tag) {
+    constexpr bool kPartial = decltype(partial_tag)::value;
     const int tok0 = t * kTile;
     uint32_t kw[kBlk][4];
 #pragma unroll
@@ -208,17 +217,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
 
-    // ---- scores S^T[token][col] = K . q' (fp16 high + residual columns
-    // added back together by a 16-lane rotation)
-    float acc_s[kBlk][4];
+    // ---- scores S^T[token][col] = K . q'.  The fp16 high-part (columns
+    // 0-7) and residual (columns 8-15) partial sums of a head are added by a
+    // 16-lane rotation, and the two 16-token blocks share the work: lanes
+    // 0-7 of each row finish block 0, lanes 8-15 block 1, so every lane
+    // carries 4 distinct scores (head `head`, tokens 16 * own + 4 * quarter + e).
+    float4v acc[kBlk];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      acc[blk] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(word_to_half8(kw[blk][c]), qop[c], acc, 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(word_to_half8(kw[blk][c]), qop[c],
+                                                          acc[blk], 0, 0, 0);
+    }
+    float sc[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc_s[blk][e] = acc[e] + row_ror8(acc[e]);
+    for (int e = 0; e < 4; ++e) {
+      const float mine = lo_part ? acc[1][e] : acc[0][e];
+      const float give = lo_part ? acc[0][e] : acc[1][e];   // what the partner lane needs
+      sc[e] = mine + row_ror8(give);
     }
     __syncthreads();   // staged V rows and scales are visible
 
@@ -226,30 +244,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // running max (0 before the first tile), and only a tile holding a score
     // above it -- and the first tile -- takes the rescaling path, which
     // recovers the scores as t + m_ref.
+    const int own = lo_part ? 1 : 0;
     const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
-    float t4[kBlk][4];
+    float t4[4];
     float tmax = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < kBlk; ++blk) {
-      const float4v kd = *(const float4v *)(sk + 16 * blk + 4 * quarter);
+    {
+      const float4v kd = *(const float4v *)(sk + 16 * own + 4 * quarter);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        t4[blk][e] = fmaf(acc_s[blk][e], kd[e], -m_ref);
-        tmax = fmaxf(tmax, t4[blk][e]);
+        t4[e] = fmaf(sc[e], kd[e], -m_ref);
+        tmax = fmaxf(tmax, t4[e]);
       }
     }
-    if (tok0 + kTile > a.n_ctx) {        // only the last tile holds tokens >= n_ctx
+    if constexpr (kPartial) {
       tmax = -INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          t4[blk][e] += (tok0 + 16 * blk + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
-          tmax = fmaxf(tmax, t4[blk][e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        t4[e] += (tok0 + 16 * own + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
+        tmax = fmaxf(tmax, t4[e]);
+      }
     }
     if (__any(tmax > 0.0f || m_run == -INFINITY)) {
       float smax = tmax + m_ref;
+      smax = fmaxf(smax, __shfl_xor(smax, 8, 64));
       smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
       smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
       const float m_new = fmaxf(m_run, smax);
@@ -265,39 +282,35 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) o[i][e] *= al[e];
       const float shift_t = m_ref - m_new;
 #pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t4[blk][e] += shift_t;
+      for (int e = 0; e < 4; ++e) t4[e] += shift_t;
     }
 
-    // ---- probabilities, folded V scale, fp16 high part (columns 0-7) or
-    // fp16 residual (columns 8-15): x - lo_mask * hi, rounded toward zero
+    // ---- probabilities and P~ = p d^V in fp16.  P~ rows 0-7 (lanes 0-7 of
+    // each row) hold the heads; rows 8-15 are zero (their lanes read the V
+    // scales from a zero block).  A row needs both blocks' tokens: its own
+    // block from itself, the other from the partner lane.
     float psum = 0.0f;
-    uint32_t pw[kBlk / 2][4];
+    float p4[4];
 #pragma unroll
-    for (int blk = 0; blk < kBlk; ++blk) {
-      const float4v vd = *(const float4v *)(sv + 16 * blk + 4 * quarter);
-      float pt[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(t4[blk][e]);
-        psum += p;
-        pt[e] = p * vd[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(pt[e], pt[e + 1]);
-        const float r0 = fmaf(-(float)h[0], lo_mask, pt[e]);
-        const float r1 = fmaf(-(float)h[1], lo_mask, pt[e + 1]);
-        pw[blk >> 1][2 * (blk & 1) + (e >> 1)] =
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-      }
+    for (int e = 0; e < 4; ++e) {
+      p4[e] = __builtin_amdgcn_exp2f(t4[e]);
+      psum += p4[e];
     }
     l_run += psum;
-    half8 pa[kBlk / 2];
+    const float4v vd0 = *(const float4v *)(sv_rd + 4 * quarter);        // block 0
+    const float4v vd1 = *(const float4v *)(sv_rd + 16 + 4 * quarter);   // block 1
+    float pt[8];
 #pragma unroll
-    for (int kk = 0; kk < kBlk / 2; ++kk)
-      pa[kk] = __builtin_bit_cast(half8, u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
+    for (int e = 0; e < 4; ++e) {
+      pt[e] = p4[e] * vd0[e];                 // lanes 0-7: own block 0
+      pt[4 + e] = row_ror8(p4[e]) * vd1[e];   // partner's block 1
+    }
+    uint32_t pw[4];   // round to nearest (v_cvt_pk_f16_f32): no truncation bias
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
+    half8 pa[kBlk / 2];
+    pa[0] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 
     // ---- O'^T += P~ V  (V read back transposed: 8 tokens x 1 byte per lane)
 #pragma unroll
@@ -318,9 +331,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   Raw r;
   fetch(r, t_begin);
-  for (int t = t_begin; t < t_end; ++t) process(r, t);
+  const int t_full = min(t_end, a.n_ctx / kTile);   // tiles below t_full are full
+  int t = t_begin;
+  for (; t < t_full; ++t) process(r, t, std::false_type{});
+  for (; t < t_end; ++t) process(r, t, std::true_type{});
 
   // ---------------- partial state of this split
+  l_run += __shfl_xor(l_run, 8, 64);
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 #pragma unroll
