@@ -182,6 +182,38 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
                                    int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
                                    void *out, tbq4_dtype out_dtype, void *hip_stream);
 
+/* Device-side lengths (ragged batches) and graph-stable decode.
+ *
+ * Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+ * section "2. Mniej przechwyceń grafu CUDA": padding the KV length to a
+ * coarse minimum cuts how often the decode graph must be re-captured as the
+ * context grows.  These two calls go further: the launch shapes depend only
+ * on (batch, heads, max_ctx, n_splits), and every per-step value -- where
+ * each sequence appends, how many slots each sequence attends -- is read
+ * from device memory, so one captured HIP graph of "append, then attend"
+ * replays unchanged while the lengths advance on the device.
+ *
+ * tbq4_quantize_append_at: as tbq4_quantize_append, but sequence b writes
+ *   slots [positions[b], positions[b] + n_new).  positions: device int32
+ *   [batch], read when the kernel runs.  Slots outside [0, capacity) are
+ *   skipped (the positions cannot be checked on the host); n_new must not
+ *   exceed capacity (TBQ4_ERR_CAPACITY).
+ * tbq4_attn_decode_varlen: as tbq4_attn_decode, but sequence b attends slots
+ *   [0, ctx_lens[b]).  ctx_lens: device int32 [batch], each clamped to
+ *   [0, max_ctx]; 1 <= max_ctx <= capacity (TBQ4_ERR_CAPACITY otherwise).
+ *   n_splits = 0 and the workspace size follow max_ctx
+ *   (tbq4_decode_workspace_bytes with n_ctx = max_ctx).  Each sequence's
+ *   slots are spread evenly over the n_splits splits at its own length.  A
+ *   sequence of length 0 gets a zero output. */
+tbq4_status tbq4_quantize_append_at(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                                    tbq4_dtype src_dtype, const int32_t *positions, int32_t n_new,
+                                    void *hip_stream);
+tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                    int32_t n_q_heads, const int32_t *ctx_lens, int32_t max_ctx,
+                                    float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                    int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream);
+
 /* Prefill-chunk attention: n_q new queries per sequence; query i sits at
  * absolute position n_past + i and attends slots [0, n_past + i] (causal
  * inside the chunk, full over the cached prefix).  Slots [n_past, n_past +

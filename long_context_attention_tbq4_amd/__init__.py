@@ -21,7 +21,7 @@ from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS
 
 __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
-    "attn_decode_partial", "attn_decode_merge",
+    "attn_decode_partial", "attn_decode_merge", "quantize_append_at", "attn_decode_varlen",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
     "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
 ]
@@ -100,6 +100,53 @@ def quantize_append(cache, k_new, v_new, pos):
     _check(_lib.lib().tbq4_quantize_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new),
                                            _dtype(k_new), pos, n_new, _stream(cache.device)),
            "tbq4_quantize_append")
+
+
+def quantize_append_at(cache, k_new, v_new, positions):
+    """As quantize_append, but sequence b writes slots [positions[b],
+    positions[b] + n_new); positions is a device int32 tensor [batch], read
+    when the kernel runs (graph-capturable).  Slots outside the capacity are
+    skipped."""
+    _require(k_new, "k_new")
+    _require(v_new, "v_new", k_new.shape)
+    _require(positions, "positions", (cache.batch,))
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    B, n_new, H, D = k_new.shape
+    if (B, H, D) != (cache.batch, cache.n_kv_heads, HEAD_DIM):
+        raise ValueError("k_new shape does not match the cache")
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_quantize_append_at(ctypes.byref(d), _ptr(k_new), _ptr(v_new),
+                                              _dtype(k_new), _ptr(positions), n_new,
+                                              _stream(cache.device)),
+           "tbq4_quantize_append_at")
+
+
+def attn_decode_varlen(cache, q, ctx_lens, max_ctx, softmax_scale, n_splits=0, out=None,
+                       out_dtype=torch.float16, workspace=None):
+    """Decode attention where sequence b attends slots [0, ctx_lens[b]);
+    ctx_lens is a device int32 tensor [batch] (clamped to [0, max_ctx]) read
+    when the kernel runs, so a captured graph stays valid as it changes."""
+    _require(q, "q")
+    B, Hq, D = q.shape
+    _require(ctx_lens, "ctx_lens", (cache.batch,))
+    if ctx_lens.dtype != torch.int32:
+        raise TypeError("ctx_lens must be int32")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, Hq, D))
+    need = decode_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, max_ctx, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_attn_decode_varlen(
+        ctypes.byref(d), _ptr(q), _dtype(q), Hq, _ptr(ctx_lens), max_ctx, float(softmax_scale),
+        _ptr(out), _dtype(out), n_splits, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device)),
+        "tbq4_attn_decode_varlen")
+    return out
 
 
 def quantize_blocks(x, sign_seed=0, out=None):

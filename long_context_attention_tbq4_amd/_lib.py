@@ -21,7 +21,7 @@ EXPORTS = (
     "tbq4_cache_bytes", "tbq4_decode_auto_splits", "tbq4_decode_workspace_bytes",
     "tbq4_sign_vector", "tbq4_quantize_append", "tbq4_quantize_blocks", "tbq4_attn_decode",
     "tbq4_attn_decode_partial", "tbq4_attn_decode_partial_timed", "tbq4_attn_decode_merge",
-    "tbq4_attn_prefill_chunk",
+    "tbq4_attn_prefill_chunk", "tbq4_quantize_append_at", "tbq4_attn_decode_varlen",
     "tbq4_status_str", "tbq4_version",
 )
 
@@ -75,6 +75,10 @@ def lib():
     L.tbq4_attn_decode_partial_timed.restype = i32
     L.tbq4_attn_decode_merge.argtypes = [vp, sz, i32, i32, i32, u64, vp, i32, vp]
     L.tbq4_attn_decode_merge.restype = i32
+    L.tbq4_quantize_append_at.argtypes = [pc, vp, vp, i32, vp, i32, vp]
+    L.tbq4_quantize_append_at.restype = i32
+    L.tbq4_attn_decode_varlen.argtypes = [pc, vp, i32, i32, vp, i32, f32, vp, i32, i32, vp, sz, vp]
+    L.tbq4_attn_decode_varlen.restype = i32
     L.tbq4_attn_prefill_chunk.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, vp]
     L.tbq4_attn_prefill_chunk.restype = i32
     L.tbq4_status_str.argtypes = [i32]

@@ -181,8 +181,6 @@ static tbq4_status prepare_decode(const tbq4_cache *cache, const void *q, tbq4_d
   a.capacity = cache->capacity;
   a.n_ctx = n_ctx;
   a.n_splits = P;
-  const int32_t n_tiles = (n_ctx + tbq4::kDecodeTile - 1) / tbq4::kDecodeTile;
-  a.tiles_per_split = (n_tiles + P - 1) / P;
   a.qscale = softmax_scale * 1.4426950408889634f;
   sign_words(cache->sign_seed, a.sign);
   return TBQ4_OK;
@@ -254,6 +252,53 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
   a.n_splits = n_splits;
   sign_words(sign_seed, a.sign);
   return from_hip(tbq4::launch_decode_merge(a, batch, (int)out_dtype, (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_quantize_append_at(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                                    tbq4_dtype src_dtype, const int32_t *positions, int32_t n_new,
+                                    void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  if (!valid_dtype(src_dtype)) return TBQ4_ERR_INVALID_ARG;
+  if (n_new < 0 || n_new > cache->capacity) return TBQ4_ERR_CAPACITY;
+  if (n_new == 0) return TBQ4_OK;
+  if (!k_new || !v_new || !positions) return TBQ4_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TBQ4_ERR_ALIGNMENT;
+  tbq4::QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.dst[0] = cache->k;
+  a.dst[1] = cache->v;
+  a.blocks_per_tensor = (int64_t)cache->batch * n_new * cache->n_kv_heads;
+  a.n_new = n_new;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.capacity = cache->capacity;
+  a.pos_dev = positions;
+  uint32_t w[4];
+  sign_words(cache->sign_seed, w);
+  a.sign_lo = w[0]; a.sign_hi = w[1]; a.sign_lo2 = w[2]; a.sign_hi2 = w[3];
+  return from_hip(tbq4::launch_quantize(a, (int)src_dtype, 2, (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                    int32_t n_q_heads, const int32_t *ctx_lens, int32_t max_ctx,
+                                    float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                    int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream) {
+  if (!out || !ctx_lens) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  tbq4::DecodeArgs a;
+  tbq4_status s = prepare_decode(cache, q, q_dtype, n_q_heads, max_ctx, softmax_scale, n_splits,
+                                 workspace, workspace_bytes, a);
+  if (s != TBQ4_OK) return s;
+  if (!aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  a.out = out;
+  a.ctx_lens = ctx_lens;
+  hipStream_t st = (hipStream_t)hip_stream;
+  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
+  if (s != TBQ4_OK) return s;
+  return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
 }
 
 tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,

@@ -132,10 +132,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // ---------------- token range of this split
-  const int n_tiles = (a.n_ctx + kTile - 1) / kTile;
-  const int t_begin = split * a.tiles_per_split;
-  const int t_end = min(t_begin + a.tiles_per_split, n_tiles);
+  // ---------------- token range of this split: this sequence's length (from
+  // device memory when given) in 32-token tiles, spread evenly over the splits
+  int n_ctx = a.n_ctx;
+  if (a.ctx_lens) n_ctx = min(max(a.ctx_lens[b], 0), a.n_ctx);
+  const int n_tiles = (n_ctx + kTile - 1) / kTile;
+  const int tiles_per_split = (n_tiles + a.n_splits - 1) / a.n_splits;
+  const int t_begin = split * tiles_per_split;
+  const int t_end = min(t_begin + tiles_per_split, n_tiles);
 
   const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
   const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        t4[e] += (tok0 + 16 * own + 4 * quarter + e < a.n_ctx) ? 0.0f : -INFINITY;
+        t4[e] += (tok0 + 16 * own + 4 * quarter + e < n_ctx) ? 0.0f : -INFINITY;
         tmax = fmaxf(tmax, t4[e]);
       }
     }
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   Raw r;
   fetch(r, t_begin);
-  const int t_full = min(t_end, a.n_ctx / kTile);   // tiles below t_full are full
+  const int t_full = min(t_end, n_ctx / kTile);   // tiles below t_full are full
   int t = t_begin;
   for (; t < t_full; ++t) process(r, t, std::false_type{});
   for (; t < t_end; ++t) process(r, t, std::true_type{});
@@ -388,6 +392,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (lane == 0) smax[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  if (M == -INFINITY) M = 0.0f;   // every split empty (a zero-length sequence): output 0
 
   float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
   int p = wave;
@@ -424,7 +429,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   o0 = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
   o1 = red[0][64 + lane] + red[1][64 + lane] + red[2][64 + lane] + red[3][64 + lane];
   L = red[0][128] + red[1][128] + red[2][128] + red[3][128];
-  const float inv = 1.0f / L;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   o0 *= inv;
   o1 *= inv;
   // o = s * (H o') / sqrt(128)

@@ -78,8 +78,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int64_t h = i % a.n_kv_heads;
     const int64_t t = (i / a.n_kv_heads) % a.n_new;
     const int64_t b = i / ((int64_t)a.n_kv_heads * a.n_new);
+    // first slot of this sequence: a host value, or per sequence from device
+    // memory (slots outside [0, capacity) are skipped; the whole wavefront
+    // leaves together)
+    const int64_t slot = (a.pos_dev ? (int64_t)a.pos_dev[b] : (int64_t)a.pos) + t;
+    if (slot < 0 || slot >= a.capacity) return;
     src = (const T *)a.src[tensor] + i * kHeadDim;
-    dst = a.dst[tensor] + ((b * a.n_kv_heads + h) * a.capacity + a.pos + t) * kBlockBytes;
+    dst = a.dst[tensor] + ((b * a.n_kv_heads + h) * a.capacity + slot) * kBlockBytes;
   }
 
   // signs of elements lane and lane+64

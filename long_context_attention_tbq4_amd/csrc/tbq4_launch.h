@@ -11,6 +11,7 @@ struct QuantArgs {
   int64_t blocks_per_tensor;   // blocks per source tensor
   int32_t n_new, n_kv_heads, capacity, pos;
   int32_t flat;                // 1: block i -> src + 128 i, dst + 66 i
+  const int32_t *pos_dev;      // device [batch] first slot per sequence, or null (use pos)
   uint32_t sign_lo, sign_hi;   // sign bits 0..31, 32..63
   uint32_t sign_lo2, sign_hi2; // sign bits 64..95, 96..127
 };
@@ -21,7 +22,10 @@ struct DecodeArgs {
   const void *q;         // [B][Hq][128]
   float *ws;             // [B][Hq][P][130]
   void *out;             // [B][Hq][128]
-  int32_t n_kv_heads, n_q_heads, group, capacity, n_ctx, n_splits, tiles_per_split;
+  const int32_t *ctx_lens;  // device [B] per-sequence lengths (clamped to [0, n_ctx]), or null
+  int32_t n_kv_heads, n_q_heads, group, capacity;
+  int32_t n_ctx;         // context length, or the upper bound of ctx_lens
+  int32_t n_splits;
   float qscale;          // softmax_scale * log2(e)
   uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
 };

@@ -115,6 +115,37 @@ def test_decode_argument_errors(L):
     assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
 
 
+def test_append_at_argument_errors(L):
+    """Device positions cannot be checked on the host; everything else is."""
+    c = _cache(heads=2, cap=64)
+    app = L.tbq4_quantize_append_at
+    assert app(None, FAKE, FAKE, 0, FAKE, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, None, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(c), FAKE, FAKE, 9, FAKE, 1, None) == _lib.ERR_INVALID_ARG
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, FAKE, 65, None) == _lib.ERR_CAPACITY
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, FAKE, -1, None) == _lib.ERR_CAPACITY
+    assert app(ctypes.byref(c), FAKE + 4, FAKE, 0, FAKE, 1, None) == _lib.ERR_ALIGNMENT
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, FAKE, 0, None) == _lib.OK       # nothing to do
+
+
+def test_decode_varlen_argument_errors(L):
+    c = _cache(heads=2, cap=64)
+    ws = 1 << 20
+
+    def dec(lens=FAKE, max_ctx=64, hq=8, out=FAKE, odt=1, p=0, w=FAKE, wb=ws):
+        return L.tbq4_attn_decode_varlen(ctypes.byref(c), FAKE, 0, hq, lens, max_ctx, 1.0, out,
+                                         odt, p, w, wb, None)
+    assert dec(lens=None) == _lib.ERR_INVALID_ARG
+    assert dec(max_ctx=0) == _lib.ERR_CAPACITY
+    assert dec(max_ctx=65) == _lib.ERR_CAPACITY
+    assert dec(hq=7) == _lib.ERR_UNSUPPORTED
+    assert dec(out=None) == _lib.ERR_INVALID_ARG
+    assert dec(odt=2) == _lib.ERR_INVALID_ARG
+    assert dec(p=2000) == _lib.ERR_INVALID_ARG
+    assert dec(wb=16) == _lib.ERR_WORKSPACE
+    assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
+
+
 def test_prefill_argument_errors(L):
     c = _cache(heads=2, cap=64)
 
