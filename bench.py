@@ -163,6 +163,7 @@ def bench_decode(tb, torch, args):
     wall = time.perf_counter() - t0
     kern_ms = hip.elapsed_ms()
     hip.destroy()
+    graph = bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w)
     kv_bytes = B * T * Hkv * 2 * 66
     q_bytes = B * Hq * 128 * 4
     out_bytes = B * Hq * 128 * 2
@@ -178,7 +179,43 @@ def bench_decode(tb, torch, args):
         "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
         "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
         "tokens_per_s": B * T / (ms * 1e-3),
+        "graph": graph,
     }
+
+
+def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
+    """The same step as one captured HIP graph: append at device positions,
+    then varlen decode over device lengths; replayed back to back."""
+    B, T = cache.batch, cache.capacity
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+
+    def step():
+        tb.quantize_append_at(cache, k_new, v_new, pos)
+        tb.attn_decode_varlen(cache, q, lens, T, w.softmax_scale, n_splits=P, out=out,
+                              workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out.float()).all()
+    return {"ms_per_step": ms, "replays": args.steps,
+            "note": "one captured graph per step (append_at + decode_varlen), replayed back to back"}
 
 
 def bench_prefill(tb, torch, args):
@@ -307,6 +344,12 @@ def main():
             "batch": 4, "n_ctx": 131072, "n_kv_heads": 8, "n_q_heads": 64, "n_splits": dec["P"],
             "hbm_frac_of_step": round(dec["value"] / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(dec["tokens_per_s"], 1),
+        },
+        "graph_step": {
+            "ms_per_step": round(dec["graph"]["ms_per_step"], 5),
+            "value": round(dec["step_bytes"] / (dec["graph"]["ms_per_step"] * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "note": dec["graph"]["note"],
         },
         "roofline": {
             "kernel": "decode_split_kernel",

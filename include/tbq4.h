@@ -182,6 +182,35 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
                                    int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
                                    void *out, tbq4_dtype out_dtype, void *hip_stream);
 
+/* Multi-query verify attention (the current token plus up to three drafted
+ * ones, per sequence).
+ *
+ * Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq":
+ * its production decode runs multi-token prediction (--spec-type mtp
+ * --spec-draft-n-max 3), so every step verifies 1 + up to 3 drafted tokens
+ * against the cache; section "Od czego zacząłem" gives the attention itself.
+ * Query i (0 <= i < n_q <= 4) of sequence b sits at absolute position
+ * n_past + i and attends slots [0, n_past + i]: causal among the new tokens,
+ * full over the prefix.  Slots [n_past, n_past + n_q) must already hold the
+ * new tokens' K and V (tbq4_quantize_append first), as for prefill.
+ *   q, out    device [batch][n_q][n_q_heads][128] (q fp32/fp16, out
+ *             fp32/fp16), 16-byte aligned
+ *   n_splits  split-K count in [1, 1024] or 0 for automatic; workspace of
+ *             tbq4_verify_workspace_bytes(..., n_splits) bytes, 16-byte
+ *             aligned, laid out as the decode workspace with row index
+ *             b * n_q + i in place of b
+ * Every (query, head) is computed from one pass over the cache: the K and V
+ * tiles are dequantised once for all n_q queries.  G = n_q_heads /
+ * n_kv_heads <= 8.  Two launches (split kernel, decode merge kernel).
+ * Errors: n_q outside [1, 4] or G > 8 -> TBQ4_ERR_UNSUPPORTED;
+ * n_past + n_q > capacity -> TBQ4_ERR_CAPACITY; otherwise as tbq4_attn_decode. */
+size_t tbq4_verify_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                   int32_t n_past, int32_t n_q, int32_t n_splits);
+tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                             int32_t n_q_heads, int32_t n_past, int32_t n_q, float softmax_scale,
+                             void *out, tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                             size_t workspace_bytes, void *hip_stream);
+
 /* Device-side lengths (ragged batches) and graph-stable decode.
  *
  * Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",

@@ -22,6 +22,7 @@ from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS
 __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
     "attn_decode_partial", "attn_decode_merge", "quantize_append_at", "attn_decode_varlen",
+    "attn_verify", "verify_workspace_bytes",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
     "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
 ]
@@ -146,6 +147,32 @@ def attn_decode_varlen(cache, q, ctx_lens, max_ctx, softmax_scale, n_splits=0, o
         _ptr(out), _dtype(out), n_splits, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q.device)),
         "tbq4_attn_decode_varlen")
+    return out
+
+
+def verify_workspace_bytes(batch, n_kv_heads, n_q_heads, n_past, n_q, n_splits=0):
+    return _lib.lib().tbq4_verify_workspace_bytes(batch, n_kv_heads, n_q_heads, n_past, n_q,
+                                                  n_splits)
+
+
+def attn_verify(cache, q, n_past, softmax_scale, n_splits=0, out=None, out_dtype=torch.float16,
+                workspace=None):
+    """Multi-query verify attention: q [batch][n_q][n_q_heads][128] with
+    n_q <= 4; query i attends slots [0, n_past + i].  Returns out
+    ([batch][n_q][n_q_heads][128])."""
+    _require(q, "q")
+    B, n_q, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, n_q, Hq, D))
+    need = verify_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, n_past, n_q, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_attn_verify(ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_past, n_q,
+                                       float(softmax_scale), _ptr(out), _dtype(out), n_splits,
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(q.device)), "tbq4_attn_verify")
     return out
 
 

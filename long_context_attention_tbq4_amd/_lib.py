@@ -22,6 +22,7 @@ EXPORTS = (
     "tbq4_sign_vector", "tbq4_quantize_append", "tbq4_quantize_blocks", "tbq4_attn_decode",
     "tbq4_attn_decode_partial", "tbq4_attn_decode_partial_timed", "tbq4_attn_decode_merge",
     "tbq4_attn_prefill_chunk", "tbq4_quantize_append_at", "tbq4_attn_decode_varlen",
+    "tbq4_verify_workspace_bytes", "tbq4_attn_verify",
     "tbq4_status_str", "tbq4_version",
 )
 
@@ -79,6 +80,10 @@ def lib():
     L.tbq4_quantize_append_at.restype = i32
     L.tbq4_attn_decode_varlen.argtypes = [pc, vp, i32, i32, vp, i32, f32, vp, i32, i32, vp, sz, vp]
     L.tbq4_attn_decode_varlen.restype = i32
+    L.tbq4_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.tbq4_verify_workspace_bytes.restype = sz
+    L.tbq4_attn_verify.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, i32, vp, sz, vp]
+    L.tbq4_attn_verify.restype = i32
     L.tbq4_attn_prefill_chunk.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, vp]
     L.tbq4_attn_prefill_chunk.restype = i32
     L.tbq4_status_str.argtypes = [i32]

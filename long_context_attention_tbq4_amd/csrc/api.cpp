@@ -254,6 +254,84 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
   return from_hip(tbq4::launch_decode_merge(a, batch, (int)out_dtype, (hipStream_t)hip_stream));
 }
 
+int32_t verify_auto_splits(int32_t batch, int32_t n_kv_heads, int32_t n_q, int32_t n_kv) {
+  // the four-query kernel keeps one wavefront per SIMD, the two-query one two
+  const int64_t waves = n_q > 2 ? 1024 : 2048;
+  const int64_t n_tiles = (n_kv + tbq4::kDecodeTile - 1) / tbq4::kDecodeTile;
+  const int64_t rows = (int64_t)batch * n_kv_heads;
+  int64_t p = (waves + rows - 1) / rows;
+  const int64_t max_by_len = (n_tiles + 3) / 4;
+  if (p > max_by_len) p = max_by_len;
+  if (p < 1) p = 1;
+  if (p > TBQ4_MAX_SPLITS) p = TBQ4_MAX_SPLITS;
+  return (int32_t)p;
+}
+
+size_t tbq4_verify_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                   int32_t n_past, int32_t n_q, int32_t n_splits) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q < 1 || n_q > 4 || n_past < 0)
+    return 0;
+  const int32_t p =
+      n_splits == 0 ? verify_auto_splits(batch, n_kv_heads, n_q, n_past + n_q) : n_splits;
+  if (p < 1 || p > TBQ4_MAX_SPLITS) return 0;
+  return round256((size_t)batch * n_q * n_q_heads * p * 130 * sizeof(float));
+}
+
+tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                             int32_t n_q_heads, int32_t n_past, int32_t n_q, float softmax_scale,
+                             void *out, tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                             size_t workspace_bytes, void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  if (!q || !out) return TBQ4_ERR_INVALID_ARG;
+  if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;
+  const int32_t G = n_q_heads / cache->n_kv_heads;
+  if (G > 8) return TBQ4_ERR_UNSUPPORTED;
+  if (n_q < 1 || n_q > 4) return TBQ4_ERR_UNSUPPORTED;
+  if (n_past < 0) return TBQ4_ERR_INVALID_ARG;
+  if ((int64_t)n_past + n_q > cache->capacity) return TBQ4_ERR_CAPACITY;
+  if (n_splits < 0 || n_splits > TBQ4_MAX_SPLITS) return TBQ4_ERR_INVALID_ARG;
+  if (cache->batch > 65535 || cache->n_kv_heads > 65535 || (int64_t)cache->batch * n_q > 65535)
+    return TBQ4_ERR_UNSUPPORTED;
+  const int32_t P = n_splits == 0 ? verify_auto_splits(cache->batch, cache->n_kv_heads, n_q,
+                                                       n_past + n_q)
+                                  : n_splits;
+  const size_t need = tbq4_verify_workspace_bytes(cache->batch, cache->n_kv_heads, n_q_heads,
+                                                  n_past, n_q, P);
+  if (!workspace || workspace_bytes < need) return TBQ4_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(q) || !aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  tbq4::VerifyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = cache->k;
+  a.v = cache->v;
+  a.q = q;
+  a.ws = (float *)workspace;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.group = G;
+  a.capacity = cache->capacity;
+  a.n_past = n_past;
+  a.n_q = n_q;
+  a.n_splits = P;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  sign_words(cache->sign_seed, a.sign);
+  hipStream_t st = (hipStream_t)hip_stream;
+  s = from_hip(tbq4::launch_verify_partial(a, cache->batch, (int)q_dtype, st));
+  if (s != TBQ4_OK) return s;
+  // merge: row (b, query) of the decode layout, output [B][n_q][Hq][128]
+  tbq4::DecodeArgs m;
+  memset(&m, 0, sizeof(m));
+  m.ws = (float *)workspace;
+  m.out = out;
+  m.n_q_heads = n_q_heads;
+  m.n_splits = P;
+  memcpy(m.sign, a.sign, sizeof(a.sign));
+  return from_hip(tbq4::launch_decode_merge(m, cache->batch * n_q, (int)out_dtype, st));
+}
+
 tbq4_status tbq4_quantize_append_at(const tbq4_cache *cache, const void *k_new, const void *v_new,
                                     tbq4_dtype src_dtype, const int32_t *positions, int32_t n_new,
                                     void *hip_stream) {

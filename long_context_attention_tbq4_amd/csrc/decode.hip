@@ -40,18 +40,6 @@ constexpr int kBlk = kTile / 16;    // 16-token MFMA row blocks per tile
 constexpr int kVRow = 80;           // LDS bytes per staged V row (64 + pad)
 
 
-__device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
-
-// 16-lane row rotation by 8: lane j receives lane (j + 8) mod 16 of its row.
-__device__ __forceinline__ float row_ror8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               0x128, 0xF, 0xF, true));
-}
-
-template <typename QT>
-__device__ __forceinline__ float load_q(const QT *p);
-template <> __device__ __forceinline__ float load_q<float>(const float *p) { return *p; }
-template <> __device__ __forceinline__ float load_q<_Float16>(const _Float16 *p) { return (float)*p; }
 
 template <typename QT>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
@@ -216,8 +204,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
     }
     if (lane < kTile) {
-      sk[lane] = half_bits_to_float(r.sk) * qs_inv;
-      sv[lane] = half_bits_to_float(r.sv);
+      float dk = half_bits_to_float(r.sk) * qs_inv, dv = half_bits_to_float(r.sv);
+      if constexpr (kPartial) {
+        // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
+        if (tok0 + lane >= n_ctx) dk = dv = 0.0f;
+      }
+      sk[lane] = dk;
+      sv[lane] = dv;
     }
     fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
 

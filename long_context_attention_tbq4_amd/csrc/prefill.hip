@@ -165,7 +165,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     r.v1 = buf_load_x1(rv, a0 + 16);
     r.sk = 0;
     r.sv = 0;
-    if (fq == 0) {
+    // keys at or past n_past + n_q may hold anything: their scales stay 0 so
+    // that a NaN there cannot survive the mask (p = 0)
+    if (fq == 0 && t * kKT + fkey < a.n_past + a.n_q) {
       r.sk = buf_load_u16(rk, base + (uint32_t)fkey * kBlockBytes);
       r.sv = buf_load_u16(rv, base + (uint32_t)fkey * kBlockBytes);
     }

@@ -134,4 +134,15 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
+// 16-lane row rotation by 8: lane j receives lane (j + 8) mod 16 of its row.
+__device__ __forceinline__ float row_ror8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x128, 0xF, 0xF, true));
+}
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT *p);
+template <> __device__ __forceinline__ float load_q<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_q<_Float16>(const _Float16 *p) { return (float)*p; }
+
 }  // namespace tbq4

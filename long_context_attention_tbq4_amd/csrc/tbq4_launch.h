@@ -30,6 +30,16 @@ struct DecodeArgs {
   uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
 };
 
+struct VerifyArgs {
+  const uint8_t *k;
+  const uint8_t *v;
+  const void *q;         // [B][n_q][Hq][128]
+  float *ws;             // [B * n_q][Hq][P][130] (the decode layout)
+  int32_t n_kv_heads, n_q_heads, group, capacity, n_past, n_q, n_splits;
+  float qscale;          // softmax_scale * log2(e)
+  uint32_t sign[4];
+};
+
 struct PrefillArgs {
   const uint8_t *k;
   const uint8_t *v;
@@ -47,6 +57,7 @@ hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream);
+hipError_t launch_verify_partial(const VerifyArgs &a, int batch, int q_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
                           hipStream_t stream);
 

@@ -1,0 +1,345 @@
+// TBQ4 multi-query verify attention (split-K) for gfx950.
+//
+// Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+// section "Od czego zacząłem" (flash attention straight on TBQ4 blocks,
+// dequantised in the inner loop, in the rotated domain) and the page's
+// production configuration (--spec-type mtp --spec-draft-n-max 3): every
+// decode step verifies the current token plus up to three drafted ones.
+// Query i of a sequence sits at absolute position n_past + i and attends slots
+// [0, n_past + i] -- causal among the drafted tokens, full over the prefix.
+//
+// Same streaming scheme as the decode split kernel (one wavefront per
+// (sequence, KV head, split), 32-token tiles, K straight from registers, V
+// transposed through LDS), but the K and V tiles are dequantised once for all
+// n_q queries:
+//   * the 16 MFMA columns hold (query, head) pairs -- queries 2c and 2c + 1
+//     of column group c, G <= 8 heads each -- and one or two column groups
+//     cover n_q <= 2 or n_q <= 4,
+//   * q' is carried as an fp16 high part and the fp16 residual, multiplied
+//     by the same K operand in two MFMAs that accumulate into one score,
+//   * every column is a distinct (query, head), so each lane finishes its
+//     own scores and P~ rows; P~ = p d^V is one fp16, rounded to nearest.
+// Partial states use the decode workspace layout with (sequence, query) as
+// the row index, so the decode merge kernel finishes them.
+#include "tbq4_device.h"
+#include "tbq4_launch.h"
+
+#include <type_traits>
+
+namespace tbq4 {
+
+namespace {
+constexpr int kTile = 32;
+constexpr int kBlk = kTile / 16;
+constexpr int kVRow = 80;
+}  // namespace
+
+template <typename QT, int CG>
+__global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
+  __shared__ __attribute__((aligned(16))) float sk[kTile];
+  __shared__ __attribute__((aligned(16))) float sv[kTile];
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int quarter = lane >> 4;
+  const int col = lane & 15;            // MFMA column: (query 2c + (col >> 3), head col & 7)
+  const int head = col & 7;
+  const int qsub = col >> 3;
+
+  // ---------------- q' = R q * scale * log2(e) per (query, head) column
+  float qv[CG][32];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const int qi = 2 * c + qsub;
+    const bool live = qi < a.n_q && head < G;
+    const QT *qp = (const QT *)a.q +
+                   (((size_t)b * a.n_q + (live ? qi : 0)) * a.n_q_heads + (size_t)g * G +
+                    (live ? head : 0)) * kHeadDim + quarter * 32;
+    const uint32_t sw = a.sign[quarter];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float x = live ? load_q<QT>(qp + i) : 0.0f;
+      qv[c][i] = ((sw >> i) & 1u) ? -x : x;
+    }
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if ((i & h) == 0) {
+          const float x = qv[c][i], y = qv[c][i + h];
+          qv[c][i] = x + y;
+          qv[c][i + h] = x - y;
+        }
+#pragma unroll
+    for (int h = 16; h <= 32; h <<= 1) {
+      const bool upper = (lane & h) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float o = __shfl_xor(qv[c][i], h, 64);
+        qv[c][i] = upper ? (o - qv[c][i]) : (qv[c][i] + o);
+      }
+    }
+  }
+  const float f = 0.08838834764831845f * a.qscale;
+  float mx = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      qv[c][i] *= f;
+      mx = fmaxf(mx, fabsf(qv[c][i]));
+    }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  int ex = 0;
+  if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
+  ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+  const float qs_inv = ldexpf(1.0f, -ex);
+  half8 qhi[CG][4], qlo[CG][4];
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int el = 0; el < 8; ++el) {
+        const int i = 8 * k + (el < 4 ? 2 * el : 2 * el - 7);
+        const float x = ldexpf(qv[c][i], ex);
+        const _Float16 hi = (_Float16)x;
+        qhi[c][k][el] = hi;
+        qlo[c][k][el] = (_Float16)(x - (float)hi);
+      }
+
+  // ---------------- token range: slots [0, n_past + n_q) in 32-token tiles
+  const int n_kv = a.n_past + a.n_q;
+  const int n_tiles = (n_kv + kTile - 1) / kTile;
+  const int tiles_per_split = (n_tiles + a.n_splits - 1) / a.n_splits;
+  const int t_begin = split * tiles_per_split;
+  const int t_end = min(t_begin + tiles_per_split, n_tiles);
+
+  const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
+  const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
+  const rsrc_t rk = make_rsrc(a.k + row, row_bytes);
+  const rsrc_t rv = make_rsrc(a.v + row, row_bytes);
+
+  float m_run[CG], l_run[CG];
+  float4v o[CG][8];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[c][i] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+
+  int tr_off;
+  {
+    const int e = col >> 1;
+    const int tok = 16 * (e >> 2) + 4 * quarter + (e & 3);
+    tr_off = tok * kVRow + 8 * (col & 1);
+  }
+
+  struct Raw {
+    u32x4 k4[kBlk], v4[kBlk];
+    uint32_t k1[kBlk], v1[kBlk];
+    uint16_t sk, sv;
+  };
+  const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
+  const uint32_t shift = lane_off & 3u;
+  auto fetch = [&](Raw &r, int t) {
+    const uint32_t base = t < t_end ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
+#pragma unroll
+    for (int blk = 0; blk < kBlk; ++blk) {
+      const uint32_t ad = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
+      r.k4[blk] = buf_load_x4(rk, ad);
+      r.k1[blk] = buf_load_x1(rk, ad + 16);
+      r.v4[blk] = buf_load_x4(rv, ad);
+      r.v1[blk] = buf_load_x1(rv, ad + 16);
+    }
+    const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
+    r.sk = buf_load_u16(rk, soff);
+    r.sv = buf_load_u16(rv, soff);
+  };
+
+  // kPartial: the tile holds slots a draft query must not see (or slots past
+  // the end); only the tiles at the end of the range
+  auto process = [&](Raw &r, int t, auto partial_tag) {
+    constexpr bool kPartial = decltype(partial_tag)::value;
+    const int tok0 = t * kTile;
+    uint32_t kw[kBlk][4];
+#pragma unroll
+    for (int blk = 0; blk < kBlk; ++blk) {
+      const u32x4 w = r.k4[blk];
+      kw[blk][0] = alignbyte(w[1], w[0], shift);
+      kw[blk][1] = alignbyte(w[2], w[1], shift);
+      kw[blk][2] = alignbyte(w[3], w[2], shift);
+      kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int blk = 0; blk < kBlk; ++blk) {
+      const u32x4 w = r.v4[blk];
+      const u32x4 al = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
+                        alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
+      *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = al;
+    }
+    if (lane < kTile) {
+      float dk = half_bits_to_float(r.sk) * qs_inv, dv = half_bits_to_float(r.sv);
+      if constexpr (kPartial) {
+        // slots past the drafted tokens may hold anything (NaN survives p = 0)
+        if (tok0 + lane >= n_kv) dk = dv = 0.0f;
+      }
+      sk[lane] = dk;
+      sv[lane] = dv;
+    }
+    fetch(r, t + 1);
+
+    // ---- scores: S^T[token][(query, head)] = K . (q'_hi + q'_lo)
+    float4v acc[CG][kBlk];
+#pragma unroll
+    for (int blk = 0; blk < kBlk; ++blk) {
+      half8 kh[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kh[k] = word_to_half8(kw[blk][k]);
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        float4v s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[k], qhi[c][k], s4, 0, 0, 0);
+          s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[k], qlo[c][k], s4, 0, 0, 0);
+        }
+        acc[c][blk] = s4;
+      }
+    }
+    __syncthreads();
+
+    half8 pa[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int qi = 2 * c + qsub;
+      const float m_ref = m_run[c] == -INFINITY ? 0.0f : m_run[c];
+      float t4[kBlk][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < kBlk; ++blk) {
+        const float4v kd = *(const float4v *)(sk + 16 * blk + 4 * quarter);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          t4[blk][e] = fmaf(acc[c][blk][e], kd[e], -m_ref);
+          if constexpr (kPartial)
+            t4[blk][e] += (tok0 + 16 * blk + 4 * quarter + e <= a.n_past + qi) ? 0.0f : -INFINITY;
+          tmax = fmaxf(tmax, t4[blk][e]);
+        }
+      }
+      if (__any(tmax > 0.0f || m_run[c] == -INFINITY)) {
+        float smax = tmax + m_ref;
+        smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+        const float m_new = fmaxf(m_run[c], smax);
+        // a column that has seen no live slot yet keeps m = -inf: alpha 1
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
+        m_run[c] = m_new;
+        l_run[c] *= alpha;
+        float al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * quarter + e, 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[c][i][e] *= al[e];
+        const float shift_t = m_new == -INFINITY ? 0.0f : m_ref - m_new;
+#pragma unroll
+        for (int blk = 0; blk < kBlk; ++blk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t4[blk][e] += shift_t;
+      }
+      float psum = 0.0f;
+      float pt[8];
+#pragma unroll
+      for (int blk = 0; blk < kBlk; ++blk) {
+        const float4v vd = *(const float4v *)(sv + 16 * blk + 4 * quarter);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(t4[blk][e]);
+          psum += p;
+          pt[4 * blk + e] = p * vd[e];
+        }
+      }
+      l_run[c] += psum;
+      uint32_t pw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
+      pa[c] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    }
+
+    // ---- O'^T += P~ V for every column group (V dequantised once)
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      typedef __attribute__((address_space(3))) int2v lds_i2;
+      const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr_off + 16 * cg));
+      const uint32_t w0 = (uint32_t)rr[0], w1 = (uint32_t)rr[1];
+      const half8 ve = lo_nibbles_to_half8(w0, w1);
+      const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], ve, o[c][2 * cg], 0, 0, 0);
+        o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vo, o[c][2 * cg + 1], 0, 0, 0);
+      }
+    }
+  };
+
+  Raw r;
+  fetch(r, t_begin);
+  // tiles entirely at or below slot n_past are visible to every query
+  const int t_full = min(t_end, (a.n_past + 1) / kTile);
+  int t = t_begin;
+  for (; t < t_full; ++t) process(r, t, std::false_type{});
+  for (; t < t_end; ++t) process(r, t, std::true_type{});
+
+  // ---------------- partial states: row (b * n_q + query) of the decode layout
+  const int P = a.n_splits;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    l_run[c] += __shfl_xor(l_run[c], 16, 64);
+    l_run[c] += __shfl_xor(l_run[c], 32, 64);
+    const int qi = 2 * c + qsub;
+    if (lane < 16 && qi < a.n_q && head < G) {
+      float *w = a.ws + (((size_t)b * a.n_q + qi) * a.n_q_heads + (size_t)g * G + head) * P * 130 +
+                 (size_t)split * 130;
+      w[0] = m_run[c];
+      w[1] = l_run[c];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rc = 4 * quarter + e;          // P~ row = column (query, head)
+      const int rq = 2 * c + (rc >> 3), rh = rc & 7;
+      if (rq < a.n_q && rh < G) {
+        float *dst = a.ws + (((size_t)b * a.n_q + rq) * a.n_q_heads + (size_t)g * G + rh) * P * 130 +
+                     (size_t)split * 130 + 2;
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) {
+          dst[32 * cg + 2 * col] = o[c][2 * cg][e];
+          dst[32 * cg + 2 * col + 1] = o[c][2 * cg + 1][e];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_verify_partial(const VerifyArgs &a, int batch, int q_dtype, hipStream_t stream) {
+  dim3 grid(a.n_splits, a.n_kv_heads, batch);
+  const bool two = a.n_q > 2;
+  if (q_dtype == 0) {
+    if (two) hipLaunchKernelGGL((verify_split_kernel<float, 2>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((verify_split_kernel<float, 1>), grid, dim3(64), 0, stream, a);
+  } else {
+    if (two) hipLaunchKernelGGL((verify_split_kernel<_Float16, 2>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((verify_split_kernel<_Float16, 1>), grid, dim3(64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tbq4

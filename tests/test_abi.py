@@ -146,6 +146,28 @@ def test_decode_varlen_argument_errors(L):
     assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
 
 
+def test_verify_argument_errors(L):
+    c = _cache(heads=2, cap=64)
+    ws = 1 << 20
+
+    def ver(n_past=10, n_q=4, hq=16, qdt=0, odt=1, p=0, out=FAKE, wb=ws):
+        return L.tbq4_attn_verify(ctypes.byref(c), FAKE, qdt, hq, n_past, n_q, 1.0, out, odt, p,
+                                  FAKE, wb, None)
+    assert ver(n_q=0) == _lib.ERR_UNSUPPORTED
+    assert ver(n_q=5) == _lib.ERR_UNSUPPORTED
+    assert ver(hq=18) == _lib.ERR_UNSUPPORTED          # group of 9
+    assert ver(n_past=-1) == _lib.ERR_INVALID_ARG
+    assert ver(n_past=61, n_q=4) == _lib.ERR_CAPACITY  # 65 > 64
+    assert ver(qdt=2) == _lib.ERR_INVALID_ARG
+    assert ver(out=None) == _lib.ERR_INVALID_ARG
+    assert ver(p=1025) == _lib.ERR_INVALID_ARG
+    assert ver(wb=16) == _lib.ERR_WORKSPACE
+    assert ver(out=FAKE + 4) == _lib.ERR_ALIGNMENT
+    # workspace size: batch * n_q * n_q_heads * P * 130 * 4, rounded to 256
+    assert L.tbq4_verify_workspace_bytes(1, 2, 16, 10, 4, 3) == ((1 * 4 * 16 * 3 * 520 + 255) // 256) * 256
+    assert L.tbq4_verify_workspace_bytes(1, 2, 16, 10, 5, 3) == 0
+
+
 def test_prefill_argument_errors(L):
     c = _cache(heads=2, cap=64)
 

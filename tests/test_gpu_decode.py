@@ -221,3 +221,23 @@ def test_timed_partial_matches_and_records_events():
     assert 0.0 < ms.value < 1000.0
     for e in ev:
         rt.hipEventDestroy(e)
+
+
+@pytest.mark.parametrize("n_ctx", [33, 1000, 1023])
+def test_unused_slots_with_nan_scales_do_not_leak(n_ctx):
+    """Slots >= n_ctx of the last tile may hold anything; 0xFF bytes are NaN
+    fp16 scales, which must not reach the output through p = 0."""
+    rng = np.random.default_rng(40 + n_ctx)
+    k = rng.standard_normal((1, n_ctx, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((1, n_ctx, 2, 128)).astype(np.float32)
+    cache = tb.KVCache(1, 2, 1056)
+    cache.k.fill_(0xFF)
+    cache.v.fill_(0xFF)
+    _fill(cache, k, v)
+    kc, vc = _oracle_cache(k, v)
+    q = rng.standard_normal((1, 16, 128)).astype(np.float32)
+    ref = o.attn_decode_ref(q, kc, vc, n_ctx, 0.1)
+    for P in (1, 3):
+        out = tb.attn_decode(cache, torch.from_numpy(q).cuda(), n_ctx, 0.1, n_splits=P,
+                             out_dtype=torch.float32)
+        check_attn(out.cpu().numpy(), ref, False, f"nan tail n_ctx={n_ctx} P={P}")

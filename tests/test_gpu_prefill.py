@@ -126,3 +126,23 @@ def test_prefill_workload_sampled():
             nk = n_past + i + 1
             ref = o.attn_decode_rows_ref(q[0, i, g * G:(g + 1) * G], Kd[:nk], Vd[:nk], w.softmax_scale)
             check_attn(out[0, i, g * G:(g + 1) * G], ref, True, f"prefill g={g} row={i}")
+
+
+def test_unused_slots_with_nan_scales_do_not_leak():
+    """Keys at or past n_past + n_q may hold anything (0xFF = NaN scales)."""
+    rng = np.random.default_rng(41)
+    n_past, n_q = 100, 37
+    T = n_past + n_q
+    k = rng.standard_normal((1, T, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((1, T, 2, 128)).astype(np.float32)
+    q = rng.standard_normal((1, n_q, 16, 128)).astype(np.float32)
+    cache = tb.KVCache(1, 2, 256)
+    cache.k.fill_(0xFF)
+    cache.v.fill_(0xFF)
+    tb.quantize_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    kc = o.quantize_blocks(k.transpose(0, 2, 1, 3))[0]
+    vc = o.quantize_blocks(v.transpose(0, 2, 1, 3))[0]
+    out = tb.attn_prefill_chunk(cache, torch.from_numpy(q).cuda(), n_past, 0.1,
+                                out_dtype=torch.float32)
+    ref = o.attn_prefill_ref(q, kc, vc, n_past, 0.1, 0)
+    check_attn(out.cpu().numpy(), ref, False, "nan tail prefill")
