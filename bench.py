@@ -41,8 +41,8 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "0a83bf0e2e61626cac8607faa4d79482a25b086b97c4d88084ed1bb443631222",
-           "n_splits": 64, "fetch_kib": 271359.6, "fetch_factor": 2.0,
+TRAFFIC = {"sources_sha256": "fb8496f036c69637ce91c18a4d214831f79089d85206ef3e028fe6401a8299f7",
+           "n_splits": 64, "fetch_kib": 271205.1, "fetch_factor": 2.0,
            "write_kib": 8704.0, "write_factor": 1.0}
 
 
@@ -164,6 +164,7 @@ def bench_decode(tb, torch, args):
     kern_ms = hip.elapsed_ms()
     hip.destroy()
     graph = bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w)
+    verify = bench_verify(tb, torch, args, cache, w)
     kv_bytes = B * T * Hkv * 2 * 66
     q_bytes = B * Hq * 128 * 4
     out_bytes = B * Hq * 128 * 2
@@ -180,6 +181,7 @@ def bench_decode(tb, torch, args):
         "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
         "tokens_per_s": B * T / (ms * 1e-3),
         "graph": graph,
+        "verify": verify,
     }
 
 
@@ -216,6 +218,33 @@ def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
     assert torch.isfinite(out.float()).all()
     return {"ms_per_step": ms, "replays": args.steps,
             "note": "one captured graph per step (append_at + decode_varlen), replayed back to back"}
+
+
+def bench_verify(tb, torch, args, cache, w, n_q=4):
+    """Multi-query verify (the current token + 3 drafted) on the same cache:
+    query i attends slots [0, T - n_q + i]; one pass over the cache serves all
+    n_q queries.  Reported beside n_q single-query decodes of the same bytes."""
+    B, T, Hq = cache.batch, cache.capacity, w.n_q_heads
+    rng = np.random.default_rng([0, 98])
+    q = torch.from_numpy(rng.standard_normal((B, n_q, Hq, 128)).astype(np.float32)).cuda()
+    out = torch.empty((B, n_q, Hq, 128), dtype=torch.float16, device="cuda")
+    n_past = T - n_q
+    ws = torch.empty(tb.verify_workspace_bytes(B, cache.n_kv_heads, Hq, n_past, n_q),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        tb.attn_verify(cache, q, n_past, w.softmax_scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        tb.attn_verify(cache, q, n_past, w.softmax_scale, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out.float()).all()
+    kv = B * T * cache.n_kv_heads * 2 * 66
+    return {"n_q": n_q, "ms_per_call": ms, "kv_gbs": kv / (ms * 1e-3) / 1e9,
+            "query_tokens_per_s": B * n_q / (ms * 1e-3)}
 
 
 def bench_prefill(tb, torch, args):
@@ -344,6 +373,14 @@ def main():
             "batch": 4, "n_ctx": 131072, "n_kv_heads": 8, "n_q_heads": 64, "n_splits": dec["P"],
             "hbm_frac_of_step": round(dec["value"] / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(dec["tokens_per_s"], 1),
+        },
+        "verify": {
+            "workload": "decode128k cache, 4 queries per sequence (1 + 3 drafted), query i "
+                        "attends slots [0, 131068 + i]; calls back to back (launch + merge)",
+            "ms_per_call": round(dec["verify"]["ms_per_call"], 5),
+            "kv_gbs": round(dec["verify"]["kv_gbs"], 1),
+            "query_tokens_per_s": round(dec["verify"]["query_tokens_per_s"], 1),
+            "vs_4_decodes": round(4 * dec["ms"] / dec["verify"]["ms_per_call"], 3),
         },
         "graph_step": {
             "ms_per_step": round(dec["graph"]["ms_per_step"], 5),
