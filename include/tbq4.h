@@ -182,6 +182,48 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
                                    int32_t n_q_heads, int32_t n_splits, uint64_t sign_seed,
                                    void *out, tbq4_dtype out_dtype, void *hip_stream);
 
+/* Mixed K/V cache formats.
+ *
+ * Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+ * section "Konfiguracja": the K and the V cache types are chosen separately
+ * (-ctk, -ctv).  The DFlash speed-test page (gptunnel blog), section "Қосымша
+ * олжа: кванттталған KV-кэш жылдамдықтың 39%-ын жейді", measures what a
+ * quantised cache costs against an fp16 one.  These calls let each tensor be
+ * TBQ4 blocks or plain fp16 rows, so the dequantisation cost can be weighed
+ * against the bytes saved per tensor.
+ *
+ *   TBQ4_FMT_TBQ4  66-byte blocks as above, rotated by the cache's signs
+ *   TBQ4_FMT_F16   head vectors stored as 128 binary16 values (round to
+ *                  nearest even from the input, overflow to infinity), not
+ *                  rotated: 256 bytes per head vector
+ * tbq4_mixed_cache: k, v point at [batch][n_kv_heads][capacity][row bytes of
+ * their format] (tbq4_format_row_bytes), 16-byte aligned; the rest as in
+ * the TBQ4-only descriptor, capacity a multiple of 8.
+ * tbq4_mixed_append: as tbq4_quantize_append, each tensor in its format.
+ * tbq4_mixed_attn_decode: as tbq4_attn_decode (same workspace size, G <= 8):
+ *   q is rotated only when K is TBQ4, and the output is rotated back only
+ *   when V is TBQ4.  Any combination of the two formats is accepted. */
+typedef enum { TBQ4_FMT_TBQ4 = 0, TBQ4_FMT_F16 = 1 } tbq4_format;
+typedef struct {
+  uint8_t *k;
+  uint8_t *v;
+  int32_t k_format;
+  int32_t v_format;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  uint64_t sign_seed;
+} tbq4_mixed_cache;
+size_t tbq4_format_row_bytes(int32_t format);
+tbq4_status tbq4_mixed_append(const tbq4_mixed_cache *cache, const void *k_new, const void *v_new,
+                              tbq4_dtype src_dtype, int32_t pos, int32_t n_new, void *hip_stream);
+tbq4_status tbq4_mixed_attn_decode(const tbq4_mixed_cache *cache, const void *q,
+                                   tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_ctx,
+                                   float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                   int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream);
+
 /* Multi-query verify attention (the current token plus up to three drafted
  * ones, per sequence).
  *

@@ -22,7 +22,8 @@ from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS
 __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
     "attn_decode_partial", "attn_decode_merge", "quantize_append_at", "attn_decode_varlen",
-    "attn_verify", "verify_workspace_bytes",
+    "attn_verify", "verify_workspace_bytes", "MixedKVCache", "mixed_append",
+    "mixed_attn_decode", "FMT_TBQ4", "FMT_F16",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
     "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
 ]
@@ -85,6 +86,72 @@ class KVCache:
     def descriptor(self):
         return _lib.Cache(self.k.data_ptr(), self.v.data_ptr(), self.batch, self.n_kv_heads,
                           HEAD_DIM, self.capacity, self.sign_seed)
+
+
+FMT_TBQ4, FMT_F16 = 0, 1
+_ROW_BYTES = {FMT_TBQ4: BLOCK_BYTES, FMT_F16: 2 * HEAD_DIM}
+
+
+class MixedKVCache:
+    """One layer's K and V caches, each in its own format: FMT_TBQ4 (uint8
+    [batch][n_kv_heads][capacity][66]) or FMT_F16 (uint8 view of fp16
+    [batch][n_kv_heads][capacity][128], not rotated)."""
+
+    def __init__(self, batch, n_kv_heads, capacity, k_format, v_format, sign_seed=0,
+                 device="cuda"):
+        if capacity % 8:
+            raise ValueError("capacity must be a multiple of 8")
+        if k_format not in _ROW_BYTES or v_format not in _ROW_BYTES:
+            raise ValueError("unknown cache format")
+        self.k = torch.zeros((batch, n_kv_heads, capacity, _ROW_BYTES[k_format]), dtype=torch.uint8,
+                             device=device)
+        self.v = torch.zeros((batch, n_kv_heads, capacity, _ROW_BYTES[v_format]), dtype=torch.uint8,
+                             device=device)
+        self.k_format, self.v_format = k_format, v_format
+        self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
+        self.sign_seed = sign_seed
+
+    @property
+    def device(self):
+        return self.k.device
+
+    def descriptor(self):
+        return _lib.MixedCache(self.k.data_ptr(), self.v.data_ptr(), self.k_format, self.v_format,
+                               self.batch, self.n_kv_heads, HEAD_DIM, self.capacity, self.sign_seed)
+
+
+def mixed_append(cache, k_new, v_new, pos):
+    """Append k_new, v_new ([batch][n_new][n_kv_heads][128]) into slots
+    [pos, pos + n_new), each tensor in its cache's format."""
+    _require(k_new, "k_new")
+    _require(v_new, "v_new", k_new.shape)
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    B, n_new, H, D = k_new.shape
+    if (B, H, D) != (cache.batch, cache.n_kv_heads, HEAD_DIM):
+        raise ValueError("k_new shape does not match the cache")
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_mixed_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _dtype(k_new),
+                                        pos, n_new, _stream(cache.device)), "tbq4_mixed_append")
+
+
+def mixed_attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None,
+                      out_dtype=torch.float16, workspace=None):
+    """Decode attention over a MixedKVCache; same shapes as attn_decode."""
+    _require(q, "q")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, Hq, D))
+    need = decode_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, n_ctx, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_mixed_attn_decode(
+        ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx, float(softmax_scale), _ptr(out),
+        _dtype(out), n_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device)), "tbq4_mixed_attn_decode")
+    return out
 
 
 def quantize_append(cache, k_new, v_new, pos):

@@ -22,7 +22,8 @@ EXPORTS = (
     "tbq4_sign_vector", "tbq4_quantize_append", "tbq4_quantize_blocks", "tbq4_attn_decode",
     "tbq4_attn_decode_partial", "tbq4_attn_decode_partial_timed", "tbq4_attn_decode_merge",
     "tbq4_attn_prefill_chunk", "tbq4_quantize_append_at", "tbq4_attn_decode_varlen",
-    "tbq4_verify_workspace_bytes", "tbq4_attn_verify",
+    "tbq4_verify_workspace_bytes", "tbq4_attn_verify", "tbq4_format_row_bytes",
+    "tbq4_mixed_append", "tbq4_mixed_attn_decode",
     "tbq4_status_str", "tbq4_version",
 )
 
@@ -32,6 +33,21 @@ class Cache(ctypes.Structure):
     _fields_ = [
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("sign_seed", ctypes.c_uint64),
+    ]
+
+
+class MixedCache(ctypes.Structure):
+    """Mirror of ``tbq4_mixed_cache``."""
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_format", ctypes.c_int32),
+        ("v_format", ctypes.c_int32),
         ("batch", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
@@ -84,6 +100,13 @@ def lib():
     L.tbq4_verify_workspace_bytes.restype = sz
     L.tbq4_attn_verify.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, i32, vp, sz, vp]
     L.tbq4_attn_verify.restype = i32
+    pm = ctypes.POINTER(MixedCache)
+    L.tbq4_format_row_bytes.argtypes = [i32]
+    L.tbq4_format_row_bytes.restype = sz
+    L.tbq4_mixed_append.argtypes = [pm, vp, vp, i32, i32, i32, vp]
+    L.tbq4_mixed_append.restype = i32
+    L.tbq4_mixed_attn_decode.argtypes = [pm, vp, i32, i32, i32, f32, vp, i32, i32, vp, sz, vp]
+    L.tbq4_mixed_attn_decode.restype = i32
     L.tbq4_attn_prefill_chunk.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, vp]
     L.tbq4_attn_prefill_chunk.restype = i32
     L.tbq4_status_str.argtypes = [i32]

@@ -181,6 +181,7 @@ static tbq4_status prepare_decode(const tbq4_cache *cache, const void *q, tbq4_d
   a.capacity = cache->capacity;
   a.n_ctx = n_ctx;
   a.n_splits = P;
+  a.rotate_out = 1;
   a.qscale = softmax_scale * 1.4426950408889634f;
   sign_words(cache->sign_seed, a.sign);
   return TBQ4_OK;
@@ -250,8 +251,104 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
   a.out = out;
   a.n_q_heads = n_q_heads;
   a.n_splits = n_splits;
+  a.rotate_out = 1;
   sign_words(sign_seed, a.sign);
   return from_hip(tbq4::launch_decode_merge(a, batch, (int)out_dtype, (hipStream_t)hip_stream));
+}
+
+size_t tbq4_format_row_bytes(int32_t format) {
+  return format == TBQ4_FMT_TBQ4 ? TBQ4_BLOCK_BYTES : format == TBQ4_FMT_F16 ? 2 * TBQ4_HEAD_DIM : 0;
+}
+
+// The TBQ4 view of a mixed cache (pointers and shape) for the shared checks,
+// plus the checks that depend on the formats.
+static tbq4_status mixed_view(const tbq4_mixed_cache *c, tbq4_cache &v) {
+  if (!c) return TBQ4_ERR_INVALID_ARG;
+  if (tbq4_format_row_bytes(c->k_format) == 0 || tbq4_format_row_bytes(c->v_format) == 0)
+    return TBQ4_ERR_UNSUPPORTED;
+  v.k = c->k;
+  v.v = c->v;
+  v.batch = c->batch;
+  v.n_kv_heads = c->n_kv_heads;
+  v.head_dim = c->head_dim;
+  v.capacity = c->capacity;
+  v.sign_seed = c->sign_seed;
+  tbq4_status s = check_cache(&v);
+  if (s != TBQ4_OK) return s;
+  if ((int64_t)c->capacity * 2 * TBQ4_HEAD_DIM > 0x7FFFFFF0ll) return TBQ4_ERR_UNSUPPORTED;
+  return TBQ4_OK;
+}
+
+tbq4_status tbq4_mixed_append(const tbq4_mixed_cache *cache, const void *k_new, const void *v_new,
+                              tbq4_dtype src_dtype, int32_t pos, int32_t n_new, void *hip_stream) {
+  tbq4_cache view;
+  tbq4_status s = mixed_view(cache, view);
+  if (s != TBQ4_OK) return s;
+  if (!valid_dtype(src_dtype)) return TBQ4_ERR_INVALID_ARG;
+  if (n_new < 0 || pos < 0) return TBQ4_ERR_INVALID_ARG;
+  if ((int64_t)pos + n_new > cache->capacity) return TBQ4_ERR_CAPACITY;
+  if (n_new == 0) return TBQ4_OK;
+  if (!k_new || !v_new) return TBQ4_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TBQ4_ERR_ALIGNMENT;
+  const void *src[2] = {k_new, v_new};
+  uint8_t *dst[2] = {cache->k, cache->v};
+  const int32_t fmt[2] = {cache->k_format, cache->v_format};
+  uint32_t w[4];
+  sign_words(cache->sign_seed, w);
+  for (int t = 0; t < 2; ++t) {
+    hipError_t e;
+    if (fmt[t] == TBQ4_FMT_TBQ4) {
+      tbq4::QuantArgs a;
+      memset(&a, 0, sizeof(a));
+      a.src[0] = src[t];
+      a.dst[0] = dst[t];
+      a.blocks_per_tensor = (int64_t)cache->batch * n_new * cache->n_kv_heads;
+      a.n_new = n_new;
+      a.n_kv_heads = cache->n_kv_heads;
+      a.capacity = cache->capacity;
+      a.pos = pos;
+      a.sign_lo = w[0]; a.sign_hi = w[1]; a.sign_lo2 = w[2]; a.sign_hi2 = w[3];
+      e = tbq4::launch_quantize(a, (int)src_dtype, 1, (hipStream_t)hip_stream);
+    } else {
+      tbq4::StoreF16Args a;
+      a.src = src[t];
+      a.dst = (_Float16 *)dst[t];
+      a.n_groups = (int64_t)cache->batch * n_new * cache->n_kv_heads * (TBQ4_HEAD_DIM / 8);
+      a.n_new = n_new;
+      a.n_kv_heads = cache->n_kv_heads;
+      a.capacity = cache->capacity;
+      a.pos = pos;
+      e = tbq4::launch_store_f16(a, (int)src_dtype, (hipStream_t)hip_stream);
+    }
+    s = from_hip(e);
+    if (s != TBQ4_OK) return s;
+  }
+  return TBQ4_OK;
+}
+
+tbq4_status tbq4_mixed_attn_decode(const tbq4_mixed_cache *cache, const void *q,
+                                   tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_ctx,
+                                   float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                   int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream) {
+  tbq4_cache view;
+  tbq4_status s = mixed_view(cache, view);
+  if (s != TBQ4_OK) return s;
+  if (!out) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  tbq4::DecodeArgs a;
+  s = prepare_decode(&view, q, q_dtype, n_q_heads, n_ctx, softmax_scale, n_splits, workspace,
+                     workspace_bytes, a);
+  if (s != TBQ4_OK) return s;
+  if (!aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  a.out = out;
+  a.k_fmt = cache->k_format;
+  a.v_fmt = cache->v_format;
+  a.rotate_out = cache->v_format == TBQ4_FMT_TBQ4 ? 1 : 0;
+  hipStream_t st = (hipStream_t)hip_stream;
+  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
+  if (s != TBQ4_OK) return s;
+  return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
 }
 
 int32_t verify_auto_splits(int32_t batch, int32_t n_kv_heads, int32_t n_q, int32_t n_kv) {
@@ -328,6 +425,7 @@ tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype 
   m.out = out;
   m.n_q_heads = n_q_heads;
   m.n_splits = P;
+  m.rotate_out = 1;
   memcpy(m.sign, a.sign, sizeof(a.sign));
   return from_hip(tbq4::launch_decode_merge(m, cache->batch * n_q, (int)out_dtype, st));
 }

@@ -41,9 +41,18 @@ constexpr int kVRow = 80;           // LDS bytes per staged V row (64 + pad)
 
 
 
-template <typename QT>
+// Cache formats of the K and V tensors (template arguments KF, VF): 0 = TBQ4
+// blocks (66 B per head vector), 1 = fp16 rows (256 B per head vector, not
+// rotated).  q is rotated when K is TBQ4; the merge applies R^T when V is.
+constexpr int kFmtTbq4 = 0, kFmtF16 = 1;
+constexpr int kF16Row = 288;        // LDS bytes per staged fp16 V row (256 + pad; 72 dwords
+                                    // put the 4 rows of one transposed read on distinct banks)
+
+template <typename QT, int KF, int VF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
+  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : 2 * kHeadDim;   // per head vector
+  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : 2 * kHeadDim;
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * (VF == kFmtTbq4 ? kVRow : kF16Row)];
   __shared__ __attribute__((aligned(16))) float sk[kTile];   // d^K * 2^-ex per token
   __shared__ __attribute__((aligned(16))) float sv[kTile + 32];   // d^V per token, then zeros
 
@@ -59,17 +68,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const float *sv_rd = lo_part ? sv + kTile : sv;
   if (lane < 32) sv[kTile + lane] = 0.0f;
 
-  // ---------------- q' = R q * scale * log2(e), split into fp16 hi + residual
+  // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
+  // fp16 K cache), split into fp16 hi + residual
   float qv[32];
   {
     const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim +
                    quarter * 32;
-    const uint32_t sw = a.sign[quarter];
+    const uint32_t sw = KF == kFmtTbq4 ? a.sign[quarter] : 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       float x = head < G ? load_q<QT>(qp + i) : 0.0f;
       qv[i] = ((sw >> i) & 1u) ? -x : x;
     }
+    if constexpr (KF == kFmtTbq4) {
 #pragma unroll
     for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -90,8 +101,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         qv[i] = upper ? (o - qv[i]) : (qv[i] + o);
       }
     }
+    }
   }
-  const float f = 0.08838834764831845f * a.qscale;
+  const float f = (KF == kFmtTbq4 ? 0.08838834764831845f : 1.0f) * a.qscale;
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -112,7 +124,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int el = 0; el < 8; ++el) {
-      const int i = 8 * c + (el < 4 ? 2 * el : 2 * el - 7);
+      // TBQ4 K operands hold the 4 even then the 4 odd dims of a code word;
+      // fp16 K operands hold 8 consecutive dims
+      const int i = KF == kFmtTbq4 ? 8 * c + (el < 4 ? 2 * el : 2 * el - 7) : 8 * c + el;
       const float x = ldexpf(qv[i], ex);
       const _Float16 hi = (_Float16)x;
       const _Float16 lo = (_Float16)(x - (float)hi);
@@ -129,10 +143,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int t_begin = split * tiles_per_split;
   const int t_end = min(t_begin + tiles_per_split, n_tiles);
 
-  const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
-  const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
-  const rsrc_t rk = make_rsrc(a.k + row, row_bytes);
-  const rsrc_t rv = make_rsrc(a.v + row, row_bytes);
+  const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity;
+  const rsrc_t rk = make_rsrc(a.k + row * kKBytes, (uint32_t)a.capacity * kKBytes);
+  const rsrc_t rv = make_rsrc(a.v + row * kVBytes, (uint32_t)a.capacity * kVBytes);
 
   float m_run = -INFINITY, l_run = 0.0f;
   float4v o[8];
@@ -147,6 +160,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int tok = 16 * (e >> 2) + 4 * quarter + (e & 3);
     tr_off = tok * kVRow + 8 * (col & 1);
   }
+  const int tr16_off = (4 * quarter + (col >> 2)) * kF16Row + 8 * (col & 3);
 
   // Raw fetch of one 32-token tile: per 16-token group, 5 words of K and of V
   // covering this lane's 16 index bytes (start offsets are even, so the words
@@ -158,26 +172,44 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // split is fetched at an offset beyond the buffer range, which the hardware
   // turns into zeros without a memory access, so every fetch is issued
   // unconditionally and the wait counts stay exact.
+  // (fp16 tensors: a lane fetches its token's 32 dims, 64 aligned bytes, as 4
+  // 16-byte loads; no scale.)
+  constexpr int kKW = KF == kFmtTbq4 ? 1 : 4, kVW = VF == kFmtTbq4 ? 1 : 4;
   struct Raw {
-    u32x4 k4[kBlk], v4[kBlk];
+    u32x4 k4[kBlk * kKW], v4[kBlk * kVW];
     uint32_t k1[kBlk], v1[kBlk];
     uint16_t sk, sv;
   };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
   const uint32_t shift = lane_off & 3u;
   auto fetch = [&](Raw &r, int t) {
-    const uint32_t base = t < t_end ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
+    const bool live = t < t_end;
+    const uint32_t base = live ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       const uint32_t a = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
-      r.k4[blk] = buf_load_x4(rk, a);
-      r.k1[blk] = buf_load_x1(rk, a + 16);
-      r.v4[blk] = buf_load_x4(rv, a);
-      r.v1[blk] = buf_load_x1(rv, a + 16);
+      if constexpr (KF == kFmtTbq4) {
+        r.k4[blk] = buf_load_x4(rk, a);
+        r.k1[blk] = buf_load_x1(rk, a + 16);
+      } else {
+        const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kKBytes + 64u * quarter)
+                                : 0xFFFF0000u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.k4[4 * blk + c] = buf_load_x4(rk, f + 16u * c);
+      }
+      if constexpr (VF == kFmtTbq4) {
+        r.v4[blk] = buf_load_x4(rv, a);
+        r.v1[blk] = buf_load_x1(rv, a + 16);
+      } else {
+        const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kVBytes + 64u * quarter)
+                                : 0xFFFF0000u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.v4[4 * blk + c] = buf_load_x4(rv, f + 16u * c);
+      }
     }
     const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
-    r.sk = buf_load_u16(rk, soff);
-    r.sv = buf_load_u16(rv, soff);
+    if constexpr (KF == kFmtTbq4) r.sk = buf_load_u16(rk, soff);
+    if constexpr (VF == kFmtTbq4) r.sv = buf_load_u16(rv, soff);
   };
 
   // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
@@ -185,26 +217,51 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   auto process = [&](Raw &r, int t, auto partial_tag) {
     constexpr bool kPartial = decltype(partial_tag)::value;
     const int tok0 = t * kTile;
+    // K words taken out of the fetch registers before the refill: TBQ4 code
+    // words realigned (converted to fp16 operands at the MFMA), or fp16 rows
     uint32_t kw[kBlk][4];
+    u32x4 kf[KF == kFmtTbq4 ? 1 : kBlk * 4];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
-      const u32x4 w = r.k4[blk];
-      kw[blk][0] = alignbyte(w[1], w[0], shift);
-      kw[blk][1] = alignbyte(w[2], w[1], shift);
-      kw[blk][2] = alignbyte(w[3], w[2], shift);
-      kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+      if constexpr (KF == kFmtTbq4) {
+        const u32x4 w = r.k4[blk];
+        kw[blk][0] = alignbyte(w[1], w[0], shift);
+        kw[blk][1] = alignbyte(w[2], w[1], shift);
+        kw[blk][2] = alignbyte(w[3], w[2], shift);
+        kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+      } else {
+        // fp16 slots >= n_ctx may hold anything: zero them (a NaN value would
+        // survive the -inf mask)
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[4 * blk + c] = dead ? u32x4{0u, 0u, 0u, 0u} : r.k4[4 * blk + c];
+      }
     }
+    auto k_operand = [&](int blk, int c) -> half8 {
+      if constexpr (KF == kFmtTbq4) return word_to_half8(kw[blk][c]);
+      else return __builtin_bit_cast(half8, kf[4 * blk + c]);
+    };
 
     __syncthreads();   // previous tile's LDS reads are done
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
-      const u32x4 w = r.v4[blk];
-      const u32x4 a = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
-                       alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
-      *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
+      if constexpr (VF == kFmtTbq4) {
+        const u32x4 w = r.v4[blk];
+        const u32x4 a = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
+                         alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
+        *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
+      } else {
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;   // (as for K)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *(u32x4 *)(vlds + (16 * blk + col) * kF16Row + 64 * quarter + 16 * c) =
+              dead ? u32x4{0u, 0u, 0u, 0u} : r.v4[4 * blk + c];
+      }
     }
     if (lane < kTile) {
-      float dk = half_bits_to_float(r.sk) * qs_inv, dv = half_bits_to_float(r.sv);
+      float dk = qs_inv, dv = 1.0f;
+      if constexpr (KF == kFmtTbq4) dk = half_bits_to_float(r.sk) * qs_inv;
+      if constexpr (VF == kFmtTbq4) dv = half_bits_to_float(r.sv);
       if constexpr (kPartial) {
         // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
         if (tok0 + lane >= n_ctx) dk = dv = 0.0f;
@@ -225,8 +282,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       acc[blk] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(word_to_half8(kw[blk][c]), qop[c],
-                                                          acc[blk], 0, 0, 0);
+        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c], acc[blk],
+                                                          0, 0, 0);
     }
     float sc[4];
 #pragma unroll
@@ -309,19 +366,36 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     half8 pa[kBlk / 2];
     pa[0] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 
-    // ---- O'^T += P~ V  (V read back transposed: 8 tokens x 1 byte per lane)
+    // ---- O'^T += P~ V
+    if constexpr (VF == kFmtTbq4) {
+      // V read back transposed: 8 tokens x 1 byte (2 dims) per lane
 #pragma unroll
-    for (int kk = 0; kk < kBlk / 2; ++kk) {
+      for (int kk = 0; kk < kBlk / 2; ++kk) {
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        typedef __attribute__((address_space(3))) int2v lds_i2;
-        const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i2 *)(vlds + tr_off + 32 * kk * kVRow + 16 * cg));
-        const uint32_t w0 = (uint32_t)r[0], w1 = (uint32_t)r[1];
-        const half8 ve = lo_nibbles_to_half8(w0, w1);
-        const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
-        o[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], ve, o[2 * cg], 0, 0, 0);
-        o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
+        for (int cg = 0; cg < 4; ++cg) {
+          typedef __attribute__((address_space(3))) int2v lds_i2;
+          const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i2 *)(vlds + tr_off + 32 * kk * kVRow + 16 * cg));
+          const uint32_t w0 = (uint32_t)r[0], w1 = (uint32_t)r[1];
+          const half8 ve = lo_nibbles_to_half8(w0, w1);
+          const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
+          o[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], ve, o[2 * cg], 0, 0, 0);
+          o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
+        }
+      }
+    } else {
+      // fp16 V: two 16-bit transposed reads give a lane 8 tokens of one dim
+      // (dim 16 db + col); source lanes point at token 4 quarter + col / 4
+      // (+ 16 for the second read) and dims 4 (col % 4) .. + 3 of the block
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        typedef __attribute__((address_space(3))) short4v lds_s4;
+        const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vlds + tr16_off + 32 * db));
+        const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4 *)(vlds + tr16_off + 16 * kF16Row + 32 * db));
+        const short8v vv = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0], __builtin_bit_cast(half8, vv), o[db],
+                                                       0, 0, 0);
       }
     }
   };
@@ -354,10 +428,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const int r = 4 * quarter + e;   // query head within the group
       if (r < G) {
         float *dst = wsb + (size_t)r * P * 130 + 2;
+        if constexpr (VF == kFmtTbq4) {
 #pragma unroll
-        for (int cg = 0; cg < 4; ++cg) {
-          dst[32 * cg + 2 * col] = o[2 * cg][e];
-          dst[32 * cg + 2 * col + 1] = o[2 * cg + 1][e];
+          for (int cg = 0; cg < 4; ++cg) {
+            dst[32 * cg + 2 * col] = o[2 * cg][e];
+            dst[32 * cg + 2 * col + 1] = o[2 * cg + 1][e];
+          }
+        } else {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) dst[16 * db + col] = o[db][e];
         }
       }
     }
@@ -425,6 +504,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   o0 *= inv;
   o1 *= inv;
+  OT *dst = (OT *)a.out + ((size_t)b * a.n_q_heads + h) * kHeadDim;
+  if (!a.rotate_out) {   // an fp16 V cache is not rotated
+    dst[lane] = (OT)o0;
+    dst[lane + 64] = (OT)o1;
+    return;
+  }
   // o = s * (H o') / sqrt(128)
 #pragma unroll
   for (int hh = 1; hh < 64; hh <<= 1) {
@@ -443,7 +528,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const bool n1 = (a.sign[2 + (lane >> 5)] >> (lane & 31)) & 1u;
   o0 = n0 ? -o0 * r : o0 * r;
   o1 = n1 ? -o1 * r : o1 * r;
-  OT *dst = (OT *)a.out + ((size_t)b * a.n_q_heads + h) * kHeadDim;
   dst[lane] = (OT)o0;
   dst[lane + 64] = (OT)o1;
 }
@@ -451,8 +535,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
                                  hipEvent_t start, hipEvent_t stop) {
   dim3 grid(a.n_splits, a.n_kv_heads, batch);
-  const void *fn = q_dtype == 0 ? reinterpret_cast<const void *>(&decode_split_kernel<float>)
-                                : reinterpret_cast<const void *>(&decode_split_kernel<_Float16>);
+  // (q dtype, K format, V format) -> kernel instance
+  static const void *const kernels[2][2][2] = {
+      {{reinterpret_cast<const void *>(&decode_split_kernel<float, 0, 0>),
+        reinterpret_cast<const void *>(&decode_split_kernel<float, 0, 1>)},
+       {reinterpret_cast<const void *>(&decode_split_kernel<float, 1, 0>),
+        reinterpret_cast<const void *>(&decode_split_kernel<float, 1, 1>)}},
+      {{reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 0, 0>),
+        reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 0, 1>)},
+       {reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 1, 0>),
+        reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 1, 1>)}}};
+  if (a.k_fmt < 0 || a.k_fmt > 1 || a.v_fmt < 0 || a.v_fmt > 1) return hipErrorInvalidValue;
+  const void *fn = kernels[q_dtype == 0 ? 0 : 1][a.k_fmt][a.v_fmt];
   DecodeArgs arg = a;
   void *params[] = {&arg};
   if (start || stop)

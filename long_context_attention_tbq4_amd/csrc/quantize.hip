@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int64_t gblock = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int tensor = gblock >= a.blocks_per_tensor ? 1 : 0;
   const int64_t i = gblock - (int64_t)tensor * a.blocks_per_tensor;
-  if (tensor == 1 && a.flat) return;
+  // the grid is rounded up to whole 4-wavefront workgroups: wavefronts past
+  // the last tensor of this launch (one or two tensors) have no block
+  if (tensor >= a.n_tensors) return;
   if (i >= a.blocks_per_tensor) return;
 
   const T *src;
@@ -160,7 +162,43 @@ template __global__ void quantize_kernel<float>(QuantArgs);
 template __global__ void quantize_kernel<_Float16>(QuantArgs);
 template __global__ void quantize_kernel<uint16_t>(QuantArgs);
 
-hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream) {
+// fp16 cache rows (the mixed-format caches): x -> binary16, round to nearest
+// even (overflow to infinity), one thread per 8 consecutive values.  Source
+// [batch][n_new][n_kv_heads][128]; destination [batch][n_kv_heads][capacity][128]
+// fp16 at slots pos .. pos + n_new - 1.
+template <typename T>
+__global__ __launch_bounds__(256) void store_f16_kernel(StoreF16Args a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // group of 8 values
+  if (i >= a.n_groups) return;
+  const int64_t vec = i >> 4;                                   // head vector
+  const int dim0 = (int)(i & 15) * 8;
+  const int64_t h = vec % a.n_kv_heads;
+  const int64_t t = (vec / a.n_kv_heads) % a.n_new;
+  const int64_t b = vec / ((int64_t)a.n_kv_heads * a.n_new);
+  const T *src = (const T *)a.src + vec * kHeadDim + dim0;
+  _Float16 *dst = a.dst + ((b * a.n_kv_heads + h) * a.capacity + a.pos + t) * kHeadDim + dim0;
+  half8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (_Float16)(float)load_exact<T>(src + e);
+  *(half8 *)dst = v;
+}
+
+hipError_t launch_store_f16(const StoreF16Args &a, int dtype, hipStream_t stream) {
+  const int64_t grid = (a.n_groups + 255) / 256;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(store_f16_kernel<float>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(store_f16_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(store_f16_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs &args, int dtype, int tensors, hipStream_t stream) {
+  if (tensors < 1 || tensors > 2 || (args.flat && tensors != 1)) return hipErrorInvalidValue;
+  QuantArgs a = args;
+  a.n_tensors = tensors;
   const int64_t blocks = a.blocks_per_tensor * tensors;
   const int64_t grid = (blocks + 3) / 4;
   if (grid == 0) return hipSuccess;

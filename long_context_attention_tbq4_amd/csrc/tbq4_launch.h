@@ -11,9 +11,17 @@ struct QuantArgs {
   int64_t blocks_per_tensor;   // blocks per source tensor
   int32_t n_new, n_kv_heads, capacity, pos;
   int32_t flat;                // 1: block i -> src + 128 i, dst + 66 i
+  int32_t n_tensors;           // 1 or 2 tensors in this launch (set by launch_quantize)
   const int32_t *pos_dev;      // device [batch] first slot per sequence, or null (use pos)
   uint32_t sign_lo, sign_hi;   // sign bits 0..31, 32..63
   uint32_t sign_lo2, sign_hi2; // sign bits 64..95, 96..127
+};
+
+struct StoreF16Args {
+  const void *src;             // [batch][n_new][n_kv_heads][128]
+  _Float16 *dst;               // [batch][n_kv_heads][capacity][128]
+  int64_t n_groups;            // batch * n_new * n_kv_heads * 16
+  int32_t n_new, n_kv_heads, capacity, pos;
 };
 
 struct DecodeArgs {
@@ -26,6 +34,8 @@ struct DecodeArgs {
   int32_t n_kv_heads, n_q_heads, group, capacity;
   int32_t n_ctx;         // context length, or the upper bound of ctx_lens
   int32_t n_splits;
+  int32_t k_fmt, v_fmt;  // cache formats: 0 TBQ4 blocks, 1 fp16 rows
+  int32_t rotate_out;    // merge applies R^T (the V cache holds rotated values)
   float qscale;          // softmax_scale * log2(e)
   uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
 };
@@ -53,6 +63,7 @@ struct PrefillArgs {
 constexpr int kDecodeTile = 32;
 
 hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream);
+hipError_t launch_store_f16(const StoreF16Args &a, int dtype, hipStream_t stream);
 // With start/stop events the dispatch itself records them (hipExtLaunchKernel).
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

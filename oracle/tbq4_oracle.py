@@ -234,6 +234,24 @@ def dequantize_blocks(packed, seed=0):
 
 
 # --------------------------------------------------------------------------
+# fp16 cache rows (mixed K/V cache formats).  Page "Kontekst 262K na jednej
+# RTX 4090: co dodałem do llama.cpp-turboq", section "Konfiguracja": the K and
+# V cache types are chosen separately; the plain alternative to TBQ4 is an fp16
+# cache.  A head vector is stored as 128 IEEE binary16 values, each the
+# binary16 nearest to the input (ties to even; beyond the largest finite value
+# it overflows to infinity), not rotated.
+# --------------------------------------------------------------------------
+def f16_rows(x):
+    """IEEE binary16 of every element (numpy's float32 -> float16 cast rounds
+    to nearest even; the fp32 input is exact in float32)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+def dequantize_f16(rows):
+    return np.asarray(rows, dtype=np.float16).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
 # Attention on the dequantised cache (plain softmax attention, fp64)
 # --------------------------------------------------------------------------
 def _softmax_rows(s):

@@ -315,3 +315,51 @@ def test_unpack_inverts_pack():
     for r in range(3):
         for i in range(128):
             assert y[r, i] == float(Fraction(d[r]) * Fraction(o.CODE_VALUES[idx[r, i]]))
+
+
+def _nearest_binary16_bruteforce(x):
+    """Nearest finite binary16 by search over every bit pattern (exact
+    rationals); ties to the even pattern; |x| >= 65520 overflows to inf."""
+    from fractions import Fraction
+    import bisect
+    vals = sorted({Fraction(float(np.uint16(b).view(np.float16))): None
+                   for b in range(0x7C00)}.keys())            # +0 .. 65504
+    out = []
+    for xv in x:
+        f = Fraction(float(xv))
+        a = abs(f)
+        if a >= 65520:
+            out.append(np.float16(np.inf) if f > 0 else np.float16(-np.inf))
+            continue
+        i = bisect.bisect_left(vals, a)
+        if i == len(vals):            # (65504, 65520): below the overflow midpoint
+            r = vals[-1]
+        elif vals[i] == a:
+            r = vals[i]
+        else:
+            lo, hi = vals[i - 1], vals[i]
+            if a - lo < hi - a:
+                r = lo
+            elif hi - a < a - lo:
+                r = hi
+            else:   # tie: the even bit pattern
+                r = lo if (np.float16(float(lo)).view(np.uint16) & 1) == 0 else hi
+        out.append(-np.float16(float(r)) if np.signbit(xv) else np.float16(float(r)))
+    return np.array(out, dtype=np.float16)
+
+
+def test_f16_rows_round_to_nearest_even_against_bruteforce():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(300).astype(np.float32) * np.float32(10.0) ** rng.integers(-8, 5, 300),
+        np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -24, 2 ** -25, 3 * 2 ** -26,
+                  65504.0, 65519.0, 65520.0, -65520.0, 1e6, -0.0, 0.0], dtype=np.float32),
+    ])
+    with np.errstate(over="ignore"):
+        got = o.f16_rows(x)
+    ref = _nearest_binary16_bruteforce(x)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+    # exact halfway cases go to the even pattern: 1 + 2^-11 -> 1.0, 1 + 3*2^-11 -> 1 + 2^-9
+    assert o.f16_rows(np.float32(1 + 2 ** -11)) == np.float16(1.0)
+    assert o.f16_rows(np.float32(1 + 3 * 2 ** -11)) == np.float16(1 + 2 ** -9)
+    assert np.array_equal(o.dequantize_f16(got[:5]), got[:5].astype(np.float64))
