@@ -99,6 +99,40 @@ def quantize_block(x, seed=0):
     return out
 
 
+_MAGS3 = [0.25, 0.75, 1.375, 2.25]
+
+
+def quantize_block3(x, seed=0):
+    """One block of 128 floats -> 50 TBQ3 bytes (list of ints): the same
+    rotation and scale as TBQ4, 3-bit sign-magnitude codes (bit 2 = sign),
+    code i at bits 3i .. 3i+2 of the little-endian integer in bytes 2..49,
+    built here with Python big-integer arithmetic."""
+    s = signs(seed)
+    v = [float(x[i]) * s[i] for i in range(128)]
+    h = 1
+    while h < 128:
+        for i in range(128):
+            if i & h == 0:
+                a, b = v[i], v[i + h]
+                v[i], v[i + h] = a + b, a - b
+        h *= 2
+    u = [vi * _R for vi in v]
+    p = [ui * ui for ui in u]
+    h = 64
+    while h >= 1:
+        for i in range(h):
+            p[i] = p[i] + p[i + h]
+        h //= 2
+    dbits = _half_round_sqrt_exact(p[0] * 2.0 ** -7)
+    d = float(_half_from_bits(dbits))
+    tau = [(_MAGS3[k] + _MAGS3[k + 1]) / 2.0 for k in range(3)]
+    big = 0
+    for i, ui in enumerate(u):
+        code = sum(1 for t in tau if d * t < abs(ui)) + (4 if ui < 0 else 0)
+        big |= code << (3 * i)
+    return [dbits & 0xFF, dbits >> 8] + list(big.to_bytes(48, "little"))
+
+
 def dequantize_block(block, seed=0):
     """66 bytes -> 128 floats in the original domain."""
     s = signs(seed)

@@ -171,12 +171,9 @@ def half_bits_to_float(bits):
 # --------------------------------------------------------------------------
 # Quantiser
 # --------------------------------------------------------------------------
-def quantize_blocks(x, seed=0):
-    """Quantise blocks of 128 values to TBQ4.
-
-    x: array (..., 128) in fp32 / fp16 / fp64 (converted to fp64 exactly).
-    Returns (packed uint8 (..., 66), codes uint8 (..., 128), d_bits uint16 (...)).
-    """
+def _rotate_and_scale(x, seed):
+    """The steps TBQ4 and TBQ3 share: u = R x in fp64 and the binary16 scale
+    d nearest sqrt(mean u^2).  Returns (u, d_bits, d)."""
     signs = sign_vector(seed)
     x = np.asarray(x)
     if x.shape[-1] != HEAD_DIM:
@@ -194,7 +191,17 @@ def quantize_blocks(x, seed=0):
     ms = p[..., 0] * (2.0 ** -7)
 
     d_bits = half_nearest_sqrt(ms)
-    d = half_bits_to_float(d_bits)
+    return u, d_bits, half_bits_to_float(d_bits)
+
+
+def quantize_blocks(x, seed=0):
+    """Quantise blocks of 128 values to TBQ4.
+
+    x: array (..., 128) in fp32 / fp16 / fp64 (converted to fp64 exactly).
+    Returns (packed uint8 (..., 66), codes uint8 (..., 128), d_bits uint16 (...)).
+    """
+    x = np.asarray(x)
+    u, d_bits, d = _rotate_and_scale(x, seed)
 
     # code = sign bit | number of scaled magnitude thresholds below |u|
     # (d * tau_k is exact in fp64)
@@ -231,6 +238,75 @@ def dequantize_rotated(packed):
 def dequantize_blocks(packed, seed=0):
     """x_hat = R^T (d * c[idx]) in fp64: the block in the original domain."""
     return unrotate(dequantize_rotated(packed), sign_vector(seed))
+
+
+# --------------------------------------------------------------------------
+# TBQ3: the same method with 3-bit codes.  The page "Kontekst 262K na jednej
+# RTX 4090: co dodałem do llama.cpp-turboq", section "6. Ten sam cache na
+# Apple silicon", names a TBQ3 KV cache beside TBQ4 (with a fix to its 3-bit
+# packing) and rotated-domain dequantisation in attention for both; the TBQ3
+# layout is not given.  Reading
+# (the plainest one consistent with TBQ4): 128 values -> a 2-byte binary16
+# scale (the same RMS rule) + 48 bytes of 3-bit codes = 50 bytes, 3.125 bits
+# per value; the same rotation; the least-MSE sign-symmetric 8-level
+# quantiser of N(0,1) whose levels have at most four significant bits; a code
+# is sign-magnitude (bit 2 set for u < 0, bits 0-1 the magnitude index = the
+# number of scaled magnitude midpoints below |u|: nearest level, ties toward
+# zero, u = 0 -> +0.25); code i occupies bits 3i .. 3i+2 of the 384-bit
+# little-endian integer held in bytes 2..49 (codes cross byte boundaries).
+# --------------------------------------------------------------------------
+BLOCK_BYTES3 = 50
+MAGNITUDES3 = np.array([0.25, 0.75, 1.375, 2.25], dtype=np.float64)
+CODEBOOK3 = np.concatenate([-MAGNITUDES3[::-1], MAGNITUDES3])
+MAG_THRESHOLDS3 = (MAGNITUDES3[:-1] + MAGNITUDES3[1:]) / 2.0   # 0.5, 1.0625, 1.8125
+CODE_VALUES3 = np.concatenate([MAGNITUDES3, -MAGNITUDES3])     # value of code 0..7
+
+
+def pack3(codes):
+    """codes uint8 (..., 128) in 0..7 -> (..., 48) bytes: code i at bits
+    3i .. 3i+2 of the little-endian bit string."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    bits = (codes[..., :, None] >> np.arange(3, dtype=np.uint8)) & 1      # (..., 128, 3)
+    bits = bits.reshape(codes.shape[:-1] + (3 * HEAD_DIM,))
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def unpack3(packed48):
+    bits = np.unpackbits(np.asarray(packed48, dtype=np.uint8), axis=-1, bitorder="little")
+    bits = bits.reshape(bits.shape[:-1] + (HEAD_DIM, 3))
+    return (bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)).astype(np.uint8)
+
+
+def quantize_blocks3(x, seed=0):
+    """Quantise blocks of 128 values to TBQ3.  Returns (packed uint8 (..., 50),
+    codes uint8 (..., 128), d_bits uint16 (...))."""
+    x = np.asarray(x)
+    u, d_bits, d = _rotate_and_scale(x, seed)
+    thr = d[..., None] * MAG_THRESHOLDS3                  # exact in fp64
+    mag = (thr[..., None, :] < np.abs(u)[..., :, None]).sum(axis=-1)
+    idx = (mag + 4 * (u < 0)).astype(np.uint8)
+    packed = np.empty(x.shape[:-1] + (BLOCK_BYTES3,), dtype=np.uint8)
+    packed[..., 0] = (d_bits & 0xFF).astype(np.uint8)
+    packed[..., 1] = (d_bits >> 8).astype(np.uint8)
+    packed[..., 2:] = pack3(idx)
+    return packed, idx, d_bits
+
+
+def unpack_blocks3(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.shape[-1] != BLOCK_BYTES3:
+        raise ValueError("last axis must be 50 bytes")
+    d_bits = packed[..., 0].astype(np.uint16) | (packed[..., 1].astype(np.uint16) << 8)
+    return unpack3(packed[..., 2:]), half_bits_to_float(d_bits)
+
+
+def dequantize_rotated3(packed):
+    idx, d = unpack_blocks3(packed)
+    return d[..., None] * CODE_VALUES3[idx]
+
+
+def dequantize_blocks3(packed, seed=0):
+    return unrotate(dequantize_rotated3(packed), sign_vector(seed))
 
 
 # --------------------------------------------------------------------------
