@@ -196,14 +196,26 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
  *   TBQ4_FMT_F16   head vectors stored as 128 binary16 values (round to
  *                  nearest even from the input, overflow to infinity), not
  *                  rotated: 256 bytes per head vector
+ *   TBQ4_FMT_TBQ3  50-byte blocks, the 3-bit sibling of TBQ4 (same page,
+ *                  section "6. Ten sam cache na Apple silicon", which runs a
+ *                  TBQ3 cache beside TBQ4 and fixes its 3-bit packing).  The
+ *                  page gives no codebook, so this library reads it as: the
+ *                  same rotation and binary16 scale d as TBQ4, then per
+ *                  rotated value the nearest of +-d x {0.25, 0.75, 1.375,
+ *                  2.25} (the 8-level Gaussian quantiser restricted to four
+ *                  significant bits; ties go to the smaller magnitude), code
+ *                  = magnitude index | 4 if negative; code i sits at bits
+ *                  3i .. 3i+2 of the little-endian integer held in bytes
+ *                  2 .. 49.  3.125 bits per value.
  * tbq4_mixed_cache: k, v point at [batch][n_kv_heads][capacity][row bytes of
  * their format] (tbq4_format_row_bytes), 16-byte aligned; the rest as in
  * the TBQ4-only descriptor, capacity a multiple of 8.
  * tbq4_mixed_append: as tbq4_quantize_append, each tensor in its format.
  * tbq4_mixed_attn_decode: as tbq4_attn_decode (same workspace size, G <= 8):
- *   q is rotated only when K is TBQ4, and the output is rotated back only
- *   when V is TBQ4.  Any combination of the two formats is accepted. */
-typedef enum { TBQ4_FMT_TBQ4 = 0, TBQ4_FMT_F16 = 1 } tbq4_format;
+ *   q is rotated only when K is stored rotated (TBQ4 or TBQ3), and the
+ *   output is rotated back only when V is.  Any combination of the three
+ *   formats is accepted. */
+typedef enum { TBQ4_FMT_TBQ4 = 0, TBQ4_FMT_F16 = 1, TBQ4_FMT_TBQ3 = 2 } tbq4_format;
 typedef struct {
   uint8_t *k;
   uint8_t *v;

@@ -41,18 +41,23 @@ constexpr int kVRow = 80;           // LDS bytes per staged V row (64 + pad)
 
 
 
-// Cache formats of the K and V tensors (template arguments KF, VF): 0 = TBQ4
-// blocks (66 B per head vector), 1 = fp16 rows (256 B per head vector, not
-// rotated).  q is rotated when K is TBQ4; the merge applies R^T when V is.
-constexpr int kFmtTbq4 = 0, kFmtF16 = 1;
+// Cache formats of the K and V tensors (template arguments KF, VF): TBQ4
+// blocks, fp16 rows (not rotated) or TBQ3 blocks.  q is rotated when K is a
+// TBQ format; the merge applies R^T when V is.
+constexpr int kE4Row = 144;         // LDS bytes per staged TBQ3 V row: 128 e4m3 bytes + pad
+                                    // (36 dwords: the 8 rows of one byte-transposed read
+                                    // fall on distinct banks)
 constexpr int kF16Row = 288;        // LDS bytes per staged fp16 V row (256 + pad; 72 dwords
                                     // put the 4 rows of one transposed read on distinct banks)
 
 template <typename QT, int KF, int VF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
-  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : 2 * kHeadDim;   // per head vector
-  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : 2 * kHeadDim;
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * (VF == kFmtTbq4 ? kVRow : kF16Row)];
+  // bytes per head vector of each tensor
+  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : VF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+  constexpr bool kKRot = KF != kFmtF16, kVRot = VF != kFmtF16;   // stored rotated
+  __shared__ __attribute__((aligned(16))) uint8_t
+      vlds[kTile * (VF == kFmtTbq4 ? kVRow : VF == kFmtTbq3 ? kE4Row : kF16Row)];
   __shared__ __attribute__((aligned(16))) float sk[kTile];   // d^K * 2^-ex per token
   __shared__ __attribute__((aligned(16))) float sv[kTile + 32];   // d^V per token, then zeros
 
@@ -74,13 +79,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   {
     const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim +
                    quarter * 32;
-    const uint32_t sw = KF == kFmtTbq4 ? a.sign[quarter] : 0u;
+    const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       float x = head < G ? load_q<QT>(qp + i) : 0.0f;
       qv[i] = ((sw >> i) & 1u) ? -x : x;
     }
-    if constexpr (KF == kFmtTbq4) {
+    if constexpr (kKRot) {
 #pragma unroll
     for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     }
   }
-  const float f = (KF == kFmtTbq4 ? 0.08838834764831845f : 1.0f) * a.qscale;
+  const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int el = 0; el < 8; ++el) {
       // TBQ4 K operands hold the 4 even then the 4 odd dims of a code word;
-      // fp16 K operands hold 8 consecutive dims
+      // fp16 and TBQ3 K operands hold 8 consecutive dims
       const int i = KF == kFmtTbq4 ? 8 * c + (el < 4 ? 2 * el : 2 * el - 7) : 8 * c + el;
       const float x = ldexpf(qv[i], ex);
       const _Float16 hi = (_Float16)x;
@@ -161,6 +166,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     tr_off = tok * kVRow + 8 * (col & 1);
   }
   const int tr16_off = (4 * quarter + (col >> 2)) * kF16Row + 8 * (col & 3);
+  // TBQ3 V (e4m3 rows): source lane s of a 16-lane group points at the
+  // token of P~ operand position 8 quarter + s/2 and bytes 8 (s & 1) .. + 7
+  // of a 16-dim block, so a byte-transposed read gives a lane 8 tokens of
+  // dim 16 db + col
+  int tr8_3_off;
+  {
+    const int j = col >> 1;
+    const int tok = j < 4 ? 4 * quarter + j : 16 + 4 * quarter + (j - 4);
+    tr8_3_off = tok * kE4Row + 8 * (col & 1);
+  }
 
   // Raw fetch of one 32-token tile: per 16-token group, 5 words of K and of V
   // covering this lane's 16 index bytes (start offsets are even, so the words
@@ -174,14 +189,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // unconditionally and the wait counts stay exact.
   // (fp16 tensors: a lane fetches its token's 32 dims, 64 aligned bytes, as 4
   // 16-byte loads; no scale.)
-  constexpr int kKW = KF == kFmtTbq4 ? 1 : 4, kVW = VF == kFmtTbq4 ? 1 : 4;
+  // (TBQ3: a lane's 32 codes are 12 bytes at an even offset: one 16-byte
+  // load at the word-aligned offset below covers them.)
+  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : 1;
   struct Raw {
     u32x4 k4[kBlk * kKW], v4[kBlk * kVW];
     uint32_t k1[kBlk], v1[kBlk];
     uint16_t sk, sv;
   };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
-  const uint32_t shift = lane_off & 3u;
+  const uint32_t shift = lane_off & 3u;   // (2 col + 2) mod 4: the same for TBQ3
+  // word-aligned start of this lane's code bytes of tile t, block blk
+  auto code_addr = [&](bool live, int t, int blk, uint32_t bb, uint32_t per_quarter) -> uint32_t {
+    if (!live) return 0xFFFF0000u;
+    return ((uint32_t)(t * kTile + 16 * blk + col) * bb + 2u + per_quarter * quarter) & ~3u;
+  };
   auto fetch = [&](Raw &r, int t) {
     const bool live = t < t_end;
     const uint32_t base = live ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
@@ -191,6 +213,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       if constexpr (KF == kFmtTbq4) {
         r.k4[blk] = buf_load_x4(rk, a);
         r.k1[blk] = buf_load_x1(rk, a + 16);
+      } else if constexpr (KF == kFmtTbq3) {
+        r.k4[blk] = buf_load_x4(rk, code_addr(live, t, blk, kBlockBytes3, 12u));
       } else {
         const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kKBytes + 64u * quarter)
                                 : 0xFFFF0000u;
@@ -200,6 +224,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       if constexpr (VF == kFmtTbq4) {
         r.v4[blk] = buf_load_x4(rv, a);
         r.v1[blk] = buf_load_x1(rv, a + 16);
+      } else if constexpr (VF == kFmtTbq3) {
+        r.v4[blk] = buf_load_x4(rv, code_addr(live, t, blk, kBlockBytes3, 12u));
       } else {
         const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kVBytes + 64u * quarter)
                                 : 0xFFFF0000u;
@@ -208,8 +234,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
     const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
+    const uint32_t soff3 = lane < kTile && live ? (uint32_t)(t * kTile + lane) * kBlockBytes3 : 0xFFFF0000u;
     if constexpr (KF == kFmtTbq4) r.sk = buf_load_u16(rk, soff);
+    if constexpr (KF == kFmtTbq3) r.sk = buf_load_u16(rk, soff3);
     if constexpr (VF == kFmtTbq4) r.sv = buf_load_u16(rv, soff);
+    if constexpr (VF == kFmtTbq3) r.sv = buf_load_u16(rv, soff3);
   };
 
   // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
@@ -220,7 +249,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // K words taken out of the fetch registers before the refill: TBQ4 code
     // words realigned (converted to fp16 operands at the MFMA), or fp16 rows
     uint32_t kw[kBlk][4];
-    u32x4 kf[KF == kFmtTbq4 ? 1 : kBlk * 4];
+    u32x4 kf[KF == kFmtF16 ? kBlk * 4 : 1];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       if constexpr (KF == kFmtTbq4) {
@@ -229,6 +258,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         kw[blk][1] = alignbyte(w[2], w[1], shift);
         kw[blk][2] = alignbyte(w[3], w[2], shift);
         kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+      } else if constexpr (KF == kFmtTbq3) {
+        const u32x4 w = r.k4[blk];       // 96 code bits of the lane's 32 dims
+        kw[blk][0] = alignbyte(w[1], w[0], shift);
+        kw[blk][1] = alignbyte(w[2], w[1], shift);
+        kw[blk][2] = alignbyte(w[3], w[2], shift);
       } else {
         // fp16 slots >= n_ctx may hold anything: zero them (a NaN value would
         // survive the -inf mask)
@@ -239,6 +273,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     auto k_operand = [&](int blk, int c) -> half8 {
       if constexpr (KF == kFmtTbq4) return word_to_half8(kw[blk][c]);
+      else if constexpr (KF == kFmtTbq3)
+        return tbq3_chunk_to_half8(tbq3_chunk(kw[blk][0], kw[blk][1], kw[blk][2], c));
       else return __builtin_bit_cast(half8, kf[4 * blk + c]);
     };
 
@@ -250,6 +286,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         const u32x4 a = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
                          alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
         *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
+      } else if constexpr (VF == kFmtTbq3) {
+        // the lane's 32 codes -> 32 e4m3 bytes (dims 32 quarter ..) in LDS
+        const u32x4 w = r.v4[blk];
+        const uint32_t w0 = alignbyte(w[1], w[0], shift), w1 = alignbyte(w[2], w[1], shift),
+                       w2 = alignbyte(w[3], w[2], shift);
+        uint32_t e[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tbq3_chunk_to_e4m3(tbq3_chunk(w0, w1, w2, c), e[2 * c], e[2 * c + 1]);
+        uint8_t *row = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
+        *(u32x4 *)row = u32x4{e[0], e[1], e[2], e[3]};
+        *(u32x4 *)(row + 16) = u32x4{e[4], e[5], e[6], e[7]};
       } else {
         const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;   // (as for K)
 #pragma unroll
@@ -260,8 +307,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     if (lane < kTile) {
       float dk = qs_inv, dv = 1.0f;
-      if constexpr (KF == kFmtTbq4) dk = half_bits_to_float(r.sk) * qs_inv;
-      if constexpr (VF == kFmtTbq4) dv = half_bits_to_float(r.sv);
+      if constexpr (KF != kFmtF16) dk = half_bits_to_float(r.sk) * qs_inv;
+      if constexpr (VF != kFmtF16) dv = half_bits_to_float(r.sv);
       if constexpr (kPartial) {
         // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
         if (tok0 + lane >= n_ctx) dk = dv = 0.0f;
@@ -382,6 +429,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
           o[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], ve, o[2 * cg], 0, 0, 0);
           o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
         }
+      }
+    } else if constexpr (VF == kFmtTbq3) {
+      // TBQ3 V staged as e4m3 bytes: one byte-transposed read per 16 dims
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        typedef __attribute__((address_space(3))) int2v lds_i2;
+        const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            pa[0], e4m3x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]), o[db], 0, 0, 0);
       }
     } else {
       // fp16 V: two 16-bit transposed reads give a lane 8 tokens of one dim
@@ -536,16 +592,14 @@ hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hi
                                  hipEvent_t start, hipEvent_t stop) {
   dim3 grid(a.n_splits, a.n_kv_heads, batch);
   // (q dtype, K format, V format) -> kernel instance
-  static const void *const kernels[2][2][2] = {
-      {{reinterpret_cast<const void *>(&decode_split_kernel<float, 0, 0>),
-        reinterpret_cast<const void *>(&decode_split_kernel<float, 0, 1>)},
-       {reinterpret_cast<const void *>(&decode_split_kernel<float, 1, 0>),
-        reinterpret_cast<const void *>(&decode_split_kernel<float, 1, 1>)}},
-      {{reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 0, 0>),
-        reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 0, 1>)},
-       {reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 1, 0>),
-        reinterpret_cast<const void *>(&decode_split_kernel<_Float16, 1, 1>)}}};
-  if (a.k_fmt < 0 || a.k_fmt > 1 || a.v_fmt < 0 || a.v_fmt > 1) return hipErrorInvalidValue;
+#define TBQ4_DEC(QT, KF, VF) reinterpret_cast<const void *>(&decode_split_kernel<QT, KF, VF>)
+#define TBQ4_DEC_K(QT, KF) {TBQ4_DEC(QT, KF, 0), TBQ4_DEC(QT, KF, 1), TBQ4_DEC(QT, KF, 2)}
+  static const void *const kernels[2][3][3] = {
+      {TBQ4_DEC_K(float, 0), TBQ4_DEC_K(float, 1), TBQ4_DEC_K(float, 2)},
+      {TBQ4_DEC_K(_Float16, 0), TBQ4_DEC_K(_Float16, 1), TBQ4_DEC_K(_Float16, 2)}};
+#undef TBQ4_DEC_K
+#undef TBQ4_DEC
+  if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
   const void *fn = kernels[q_dtype == 0 ? 0 : 1][a.k_fmt][a.v_fmt];
   DecodeArgs arg = a;
   void *params[] = {&arg};

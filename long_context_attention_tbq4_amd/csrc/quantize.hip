@@ -59,8 +59,9 @@ template <> __device__ __forceinline__ double load_exact<uint16_t>(const uint16_
 }
 
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+  constexpr int64_t kBB = FMT == kFmtTbq3 ? kBlockBytes3 : kBlockBytes;   // bytes per block
   const int lane = threadIdx.x & 63;
   const int64_t gblock = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int tensor = gblock >= a.blocks_per_tensor ? 1 : 0;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   uint8_t *dst;
   if (a.flat) {
     src = (const T *)a.src[0] + i * kHeadDim;
-    dst = a.dst[0] + i * kBlockBytes;
+    dst = a.dst[0] + i * kBB;
   } else {
     // source [batch][n_new][n_kv_heads][128]; cache [batch][n_kv_heads][capacity][66]
     const int64_t h = i % a.n_kv_heads;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int64_t slot = (a.pos_dev ? (int64_t)a.pos_dev[b] : (int64_t)a.pos) + t;
     if (slot < 0 || slot >= a.capacity) return;
     src = (const T *)a.src[tensor] + i * kHeadDim;
-    dst = a.dst[tensor] + ((b * a.n_kv_heads + h) * a.capacity + slot) * kBlockBytes;
+    dst = a.dst[tensor] + ((b * a.n_kv_heads + h) * a.capacity + slot) * kBB;
   }
 
   // signs of elements lane and lane+64
@@ -131,10 +132,43 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int dbits = half_round_sqrt(ms);
   const double d = half_value(dbits);
 
+  const double a0 = fabs(u0), a1 = fabs(u1);
+  if constexpr (FMT == kFmtTbq3) {
+    // TBQ3: bit 2 = sign, bits 0-1 = number of scaled midpoints of the
+    // magnitudes 0.25 0.75 1.375 2.25 below |u|; code i at bits 3i .. 3i+2
+    // of the little-endian integer in bytes 2..49
+    const double tau3[3] = {0.5, 1.0625, 1.8125};
+    int c0 = u0 < 0.0 ? 4 : 0, c1 = u1 < 0.0 ? 4 : 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const double dt = d * tau3[k];
+      c0 += dt < a0 ? 1 : 0;
+      c1 += dt < a1 ? 1 : 0;
+    }
+    // lane w < 12 assembles bits 32w .. 32w+31: the codes i with
+    // 3i + 3 > 32w and 3i < 32w + 32 (code i lives in lane i & 63)
+    const int both = c0 | (c1 << 8);
+    const int w = lane < 12 ? lane : 0;
+    const int i_first = (32 * w) / 3;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      const int i = i_first + k;
+      const int src = __shfl(both, i & 63, 64);
+      const uint32_t c = (uint32_t)((i >= 64 ? src >> 8 : src) & 7);
+      const int off = 3 * i - 32 * w;
+      if (i < 128 && off < 32) word |= off >= 0 ? (c << off) : (c >> -off);
+    }
+    // 24 half-words at byte 2 + 2j (block starts are 2-byte aligned)
+    const uint32_t wj = (uint32_t)__shfl((int)word, (lane >> 1) & 15, 64);
+    if (lane < 24) *(uint16_t *)(dst + 2 + 2 * lane) = (uint16_t)(wj >> (16 * (lane & 1)));
+    if (lane == 0) *(uint16_t *)dst = (uint16_t)dbits;
+    return;
+  }
+
   // sign-magnitude code: bit 3 = sign of u, bits 0-2 = number of scaled
   // magnitude midpoints strictly below |u| (d * tau_k is exact)
   const double tau[7] = {0.25, 0.5, 0.78125, 1.09375, 1.4375, 1.8125, 2.375};
-  const double a0 = fabs(u0), a1 = fabs(u1);
   int i0 = u0 < 0.0 ? 8 : 0, i1 = u1 < 0.0 ? 8 : 0;
 #pragma unroll
   for (int k = 0; k < 7; ++k) {
@@ -158,9 +192,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   if (lane == 0) *(uint16_t *)dst = (uint16_t)dbits;
 }
 
-template __global__ void quantize_kernel<float>(QuantArgs);
-template __global__ void quantize_kernel<_Float16>(QuantArgs);
-template __global__ void quantize_kernel<uint16_t>(QuantArgs);
 
 // fp16 cache rows (the mixed-format caches): x -> binary16, round to nearest
 // even (overflow to infinity), one thread per 8 consecutive values.  Source
@@ -195,19 +226,27 @@ hipError_t launch_store_f16(const StoreF16Args &a, int dtype, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const QuantArgs &args, int dtype, int tensors, hipStream_t stream) {
+template <int FMT>
+static void launch_quantize_fmt(const QuantArgs &a, int dtype, unsigned grid, hipStream_t stream) {
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL((quantize_kernel<float, FMT>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((quantize_kernel<_Float16, FMT>), dim3(grid), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((quantize_kernel<uint16_t, FMT>), dim3(grid), dim3(256), 0, stream, a); break;
+  }
+}
+
+hipError_t launch_quantize(const QuantArgs &args, int dtype, int tensors, hipStream_t stream,
+                           int format) {
   if (tensors < 1 || tensors > 2 || (args.flat && tensors != 1)) return hipErrorInvalidValue;
+  if (format != kFmtTbq4 && format != kFmtTbq3) return hipErrorInvalidValue;
   QuantArgs a = args;
   a.n_tensors = tensors;
   const int64_t blocks = a.blocks_per_tensor * tensors;
   const int64_t grid = (blocks + 3) / 4;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  switch (dtype) {
-    case 0: hipLaunchKernelGGL(quantize_kernel<float>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    case 1: hipLaunchKernelGGL(quantize_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-  }
+  if (format == kFmtTbq3) launch_quantize_fmt<kFmtTbq3>(a, dtype, (unsigned)grid, stream);
+  else launch_quantize_fmt<kFmtTbq4>(a, dtype, (unsigned)grid, stream);
   return hipGetLastError();
 }
 

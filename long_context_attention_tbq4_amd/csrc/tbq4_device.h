@@ -91,6 +91,60 @@ __device__ __forceinline__ uint32_t nib4_to_i8(uint32_t t) {
 }
 
 // ---------------------------------------------------------------------------
+// TBQ3 codes: 3-bit sign-magnitude (bit 2 = sign), magnitudes 0.25 0.75 1.375
+// 2.25.  A 3-bit code is exactly a byte selector of v_perm over 8 table
+// bytes, so the 8 signed values are one table:
+//   e4m3 of +0.25 +0.75 +1.375 +2.25 | -0.25 -0.75 -1.375 -2.25
+//          28    34    3B     41    | A8    B4    BB     C1
+// ---------------------------------------------------------------------------
+constexpr uint32_t kE4T3Lo = 0x413B3428u, kE4T3Hi = 0xC1BBB4A8u;
+
+// Four 3-bit codes (bits 0..11 of y) -> one code in bits 0-2 of each byte:
+// codes 0,1 stay in bits 0-5, codes 2,3 move to bits 16-21, then a copy
+// shifted by 5 puts codes 1 and 3 at bits 8 and 24 (the other copies land
+// in bits the mask clears).
+__device__ __forceinline__ uint32_t spread3(uint32_t y) {
+  const uint32_t z = (y & 0x3Fu) | (((y >> 6) & 0x3Fu) << 16);
+  return (z | (z << 5)) & 0x07070707u;
+}
+
+// Eight 3-bit codes (bits 0..23 of x) -> eight e4m3 bytes in code order.
+__device__ __forceinline__ void tbq3_chunk_to_e4m3(uint32_t x, uint32_t &e03, uint32_t &e47) {
+  e03 = perm(kE4T3Hi, kE4T3Lo, spread3(x));
+  e47 = perm(kE4T3Hi, kE4T3Lo, spread3(x >> 12));
+}
+
+// Eight 3-bit codes -> an fp16 MFMA operand, codes in natural order.
+__device__ __forceinline__ half8 tbq3_chunk_to_half8(uint32_t x) {
+  uint32_t e03, e47;
+  tbq3_chunk_to_e4m3(x, e03, e47);
+  const fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e03, 1.0f, false);
+  const fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e03, 1.0f, true);
+  const fp16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e47, 1.0f, false);
+  const fp16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e47, 1.0f, true);
+  u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+             __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(half8, v);
+}
+
+// Eight e4m3 bytes (two words) -> an fp16 MFMA operand in byte order.
+__device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
+  const fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const fp16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const fp16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+             __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(half8, v);
+}
+
+// 24-bit chunk c (0..3) of a lane's 96 code bits held in three words.
+__device__ __forceinline__ uint32_t tbq3_chunk(uint32_t w0, uint32_t w1, uint32_t w2, int c) {
+  return c == 0 ? w0 : c == 1 ? __builtin_amdgcn_alignbit(w1, w0, 24)
+                     : c == 2 ? __builtin_amdgcn_alignbit(w2, w1, 16) : (w2 >> 8);
+}
+
+// ---------------------------------------------------------------------------
 // Buffer resources: loads through a V# are range checked by the hardware --
 // bytes past num_records read as zero -- so a wave may over-fetch a few bytes
 // at the end of a row without touching memory outside it.

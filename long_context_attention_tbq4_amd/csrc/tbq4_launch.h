@@ -34,7 +34,7 @@ struct DecodeArgs {
   int32_t n_kv_heads, n_q_heads, group, capacity;
   int32_t n_ctx;         // context length, or the upper bound of ctx_lens
   int32_t n_splits;
-  int32_t k_fmt, v_fmt;  // cache formats: 0 TBQ4 blocks, 1 fp16 rows
+  int32_t k_fmt, v_fmt;  // cache formats (kFmtTbq4, kFmtF16, kFmtTbq3)
   int32_t rotate_out;    // merge applies R^T (the V cache holds rotated values)
   float qscale;          // softmax_scale * log2(e)
   uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
@@ -62,7 +62,13 @@ struct PrefillArgs {
 
 constexpr int kDecodeTile = 32;
 
-hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream);
+// Cache formats of a K or V tensor: TBQ4 blocks (66 B per head vector), fp16
+// rows (256 B, not rotated), TBQ3 blocks (50 B).
+constexpr int kFmtTbq4 = 0, kFmtF16 = 1, kFmtTbq3 = 2;
+constexpr uint32_t kBlockBytes3 = 50;
+
+hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream,
+                           int format = kFmtTbq4);
 hipError_t launch_store_f16(const StoreF16Args &a, int dtype, hipStream_t stream);
 // With start/stop events the dispatch itself records them (hipExtLaunchKernel).
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,

@@ -1,13 +1,15 @@
-"""Mixed K/V cache formats (TBQ4 or fp16 per tensor) against the fp64 oracle.
+"""Mixed K/V cache formats (TBQ4, TBQ3 or fp16 per tensor) against the fp64 oracle.
 
 Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
-section "Konfiguracja": the K and the V cache types are chosen separately.
-Each tensor is stored either as TBQ4 blocks (rotated) or as binary16 rows (not
-rotated); attention is the plain definition on the dequantised tensors.  Bar:
-stored bytes identical to the oracle's (TBQ4 blocks, binary16 rows); outputs
-within max-abs 2e-3 (+ half an fp16 ulp for fp16 output) and relative L2 1e-3.
+section "Konfiguracja": the K and the V cache types are chosen separately;
+section "6. Ten sam cache na Apple silicon" adds a TBQ3 cache.  Each tensor is
+stored as TBQ4 or TBQ3 blocks (rotated) or as binary16 rows (not rotated);
+attention is the plain definition on the dequantised tensors.  Bar: stored
+bytes identical to the oracle's; outputs within max-abs 2e-3 (+ half an fp16
+ulp for fp16 output) and relative L2 1e-3.
 """
 
+import itertools
 import math
 
 import numpy as np
@@ -20,8 +22,8 @@ from _util import check_attn
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = [(tb.FMT_TBQ4, tb.FMT_F16), (tb.FMT_F16, tb.FMT_TBQ4), (tb.FMT_F16, tb.FMT_F16),
-           (tb.FMT_TBQ4, tb.FMT_TBQ4)]
+ALL = list(itertools.product([tb.FMT_TBQ4, tb.FMT_F16, tb.FMT_TBQ3], repeat=2))
+MIXED = [f for f in ALL if f != (tb.FMT_TBQ4, tb.FMT_TBQ4)]
 
 
 def _oracle_tensor(x, fmt, seed):
@@ -31,6 +33,9 @@ def _oracle_tensor(x, fmt, seed):
     if fmt == tb.FMT_TBQ4:
         packed = o.quantize_blocks(xh, seed)[0]
         return packed, o.dequantize_blocks(packed, seed)
+    if fmt == tb.FMT_TBQ3:
+        packed = o.quantize_blocks3(xh, seed)[0]
+        return packed, o.dequantize_blocks3(packed, seed)
     rows = o.f16_rows(xh)
     return rows.view(np.uint8), o.dequantize_f16(rows)
 
@@ -64,14 +69,14 @@ def _case(kf, vf, B, H, G, T, cap, scale, P, seed=0, rng_seed=0, kscale=1.0, jun
     return out, ref
 
 
-@pytest.mark.parametrize("kf,vf", FORMATS)
+@pytest.mark.parametrize("kf,vf", ALL)
 @pytest.mark.parametrize("P", [0, 3])
 def test_formats(kf, vf, P):
-    out, ref = _case(kf, vf, 2, 2, 8, 700, 712, 1 / math.sqrt(128), P, seed=3, rng_seed=kf + 2 * vf)
+    out, ref = _case(kf, vf, 2, 2, 8, 700, 712, 1 / math.sqrt(128), P, seed=3, rng_seed=kf + 3 * vf)
     check_attn(out, ref, False, f"k{kf} v{vf} P={P}")
 
 
-@pytest.mark.parametrize("kf,vf", FORMATS[:3])
+@pytest.mark.parametrize("kf,vf", MIXED)
 def test_group_sizes_fp16_output_and_seed(kf, vf):
     for G in (1, 4):
         out, ref = _case(kf, vf, 1, 3, G, 1000, 1008, 0.1, 5, seed=11, rng_seed=G,
@@ -79,13 +84,13 @@ def test_group_sizes_fp16_output_and_seed(kf, vf):
         check_attn(out, ref, True, f"k{kf} v{vf} G={G}")
 
 
-@pytest.mark.parametrize("kf,vf", FORMATS[:3])
+@pytest.mark.parametrize("kf,vf", MIXED)
 def test_peaky_scores(kf, vf):
     out, ref = _case(kf, vf, 1, 1, 8, 2048, 2048, 1 / math.sqrt(128), 8, kscale=30.0, rng_seed=5)
     check_attn(out, ref, False, f"peaky k{kf} v{vf}")
 
 
-@pytest.mark.parametrize("kf,vf", FORMATS[:3])
+@pytest.mark.parametrize("kf,vf", MIXED)
 @pytest.mark.parametrize("T", [33, 1023])
 def test_unused_slots_with_nan_do_not_leak(kf, vf, T):
     out, ref = _case(kf, vf, 1, 2, 8, T, 1056, 0.1, 2, rng_seed=T, junk=True)
@@ -106,7 +111,7 @@ def test_tbq4_formats_match_the_tbq4_cache():
                        tb.mixed_attn_decode(m, q, 500, 0.1, n_splits=4))
 
 
-@pytest.mark.parametrize("kf,vf", FORMATS)
+@pytest.mark.parametrize("kf,vf", ALL)
 @pytest.mark.parametrize("B,H,n_new", [(1, 1, 1), (1, 3, 1), (1, 2, 17)])
 def test_append_block_counts_not_multiple_of_four(kf, vf, B, H, n_new):
     """Appends whose block count is not a multiple of the 4 wavefronts of a
