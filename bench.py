@@ -1,7 +1,7 @@
 """Benchmark of the TBQ4 attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--splits P]
-                    [--no-prefill] [--no-cpu-baseline]
+                    [--no-prefill] [--no-cpu-baseline] [--no-formats]
 
 One step = one pass of the whole decode hot path over the decode128k workload
 (batch 4 independent sequences, 8 KV / 64 query heads, head_dim 128, 131072
@@ -13,6 +13,8 @@ rows) divided by the step time, in GB/s.  The prefill-chunk workload (2048
 queries on 131072 cached tokens, 8 KV / 64 query heads, append of the chunk's
 K/V then causal attention) is timed in the same run and reported under
 "prefill" in TFLOP/s (4 * 128 * 64 FLOPs per unmasked (query, key) pair).
+The same decode rows stored as TBQ3 or fp16 K / V tensors (mixed formats) are
+timed under "formats" (one decode call per format pair, KV GB/s).
 
 The dominant kernel's roofline entry uses HIP events on the stream the kernels
 run on, recorded by the dispatch of every decode-partial launch of the timed
@@ -41,7 +43,7 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "fb8496f036c69637ce91c18a4d214831f79089d85206ef3e028fe6401a8299f7",
+TRAFFIC = {"sources_sha256": "cf918d0cd7d9efea2d4980fdb5e701b6bc639926e0acb8ea69f14b540b248418",
            "n_splits": 64, "fetch_kib": 271205.1, "fetch_factor": 2.0,
            "write_kib": 8704.0, "write_factor": 1.0}
 
@@ -70,6 +72,8 @@ def parse():
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-formats", dest="formats", action="store_false",
+                   help="skip the decode timings of the TBQ3 / fp16 cache formats")
     p.add_argument("--prefill-steps", type=int, default=0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB five times "
@@ -119,7 +123,9 @@ class HipEvents:
         self.ev = []
 
 
-def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768):
+def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768, mixed=()):
+    """Append tokens t0 .. t1 of the workload to the TBQ4 cache and to every
+    cache in `mixed` (MixedKVCache) from the same generated K/V rows."""
     from workloads import K, V, kv_tensor
     for a in range(t0, t1, chunk):
         log(f"{w.name}: filling tokens {a}..{min(t1, a + chunk)}")
@@ -127,6 +133,8 @@ def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768):
         k = torch.from_numpy(kv_tensor(w, 0, K, a, b)).cuda()
         v = torch.from_numpy(kv_tensor(w, 0, V, a, b)).cuda()
         tb.quantize_append(cache, k, v, a)
+        for m in mixed:
+            tb.mixed_append(m, k, v, a)
         del k, v
     torch.cuda.synchronize()
 
@@ -136,7 +144,8 @@ def bench_decode(tb, torch, args):
     w = WORKLOADS["decode128k"]
     B, Hkv, Hq, T = w.batch, w.n_kv_heads, w.n_q_heads, w.n_ctx
     cache = tb.KVCache(B, Hkv, T)
-    fill_cache(tb, torch, cache, w, 0, T - 1)
+    mixed = [tb.MixedKVCache(B, Hkv, T, kf, vf) for kf, vf in FORMATS] if args.formats else []
+    fill_cache(tb, torch, cache, w, 0, T, mixed=mixed)
     rng = np.random.default_rng([0, 99])
     k_new = torch.from_numpy(rng.standard_t(5, size=(B, 1, Hkv, 128)).astype(np.float32)).cuda()
     v_new = torch.from_numpy(rng.standard_t(5, size=(B, 1, Hkv, 128)).astype(np.float32)).cuda()
@@ -165,6 +174,8 @@ def bench_decode(tb, torch, args):
     hip.destroy()
     graph = bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w)
     verify = bench_verify(tb, torch, args, cache, w)
+    formats = [bench_format(tb, torch, args, m, q, out, ws, P, w) for m in mixed]
+    del mixed
     kv_bytes = B * T * Hkv * 2 * 66
     q_bytes = B * Hq * 128 * 4
     out_bytes = B * Hq * 128 * 2
@@ -182,7 +193,41 @@ def bench_decode(tb, torch, args):
         "tokens_per_s": B * T / (ms * 1e-3),
         "graph": graph,
         "verify": verify,
+        "formats": formats,
     }
+
+
+# (K format, V format) pairs timed beside the TBQ4 cache on the same rows
+FORMAT_NAMES = {0: "tbq4", 1: "f16", 2: "tbq3"}
+FORMATS = ((2, 2), (0, 2), (0, 1), (1, 0), (1, 1))
+
+
+def bench_format(tb, torch, args, cache, q, out, ws, P, w):
+    """Decode (split kernel + merge) over a cache whose K and V tensors are
+    stored in the given formats; calls back to back between two events."""
+    B, T = cache.batch, cache.capacity
+
+    def call():
+        tb.mixed_attn_decode(cache, q, T, w.softmax_scale, n_splits=P, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out.float()).all()
+    kv = cache.k.numel() + cache.v.numel()
+    name = f"K {FORMAT_NAMES[cache.k_format]} / V {FORMAT_NAMES[cache.v_format]}"
+    log(f"decode {name}: {ms:.4f} ms/call, {kv / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return {"formats": name, "kv_bytes": kv, "ms_per_call": round(ms, 5),
+            "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_tokens_per_s": round(B * T / (ms * 1e-3), 1)}
 
 
 def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
@@ -381,6 +426,12 @@ def main():
             "kv_gbs": round(dec["verify"]["kv_gbs"], 1),
             "query_tokens_per_s": round(dec["verify"]["query_tokens_per_s"], 1),
             "vs_4_decodes": round(4 * dec["ms"] / dec["verify"]["ms_per_call"], 3),
+        },
+        "formats": {
+            "workload": "decode128k rows stored per tensor as TBQ4 (66 B), TBQ3 (50 B) or "
+                        "fp16 (256 B) per head vector; one decode call (split kernel + merge) "
+                        "over 131072 slots, calls back to back",
+            "results": dec["formats"],
         },
         "graph_step": {
             "ms_per_step": round(dec["graph"]["ms_per_step"], 5),
