@@ -10,10 +10,11 @@
 // rows (4 wavefronts x 32 rows); blockIdx.x % n_kv_heads is the KV head, so
 // on an 8-XCD part each XCD streams the cache of its own head.  Per 64-key
 // tile the workgroup
-//   * fetches the next tile's packed K and V rows (coalesced 16-byte-per-lane
-//     loads) before it computes on the current one, and dequantises them into
-//     the other half of a double-buffered LDS tile: fp16 codebook values, one
-//     fp32 scale per key and tensor,
+//   * fetches the next tile's packed K and V rows before it computes on the
+//     current one (wavefront w loads quarter w of every key's index bytes;
+//     together the four cover the tile's contiguous bytes) and dequantises
+//     them into the other half of a double-buffered LDS tile: fp16 codebook
+//     values, one fp32 scale per key and tensor,
 //   * S^T = K Q'^T on v_mfma_f32_32x32x16_f16, with q' split into an fp16
 //     high part and the fp16 residual that both accumulate into the same
 //     fp32 scores (~22 bits of q'), then scales by d^K per key,
@@ -32,12 +33,23 @@
 namespace tbq4 {
 
 constexpr int kKT = 64;             // keys per tile
-constexpr int kRowB = 272;          // LDS bytes per fp16 row (256 + pad)
-constexpr int kTileB = kKT * kRowB; // bytes of one K (or V) tile
+// LDS row pitches.  K rows are read one row per lane (16 bytes): a 272-byte
+// pitch (68 dwords) puts 8 consecutive rows on distinct banks.  V rows are
+// read transposed, 4 consecutive rows x 32 bytes per 16 lanes: a 288-byte
+// pitch (72 dwords) puts those on distinct banks, and the 16-byte chunks of
+// rows with bit 2 set are swapped in pairs so that the stores of 8
+// consecutive rows (one key per lane) do not collide either.
+constexpr int kRowB = 272;
+constexpr int kVRowB = 288;
+constexpr int kTileB = kKT * kRowB;
+constexpr int kVTileB = kKT * kVRowB;
+
+// byte offset within V row r of the 16-byte chunk holding byte `byte`
+__device__ __forceinline__ int v_swizzle(int r, int byte) { return byte ^ (((r >> 2) & 1) << 4); }
 
 struct __attribute__((aligned(16))) PrefillLds {
   uint8_t k[2][kTileB];
-  uint8_t v[2][kTileB];
+  uint8_t v[2][kVTileB];
   float sk[2][kKT];
   float sv[2][kKT];
 };
@@ -151,9 +163,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const rsrc_t rk = make_rsrc(a.k + rowoff, row_bytes);
   const rsrc_t rv = make_rsrc(a.v + rowoff, row_bytes);
 
-  // fetch mapping: thread -> (key, quarter); start offsets are even, so the
-  // realignment shift is 0 or 2 (a per-thread constant)
-  const int fkey = tid >> 2, fq = tid & 3;
+  // fetch mapping: thread -> (key, quarter), wavefront w fetching quarter w
+  // of the tile's 64 keys; start offsets are even, so the realignment shift
+  // is 0 or 2 (a per-thread constant)
+  const int fkey = tid & 63, fq = tid >> 6;
   const uint32_t foff = (uint32_t)fkey * kBlockBytes + 2 + 16 * fq;
   const uint32_t fshift = foff & 3u;
   auto fetch = [&](TileRaw &r, int t) {
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const uint32_t vw[4] = {alignbyte(r.v4[1], r.v4[0], fshift), alignbyte(r.v4[2], r.v4[1], fshift),
                             alignbyte(r.v4[3], r.v4[2], fshift), alignbyte(r.v1, r.v4[3], fshift)};
     uint8_t *kr = L.k[buf] + fkey * kRowB + 64 * fq;
-    uint8_t *vr = L.v[buf] + fkey * kRowB + 64 * fq;
+    uint8_t *vr = L.v[buf] + fkey * kVRowB;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t r0, r1, r2, r3;
@@ -189,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       *(u32x4 *)(kr + 16 * c) = u32x4{r0, r1, r2, r3};
       nib4_to_f16(vw[c], r0, r1);
       nib4_to_f16(vw[c] >> 4, r2, r3);
-      *(u32x4 *)(vr + 16 * c) = u32x4{r0, r1, r2, r3};
+      *(u32x4 *)(vr + v_swizzle(fkey, 64 * fq + 16 * c)) = u32x4{r0, r1, r2, r3};
     }
     if (fq == 0) {
       L.sk[buf][fkey] = half_bits_to_float(r.sk);
@@ -207,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // transposed V reads: lane s of a 16-lane group points at key 4*half + s/4
   // (+ 8 for the second read) and position 16*((lane>>4)&1) + 4*(s&3)
   const int s16 = lane & 15;
-  const int tr_base = (4 * half + (s16 >> 2)) * kRowB + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+  const int tr_row = 4 * half + (s16 >> 2);
+  const int tr_col = 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
 
   {
     TileRaw r0;
@@ -286,12 +300,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       // ---- O'^T[dim][row] += V^T P~^T
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint8_t *vbase = vb + (kb0 + 16 * ks) * kRowB + tr_base;
+        const int r0 = kb0 + 16 * ks + tr_row;     // (rows r0 and r0 + 8 share bit 2)
+        const uint8_t *vbase = vb + r0 * kVRowB;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           typedef __attribute__((address_space(3))) short4v lds_s4;
-          const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 64 * db));
-          const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kRowB + 64 * db));
+          const int col = v_swizzle(r0, tr_col + 64 * db);
+          const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
+          const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
           const short8v vs = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, vs), pb[ks], o[db],
                                                          0, 0, 0);
