@@ -328,6 +328,60 @@ def dequantize_f16(rows):
 
 
 # --------------------------------------------------------------------------
+# q8_0 cache rows (mixed K/V cache formats).  The pages name q8_0 as a KV cache
+# type (the tgstat.ru channel @tech_di page: its server configuration sets
+# both the K and the V cache to q8_0; the DFlash speed-test page weighs a
+# quantised cache against fp16) but never define it.  Read here as the common
+# 8-bit block format: each head vector is four blocks of 32 values; a block
+# is its binary16 scale d (little endian) followed by 32 int8 codes, 34 bytes,
+# 136 bytes per head vector, not rotated.  Decisions are made in IEEE fp32,
+# the precision of the kernel:
+#   amax = max |x_i| (exact),  d32 = amax / 127 (fp32, nearest even),
+#   q_i  = x_i / d32 (fp32, nearest even) rounded to the nearest integer,
+#          halves away from zero; q_i = 0 when d32 = 0,
+#   d    = the binary16 nearest d32 (ties to even).
+# A code's value is d * q_i.  (Inputs are finite.)
+# --------------------------------------------------------------------------
+Q8_BLOCK = 32
+Q8_BLOCK_BYTES = 34
+Q8_ROW_BYTES = 136
+
+
+def q8_0_rows(x):
+    """Head vectors (..., 128) -> q8_0 rows uint8 (..., 136)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    xb = x32.reshape(x32.shape[:-1] + (HEAD_DIM // Q8_BLOCK, Q8_BLOCK))
+    amax = np.max(np.abs(xb), axis=-1)
+    d32 = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = (xb / d32[..., None]).astype(np.float32)
+    av = np.floor(np.abs(v.astype(np.float64)) + 0.5)
+    q = np.where(d32[..., None] > 0, np.where(v < 0, -av, av), 0.0).astype(np.int8)
+    rows = np.empty(x32.shape[:-1] + (HEAD_DIM // Q8_BLOCK, Q8_BLOCK_BYTES), dtype=np.uint8)
+    d_bits = d32.astype(np.float16).view(np.uint16)
+    rows[..., 0] = (d_bits & 0xFF).astype(np.uint8)
+    rows[..., 1] = (d_bits >> 8).astype(np.uint8)
+    rows[..., 2:] = q.view(np.uint8)
+    return rows.reshape(x32.shape[:-1] + (Q8_ROW_BYTES,))
+
+
+def unpack_q8_0(rows):
+    """q8_0 rows (..., 136) -> (codes int8 (..., 4, 32), d fp64 (..., 4))."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    if rows.shape[-1] != Q8_ROW_BYTES:
+        raise ValueError("last axis must be 136 bytes")
+    b = rows.reshape(rows.shape[:-1] + (HEAD_DIM // Q8_BLOCK, Q8_BLOCK_BYTES))
+    d_bits = b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8)
+    return b[..., 2:].view(np.int8), half_bits_to_float(d_bits)
+
+
+def dequantize_q8_0(rows):
+    q, d = unpack_q8_0(rows)
+    x = d[..., None] * q.astype(np.float64)
+    return x.reshape(x.shape[:-2] + (HEAD_DIM,))
+
+
+# --------------------------------------------------------------------------
 # Attention on the dequantised cache (plain softmax attention, fp64)
 # --------------------------------------------------------------------------
 def _softmax_rows(s):
