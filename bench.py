@@ -13,8 +13,8 @@ rows) divided by the step time, in GB/s.  The prefill-chunk workload (2048
 queries on 131072 cached tokens, 8 KV / 64 query heads, append of the chunk's
 K/V then causal attention) is timed in the same run and reported under
 "prefill" in TFLOP/s (4 * 128 * 64 FLOPs per unmasked (query, key) pair).
-The same decode rows stored as TBQ3 or fp16 K / V tensors (mixed formats) are
-timed under "formats" (one decode call per format pair, KV GB/s).
+The same decode rows stored as TBQ3, q8_0 or fp16 K / V tensors (mixed
+formats) are timed under "formats" (one decode call per format pair, KV GB/s).
 
 The dominant kernel's roofline entry uses HIP events on the stream the kernels
 run on, recorded by the dispatch of every decode-partial launch of the timed
@@ -198,8 +198,8 @@ def bench_decode(tb, torch, args):
 
 
 # (K format, V format) pairs timed beside the TBQ4 cache on the same rows
-FORMAT_NAMES = {0: "tbq4", 1: "f16", 2: "tbq3"}
-FORMATS = ((2, 2), (0, 2), (0, 1), (1, 0), (1, 1))
+FORMAT_NAMES = {0: "tbq4", 1: "f16", 2: "tbq3", 3: "q8_0"}
+FORMATS = ((2, 2), (0, 2), (0, 1), (1, 0), (0, 3), (3, 0), (3, 3), (1, 1))
 
 
 def bench_format(tb, torch, args, cache, q, out, ws, P, w):
@@ -428,9 +428,9 @@ def main():
             "vs_4_decodes": round(4 * dec["ms"] / dec["verify"]["ms_per_call"], 3),
         },
         "formats": {
-            "workload": "decode128k rows stored per tensor as TBQ4 (66 B), TBQ3 (50 B) or "
-                        "fp16 (256 B) per head vector; one decode call (split kernel + merge) "
-                        "over 131072 slots, calls back to back",
+            "workload": "decode128k rows stored per tensor as TBQ4 (66 B), TBQ3 (50 B), "
+                        "q8_0 (136 B) or fp16 (256 B) per head vector; one decode call (split "
+                        "kernel + merge) over 131072 slots, calls back to back",
             "results": dec["formats"],
         },
         "graph_step": {

@@ -207,15 +207,24 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
  *                  = magnitude index | 4 if negative; code i sits at bits
  *                  3i .. 3i+2 of the little-endian integer held in bytes
  *                  2 .. 49.  3.125 bits per value.
+ *   TBQ4_FMT_Q8_0  136-byte rows, not rotated: four blocks of 32 values,
+ *                  each the binary16 scale d (little endian) then 32 int8
+ *                  codes (34 bytes).  The pages name q8_0 as a KV cache type
+ *                  (the tgstat.ru channel @tech_di page's server
+ *                  configuration sets both tensors to it) without defining
+ *                  it; read as: d32 = max|x| / 127 and q = x / d32 in IEEE
+ *                  fp32, q rounded to the nearest integer with halves away
+ *                  from zero, d = the binary16 nearest d32.  8.5 bits per
+ *                  value.  Inputs must be finite.
  * tbq4_mixed_cache: k, v point at [batch][n_kv_heads][capacity][row bytes of
  * their format] (tbq4_format_row_bytes), 16-byte aligned; the rest as in
  * the TBQ4-only descriptor, capacity a multiple of 8.
  * tbq4_mixed_append: as tbq4_quantize_append, each tensor in its format.
  * tbq4_mixed_attn_decode: as tbq4_attn_decode (same workspace size, G <= 8):
  *   q is rotated only when K is stored rotated (TBQ4 or TBQ3), and the
- *   output is rotated back only when V is.  Any combination of the three
+ *   output is rotated back only when V is.  Any combination of the four
  *   formats is accepted. */
-typedef enum { TBQ4_FMT_TBQ4 = 0, TBQ4_FMT_F16 = 1, TBQ4_FMT_TBQ3 = 2 } tbq4_format;
+typedef enum { TBQ4_FMT_TBQ4 = 0, TBQ4_FMT_F16 = 1, TBQ4_FMT_TBQ3 = 2, TBQ4_FMT_Q8_0 = 3 } tbq4_format;
 typedef struct {
   uint8_t *k;
   uint8_t *v;

@@ -23,7 +23,7 @@ __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
     "attn_decode_partial", "attn_decode_merge", "quantize_append_at", "attn_decode_varlen",
     "attn_verify", "verify_workspace_bytes", "MixedKVCache", "mixed_append",
-    "mixed_attn_decode", "FMT_TBQ4", "FMT_F16", "FMT_TBQ3",
+    "mixed_attn_decode", "FMT_TBQ4", "FMT_F16", "FMT_TBQ3", "FMT_Q8_0",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
     "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
 ]
@@ -88,15 +88,16 @@ class KVCache:
                           HEAD_DIM, self.capacity, self.sign_seed)
 
 
-FMT_TBQ4, FMT_F16, FMT_TBQ3 = 0, 1, 2
-_ROW_BYTES = {FMT_TBQ4: BLOCK_BYTES, FMT_F16: 2 * HEAD_DIM, FMT_TBQ3: 50}
+FMT_TBQ4, FMT_F16, FMT_TBQ3, FMT_Q8_0 = 0, 1, 2, 3
+_ROW_BYTES = {FMT_TBQ4: BLOCK_BYTES, FMT_F16: 2 * HEAD_DIM, FMT_TBQ3: 50, FMT_Q8_0: 136}
 
 
 class MixedKVCache:
     """One layer's K and V caches, each in its own format: FMT_TBQ4 (uint8
     [batch][n_kv_heads][capacity][66]), FMT_TBQ3 (uint8 [...][50]: binary16
-    scale + 128 3-bit codes) or FMT_F16 (uint8 view of fp16
-    [batch][n_kv_heads][capacity][128], not rotated)."""
+    scale + 128 3-bit codes), FMT_Q8_0 (uint8 [...][136]: four blocks of a
+    binary16 scale + 32 int8 codes, not rotated) or FMT_F16 (uint8 view of
+    fp16 [batch][n_kv_heads][capacity][128], not rotated)."""
 
     def __init__(self, batch, n_kv_heads, capacity, k_format, v_format, sign_seed=0,
                  device="cuda"):

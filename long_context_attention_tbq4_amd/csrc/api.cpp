@@ -257,7 +257,7 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
 }
 
 static_assert(TBQ4_FMT_TBQ4 == tbq4::kFmtTbq4 && TBQ4_FMT_F16 == tbq4::kFmtF16 &&
-                  TBQ4_FMT_TBQ3 == tbq4::kFmtTbq3,
+                  TBQ4_FMT_TBQ3 == tbq4::kFmtTbq3 && TBQ4_FMT_Q8_0 == tbq4::kFmtQ8,
               "format codes of the ABI and the kernels agree");
 
 size_t tbq4_format_row_bytes(int32_t format) {
@@ -265,6 +265,7 @@ size_t tbq4_format_row_bytes(int32_t format) {
     case TBQ4_FMT_TBQ4: return TBQ4_BLOCK_BYTES;
     case TBQ4_FMT_F16: return 2 * TBQ4_HEAD_DIM;
     case TBQ4_FMT_TBQ3: return tbq4::kBlockBytes3;
+    case TBQ4_FMT_Q8_0: return tbq4::kQ8RowBytes;
     default: return 0;
   }
 }
@@ -306,7 +307,7 @@ tbq4_status tbq4_mixed_append(const tbq4_mixed_cache *cache, const void *k_new, 
   sign_words(cache->sign_seed, w);
   for (int t = 0; t < 2; ++t) {
     hipError_t e;
-    if (fmt[t] != TBQ4_FMT_F16) {
+    if (fmt[t] == TBQ4_FMT_TBQ4 || fmt[t] == TBQ4_FMT_TBQ3) {
       tbq4::QuantArgs a;
       memset(&a, 0, sizeof(a));
       a.src[0] = src[t];
@@ -319,7 +320,7 @@ tbq4_status tbq4_mixed_append(const tbq4_mixed_cache *cache, const void *k_new, 
       a.sign_lo = w[0]; a.sign_hi = w[1]; a.sign_lo2 = w[2]; a.sign_hi2 = w[3];
       e = tbq4::launch_quantize(a, (int)src_dtype, 1, (hipStream_t)hip_stream,
                                 fmt[t] == TBQ4_FMT_TBQ3 ? tbq4::kFmtTbq3 : tbq4::kFmtTbq4);
-    } else {
+    } else if (fmt[t] == TBQ4_FMT_F16) {
       tbq4::StoreF16Args a;
       a.src = src[t];
       a.dst = (_Float16 *)dst[t];
@@ -329,6 +330,16 @@ tbq4_status tbq4_mixed_append(const tbq4_mixed_cache *cache, const void *k_new, 
       a.capacity = cache->capacity;
       a.pos = pos;
       e = tbq4::launch_store_f16(a, (int)src_dtype, (hipStream_t)hip_stream);
+    } else {
+      tbq4::StoreQ8Args a;
+      a.src = src[t];
+      a.dst = dst[t];
+      a.n_blocks = (int64_t)cache->batch * n_new * cache->n_kv_heads * (TBQ4_HEAD_DIM / 32);
+      a.n_new = n_new;
+      a.n_kv_heads = cache->n_kv_heads;
+      a.capacity = cache->capacity;
+      a.pos = pos;
+      e = tbq4::launch_store_q8(a, (int)src_dtype, (hipStream_t)hip_stream);
     }
     s = from_hip(e);
     if (s != TBQ4_OK) return s;
@@ -354,7 +365,7 @@ tbq4_status tbq4_mixed_attn_decode(const tbq4_mixed_cache *cache, const void *q,
   a.out = out;
   a.k_fmt = cache->k_format;
   a.v_fmt = cache->v_format;
-  a.rotate_out = cache->v_format != TBQ4_FMT_F16 ? 1 : 0;
+  a.rotate_out = cache->v_format == TBQ4_FMT_TBQ4 || cache->v_format == TBQ4_FMT_TBQ3 ? 1 : 0;
   hipStream_t st = (hipStream_t)hip_stream;
   s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
   if (s != TBQ4_OK) return s;

@@ -42,9 +42,9 @@ constexpr int kVRow = 80;           // LDS bytes per staged V row (64 + pad)
 
 
 // Cache formats of the K and V tensors (template arguments KF, VF): TBQ4
-// blocks, fp16 rows (not rotated) or TBQ3 blocks.  q is rotated when K is a
-// TBQ format; the merge applies R^T when V is.
-constexpr int kE4Row = 144;         // LDS bytes per staged TBQ3 V row: 128 e4m3 bytes + pad
+// blocks, fp16 rows (not rotated), TBQ3 blocks or q8_0 rows (not rotated).
+// q is rotated when K is a TBQ format; the merge applies R^T when V is.
+constexpr int kE4Row = 144;         // LDS bytes per staged TBQ3 (e4m3) or q8_0 (int8) V row: 128 bytes + pad
                                     // (36 dwords: the 8 rows of one byte-transposed read
                                     // fall on distinct banks)
 constexpr int kF16Row = 288;        // LDS bytes per staged fp16 V row (256 + pad; 72 dwords
@@ -53,11 +53,17 @@ constexpr int kF16Row = 288;        // LDS bytes per staged fp16 V row (256 + pa
 template <typename QT, int KF, int VF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // bytes per head vector of each tensor
-  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
-  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : VF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
-  constexpr bool kKRot = KF != kFmtF16, kVRot = VF != kFmtF16;   // stored rotated
+  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3
+                             : KF == kFmtQ8 ? kQ8RowBytes : 2 * kHeadDim;
+  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : VF == kFmtTbq3 ? kBlockBytes3
+                             : VF == kFmtQ8 ? kQ8RowBytes : 2 * kHeadDim;
+  constexpr bool kKRot = KF == kFmtTbq4 || KF == kFmtTbq3;   // stored rotated
   __shared__ __attribute__((aligned(16))) uint8_t
-      vlds[kTile * (VF == kFmtTbq4 ? kVRow : VF == kFmtTbq3 ? kE4Row : kF16Row)];
+      vlds[kTile * (VF == kFmtTbq4 ? kVRow : VF == kFmtF16 ? kF16Row : kE4Row)];
+  // q8_0: one scale per (32-dim block, token): K scales * 2^-ex, V scales
+  // followed by 32 zeros (read by the lanes of P~ rows 8-15)
+  __shared__ __attribute__((aligned(16))) float skq[KF == kFmtQ8 ? 4 * kTile : 4];
+  __shared__ __attribute__((aligned(16))) float svq[VF == kFmtQ8 ? 4 * kTile + 32 : 4];
   __shared__ __attribute__((aligned(16))) float sk[kTile];   // d^K * 2^-ex per token
   __shared__ __attribute__((aligned(16))) float sv[kTile + 32];   // d^V per token, then zeros
 
@@ -72,17 +78,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // lanes of P~ rows 8-15 read zero V scales
   const float *sv_rd = lo_part ? sv + kTile : sv;
   if (lane < 32) sv[kTile + lane] = 0.0f;
+  if constexpr (VF == kFmtQ8) {
+    if (lane < 32) svq[4 * kTile + lane] = 0.0f;
+  }
 
   // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
   // fp16 K cache), split into fp16 hi + residual
   float qv[32];
   {
-    const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim +
-                   quarter * 32;
+    // lane quarter q holds dims 32 q + i; for a q8_0 K cache dims
+    // 32 (i/8) + 8 q + i%8 instead, so that MFMA step c spans q8_0 block c
+    const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim;
     const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      float x = head < G ? load_q<QT>(qp + i) : 0.0f;
+      const int d = KF == kFmtQ8 ? 32 * (i >> 3) + 8 * quarter + (i & 7) : 32 * quarter + i;
+      float x = head < G ? load_q<QT>(qp + d) : 0.0f;
       qv[i] = ((sw >> i) & 1u) ? -x : x;
     }
     if constexpr (kKRot) {
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int el = 0; el < 8; ++el) {
       // TBQ4 K operands hold the 4 even then the 4 odd dims of a code word;
-      // fp16 and TBQ3 K operands hold 8 consecutive dims
+      // fp16, TBQ3 and q8_0 K operands hold 8 consecutive dims
       const int i = KF == kFmtTbq4 ? 8 * c + (el < 4 ? 2 * el : 2 * el - 7) : 8 * c + el;
       const float x = ldexpf(qv[i], ex);
       const _Float16 hi = (_Float16)x;
@@ -191,11 +202,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // 16-byte loads; no scale.)
   // (TBQ3: a lane's 32 codes are 12 bytes at an even offset: one 16-byte
   // load at the word-aligned offset below covers them.)
-  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : 1;
+  // (q8_0 K: a lane's 8 codes of each of the token's 4 blocks, 10 words;
+  // q8_0 V: the lane's block -- scale and 32 codes -- in 9 words; the K
+  // scales come two per lane.)
+  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : VF == kFmtQ8 ? 2 : 1;
   struct Raw {
     u32x4 k4[kBlk * kKW], v4[kBlk * kVW];
     uint32_t k1[kBlk], v1[kBlk];
+    u32x3 kq3[KF == kFmtQ8 ? 2 * kBlk : 1];
+    u32x2 kq2[KF == kFmtQ8 ? 2 * kBlk : 1];
     uint16_t sk, sv;
+    uint16_t skq[2];
   };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
   const uint32_t shift = lane_off & 3u;   // (2 col + 2) mod 4: the same for TBQ3
@@ -215,6 +232,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         r.k1[blk] = buf_load_x1(rk, a + 16);
       } else if constexpr (KF == kFmtTbq3) {
         r.k4[blk] = buf_load_x4(rk, code_addr(live, t, blk, kBlockBytes3, 12u));
+      } else if constexpr (KF == kFmtQ8) {
+        // codes 8 q .. 8 q + 7 of block c start at byte 34 c + 2 + 8 q of
+        // the token (token rows are 8-byte aligned): 2 bytes into a word for
+        // even c, word-aligned for odd c
+        const uint32_t tb =
+            live ? (uint32_t)(t * kTile + 16 * blk + col) * kQ8RowBytes + 8u * quarter : 0xFFFF0000u;
+        r.kq3[2 * blk] = buf_load_x3(rk, tb);
+        r.kq2[2 * blk] = buf_load_x2(rk, tb + 36);
+        r.kq3[2 * blk + 1] = buf_load_x3(rk, tb + 68);
+        r.kq2[2 * blk + 1] = buf_load_x2(rk, tb + 104);
       } else {
         const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kKBytes + 64u * quarter)
                                 : 0xFFFF0000u;
@@ -226,6 +253,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         r.v1[blk] = buf_load_x1(rv, a + 16);
       } else if constexpr (VF == kFmtTbq3) {
         r.v4[blk] = buf_load_x4(rv, code_addr(live, t, blk, kBlockBytes3, 12u));
+      } else if constexpr (VF == kFmtQ8) {
+        const uint32_t vb =
+            live ? ((uint32_t)(t * kTile + 16 * blk + col) * kQ8RowBytes + 34u * quarter) & ~3u
+                 : 0xFFFF0000u;
+        r.v4[2 * blk] = buf_load_x4(rv, vb);
+        r.v4[2 * blk + 1] = buf_load_x4(rv, vb + 16);
+        r.v1[blk] = buf_load_x1(rv, vb + 32);
       } else {
         const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kVBytes + 64u * quarter)
                                 : 0xFFFF0000u;
@@ -239,6 +273,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if constexpr (KF == kFmtTbq3) r.sk = buf_load_u16(rk, soff3);
     if constexpr (VF == kFmtTbq4) r.sv = buf_load_u16(rv, soff);
     if constexpr (VF == kFmtTbq3) r.sv = buf_load_u16(rv, soff3);
+    if constexpr (KF == kFmtQ8) {   // lane: token lane % 32, blocks 2 (lane / 32) + 0, 1
+      const uint32_t so = live ? (uint32_t)(t * kTile + (lane & 31)) * kQ8RowBytes + 68u * (lane >> 5)
+                               : 0xFFFF0000u;
+      r.skq[0] = buf_load_u16(rk, so);
+      r.skq[1] = buf_load_u16(rk, so + 34);
+    }
   };
 
   // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
@@ -250,6 +290,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // words realigned (converted to fp16 operands at the MFMA), or fp16 rows
     uint32_t kw[kBlk][4];
     u32x4 kf[KF == kFmtF16 ? kBlk * 4 : 1];
+    uint32_t kq[KF == kFmtQ8 ? kBlk : 1][8];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       if constexpr (KF == kFmtTbq4) {
@@ -263,6 +304,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         kw[blk][0] = alignbyte(w[1], w[0], shift);
         kw[blk][1] = alignbyte(w[2], w[1], shift);
         kw[blk][2] = alignbyte(w[3], w[2], shift);
+      } else if constexpr (KF == kFmtQ8) {
+        const u32x3 a0 = r.kq3[2 * blk], a2 = r.kq3[2 * blk + 1];
+        const u32x2 a1 = r.kq2[2 * blk], a3 = r.kq2[2 * blk + 1];
+        kq[blk][0] = alignbyte(a0[1], a0[0], 2u);
+        kq[blk][1] = alignbyte(a0[2], a0[1], 2u);
+        kq[blk][2] = a1[0];
+        kq[blk][3] = a1[1];
+        kq[blk][4] = alignbyte(a2[1], a2[0], 2u);
+        kq[blk][5] = alignbyte(a2[2], a2[1], 2u);
+        kq[blk][6] = a3[0];
+        kq[blk][7] = a3[1];
       } else {
         // fp16 slots >= n_ctx may hold anything: zero them (a NaN value would
         // survive the -inf mask)
@@ -275,6 +327,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       if constexpr (KF == kFmtTbq4) return word_to_half8(kw[blk][c]);
       else if constexpr (KF == kFmtTbq3)
         return tbq3_chunk_to_half8(tbq3_chunk(kw[blk][0], kw[blk][1], kw[blk][2], c));
+      else if constexpr (KF == kFmtQ8) return i8x8_to_half8(kq[blk][2 * c], kq[blk][2 * c + 1]);
       else return __builtin_bit_cast(half8, kf[4 * blk + c]);
     };
 
@@ -297,6 +350,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         uint8_t *row = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
         *(u32x4 *)row = u32x4{e[0], e[1], e[2], e[3]};
         *(u32x4 *)(row + 16) = u32x4{e[4], e[5], e[6], e[7]};
+      } else if constexpr (VF == kFmtQ8) {
+        // block `quarter` of the token: the scale then 32 codes, from byte
+        // 0 (even quarter: codes 2 bytes into the words) or byte 2 (odd
+        // quarter: codes from the second word on) of the fetched words
+        const u32x4 w0 = r.v4[2 * blk], w1 = r.v4[2 * blk + 1];
+        const uint32_t d[9] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], r.v1[blk]};
+        const bool odd = (quarter & 1) != 0;
+        uint32_t cw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cw[j] = odd ? d[j + 1] : alignbyte(d[j + 1], d[j], 2u);
+        uint8_t *row = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
+        *(u32x4 *)row = u32x4{cw[0], cw[1], cw[2], cw[3]};
+        *(u32x4 *)(row + 16) = u32x4{cw[4], cw[5], cw[6], cw[7]};
+        const uint16_t sbits = (uint16_t)(odd ? d[0] >> 16 : d[0] & 0xFFFFu);
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;   // (NaN guard)
+        svq[quarter * kTile + 16 * blk + col] = dead ? 0.0f : half_bits_to_float(sbits);
       } else {
         const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;   // (as for K)
 #pragma unroll
@@ -306,15 +375,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
     if (lane < kTile) {
-      float dk = qs_inv, dv = 1.0f;
-      if constexpr (KF != kFmtF16) dk = half_bits_to_float(r.sk) * qs_inv;
-      if constexpr (VF != kFmtF16) dv = half_bits_to_float(r.sv);
+      float dk = qs_inv, dv = 1.0f;   // (q8_0: per-block scales below)
+      if constexpr (KF == kFmtTbq4 || KF == kFmtTbq3) dk = half_bits_to_float(r.sk) * qs_inv;
+      if constexpr (KF == kFmtQ8) dk = 1.0f;
+      if constexpr (VF == kFmtTbq4 || VF == kFmtTbq3) dv = half_bits_to_float(r.sv);
       if constexpr (kPartial) {
         // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
         if (tok0 + lane >= n_ctx) dk = dv = 0.0f;
       }
       sk[lane] = dk;
       sv[lane] = dv;
+    }
+    if constexpr (KF == kFmtQ8) {
+      const int tk = lane & 31, c0 = 2 * (lane >> 5);
+      const bool dead = kPartial && tok0 + tk >= n_ctx;
+      skq[c0 * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[0]) * qs_inv;
+      skq[(c0 + 1) * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[1]) * qs_inv;
     }
     fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
 
@@ -323,14 +399,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // 16-lane rotation, and the two 16-token blocks share the work: lanes
     // 0-7 of each row finish block 0, lanes 8-15 block 1, so every lane
     // carries 4 distinct scores (head `head`, tokens 16 * own + 4 * quarter + e).
+    // (q8_0 K: step c spans block c, whose scale differs per token, so each
+    // step has its own accumulator and the scales are applied in fp32.)
     float4v acc[kBlk];
+    float4v acq[KF == kFmtQ8 ? kBlk : 1][4];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       acc[blk] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c], acc[blk],
-                                                          0, 0, 0);
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (KF == kFmtQ8)
+          acq[blk][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c],
+                                                               float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        else
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c], acc[blk],
+                                                            0, 0, 0);
+      }
+    }
+    __syncthreads();   // staged V rows and scales are visible
+    if constexpr (KF == kFmtQ8) {
+#pragma unroll
+      for (int blk = 0; blk < kBlk; ++blk)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4v kd4 = *(const float4v *)(skq + c * kTile + 16 * blk + 4 * quarter);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[blk][e] = fmaf(kd4[e], acq[blk][c][e], acc[blk][e]);
+        }
     }
     float sc[4];
 #pragma unroll
@@ -339,7 +434,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const float give = lo_part ? acc[0][e] : acc[1][e];   // what the partner lane needs
       sc[e] = mine + row_ror8(give);
     }
-    __syncthreads();   // staged V rows and scales are visible
 
     // t = score - m_ref with the running max updated lazily: m_ref is the
     // running max (0 before the first tile), and only a tile holding a score
@@ -412,6 +506,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
     half8 pa[kBlk / 2];
     pa[0] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    // q8_0 V: one P~ per 32-dim block c, p times that block's scale
+    half8 paq[VF == kFmtQ8 ? 4 : 1];
+    if constexpr (VF == kFmtQ8) {
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[e] = row_ror8(p4[e]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float *svc = lo_part ? svq + 4 * kTile : svq + c * kTile;
+        const float4v q0 = *(const float4v *)(svc + 4 * quarter);
+        const float4v q1 = *(const float4v *)(svc + 16 + 4 * quarter);
+        uint32_t qw[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          qw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(p4[2 * j] * q0[2 * j]),
+                                                      (_Float16)(p4[2 * j + 1] * q0[2 * j + 1])});
+          qw[2 + j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(pr[2 * j] * q1[2 * j]),
+                                                          (_Float16)(pr[2 * j + 1] * q1[2 * j + 1])});
+        }
+        paq[c] = __builtin_bit_cast(half8, u32x4{qw[0], qw[1], qw[2], qw[3]});
+      }
+    }
 
     // ---- O'^T += P~ V
     if constexpr (VF == kFmtTbq4) {
@@ -429,6 +545,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
           o[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], ve, o[2 * cg], 0, 0, 0);
           o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
         }
+      }
+    } else if constexpr (VF == kFmtQ8) {
+      // q8_0 V staged as int8 codes: one byte-transposed read per 16 dims
+      // (dims 16 db .. lie in block db / 2)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        typedef __attribute__((address_space(3))) int2v lds_i2;
+        const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            paq[db >> 1], i8x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]), o[db], 0, 0, 0);
       }
     } else if constexpr (VF == kFmtTbq3) {
       // TBQ3 V staged as e4m3 bytes: one byte-transposed read per 16 dims
@@ -593,13 +719,15 @@ hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hi
   dim3 grid(a.n_splits, a.n_kv_heads, batch);
   // (q dtype, K format, V format) -> kernel instance
 #define TBQ4_DEC(QT, KF, VF) reinterpret_cast<const void *>(&decode_split_kernel<QT, KF, VF>)
-#define TBQ4_DEC_K(QT, KF) {TBQ4_DEC(QT, KF, 0), TBQ4_DEC(QT, KF, 1), TBQ4_DEC(QT, KF, 2)}
-  static const void *const kernels[2][3][3] = {
-      {TBQ4_DEC_K(float, 0), TBQ4_DEC_K(float, 1), TBQ4_DEC_K(float, 2)},
-      {TBQ4_DEC_K(_Float16, 0), TBQ4_DEC_K(_Float16, 1), TBQ4_DEC_K(_Float16, 2)}};
+#define TBQ4_DEC_K(QT, KF) {TBQ4_DEC(QT, KF, 0), TBQ4_DEC(QT, KF, 1), TBQ4_DEC(QT, KF, 2), TBQ4_DEC(QT, KF, 3)}
+  static const void *const kernels[2][kNumFormats][kNumFormats] = {
+      {TBQ4_DEC_K(float, 0), TBQ4_DEC_K(float, 1), TBQ4_DEC_K(float, 2), TBQ4_DEC_K(float, 3)},
+      {TBQ4_DEC_K(_Float16, 0), TBQ4_DEC_K(_Float16, 1), TBQ4_DEC_K(_Float16, 2),
+       TBQ4_DEC_K(_Float16, 3)}};
 #undef TBQ4_DEC_K
 #undef TBQ4_DEC
-  if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
+  if (a.k_fmt < 0 || a.k_fmt >= kNumFormats || a.v_fmt < 0 || a.v_fmt >= kNumFormats)
+    return hipErrorInvalidValue;
   const void *fn = kernels[q_dtype == 0 ? 0 : 1][a.k_fmt][a.v_fmt];
   DecodeArgs arg = a;
   void *params[] = {&arg};

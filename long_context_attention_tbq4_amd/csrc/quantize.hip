@@ -226,6 +226,47 @@ hipError_t launch_store_f16(const StoreF16Args &a, int dtype, hipStream_t stream
   return hipGetLastError();
 }
 
+// q8_0 rows: one thread per value, the 32 lanes of a half-wavefront one
+// 32-value block.  d32 = amax / 127 and x / d32 are IEEE fp32 divisions
+// (correctly rounded), the code is x / d32 rounded to the nearest integer
+// with halves away from zero (roundf), the stored scale is the binary16
+// nearest d32.  Source [batch][n_new][n_kv_heads][128]; destination
+// [batch][n_kv_heads][capacity][136] at slots pos .. pos + n_new - 1.
+template <typename T>
+__global__ __launch_bounds__(256) void store_q8_kernel(StoreQ8Args a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // value index
+  const int64_t blk = i >> 5;                                   // same for 32 lanes
+  const int e = (int)(i & 31);
+  const bool live = blk < a.n_blocks;
+  const float x = live ? (float)load_exact<T>((const T *)a.src + i) : 0.0f;
+  float amax = fabsf(x);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (!live) return;
+  const float d32 = amax / 127.0f;
+  const int q = d32 > 0.0f ? (int)roundf(x / d32) : 0;
+  const int64_t vec = blk >> 2;                                 // head vector
+  const int kb = (int)(blk & 3);
+  const int64_t h = vec % a.n_kv_heads;
+  const int64_t t = (vec / a.n_kv_heads) % a.n_new;
+  const int64_t b = vec / ((int64_t)a.n_kv_heads * a.n_new);
+  uint8_t *dst = a.dst + ((b * a.n_kv_heads + h) * a.capacity + a.pos + t) * kQ8RowBytes + 34 * kb;
+  dst[2 + e] = (uint8_t)(int8_t)q;
+  if (e == 0) *(uint16_t *)dst = __builtin_bit_cast(uint16_t, (_Float16)d32);
+}
+
+hipError_t launch_store_q8(const StoreQ8Args &a, int dtype, hipStream_t stream) {
+  const int64_t grid = (a.n_blocks * 32 + 255) / 256;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(store_q8_kernel<float>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(store_q8_kernel<_Float16>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(store_q8_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int FMT>
 static void launch_quantize_fmt(const QuantArgs &a, int dtype, unsigned grid, hipStream_t stream) {
   switch (dtype) {

@@ -138,6 +138,22 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(half8, v);
 }
 
+// Eight int8 values (two words, byte order) -> an fp16 MFMA operand.  Each
+// byte b becomes the binary16 1024 + (b + 128) by a byte permute (0x64 is the
+// high byte of 1024 and the flipped sign bit makes b + 128 unsigned), then
+// 1152 is subtracted; exact, since every value is an integer below 2048.
+__device__ __forceinline__ half8 i8x8_to_half8(uint32_t w0, uint32_t w1) {
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+  const fp16x2 k = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const fp16x2 a = __builtin_bit_cast(fp16x2, perm(0x64646464u, x0, 0x04010400u)) + k;
+  const fp16x2 b = __builtin_bit_cast(fp16x2, perm(0x64646464u, x0, 0x04030402u)) + k;
+  const fp16x2 c = __builtin_bit_cast(fp16x2, perm(0x64646464u, x1, 0x04010400u)) + k;
+  const fp16x2 d = __builtin_bit_cast(fp16x2, perm(0x64646464u, x1, 0x04030402u)) + k;
+  u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+             __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(half8, v);
+}
+
 // 24-bit chunk c (0..3) of a lane's 96 code bits held in three words.
 __device__ __forceinline__ uint32_t tbq3_chunk(uint32_t w0, uint32_t w1, uint32_t w2, int c) {
   return c == 0 ? w0 : c == 1 ? __builtin_amdgcn_alignbit(w1, w0, 24)
@@ -159,6 +175,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_bytes
 
 __device__ __forceinline__ u32x4 buf_load_x4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ u32x3 buf_load_x3(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load_x2(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 __device__ __forceinline__ uint32_t buf_load_x1(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);

@@ -24,6 +24,13 @@ struct StoreF16Args {
   int32_t n_new, n_kv_heads, capacity, pos;
 };
 
+struct StoreQ8Args {
+  const void *src;             // [batch][n_new][n_kv_heads][128]
+  uint8_t *dst;                // [batch][n_kv_heads][capacity][136]
+  int64_t n_blocks;            // batch * n_new * n_kv_heads * 4 (32-value blocks)
+  int32_t n_new, n_kv_heads, capacity, pos;
+};
+
 struct DecodeArgs {
   const uint8_t *k;
   const uint8_t *v;
@@ -34,7 +41,7 @@ struct DecodeArgs {
   int32_t n_kv_heads, n_q_heads, group, capacity;
   int32_t n_ctx;         // context length, or the upper bound of ctx_lens
   int32_t n_splits;
-  int32_t k_fmt, v_fmt;  // cache formats (kFmtTbq4, kFmtF16, kFmtTbq3)
+  int32_t k_fmt, v_fmt;  // cache formats (kFmtTbq4, kFmtF16, kFmtTbq3, kFmtQ8)
   int32_t rotate_out;    // merge applies R^T (the V cache holds rotated values)
   float qscale;          // softmax_scale * log2(e)
   uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
@@ -63,13 +70,17 @@ struct PrefillArgs {
 constexpr int kDecodeTile = 32;
 
 // Cache formats of a K or V tensor: TBQ4 blocks (66 B per head vector), fp16
-// rows (256 B, not rotated), TBQ3 blocks (50 B).
-constexpr int kFmtTbq4 = 0, kFmtF16 = 1, kFmtTbq3 = 2;
+// rows (256 B, not rotated), TBQ3 blocks (50 B), q8_0 rows (four 34-byte
+// blocks of a binary16 scale and 32 int8 codes, 136 B, not rotated).
+constexpr int kFmtTbq4 = 0, kFmtF16 = 1, kFmtTbq3 = 2, kFmtQ8 = 3;
+constexpr int kNumFormats = 4;
 constexpr uint32_t kBlockBytes3 = 50;
+constexpr uint32_t kQ8RowBytes = 136;
 
 hipError_t launch_quantize(const QuantArgs &a, int dtype, int tensors, hipStream_t stream,
                            int format = kFmtTbq4);
 hipError_t launch_store_f16(const StoreF16Args &a, int dtype, hipStream_t stream);
+hipError_t launch_store_q8(const StoreQ8Args &a, int dtype, hipStream_t stream);
 // With start/stop events the dispatch itself records them (hipExtLaunchKernel).
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

@@ -194,12 +194,13 @@ def test_mixed_format_row_bytes_and_argument_errors(L):
     assert L.tbq4_format_row_bytes(0) == o.BLOCK_BYTES == 66        # TBQ4
     assert L.tbq4_format_row_bytes(1) == 2 * o.HEAD_DIM             # binary16 rows
     assert L.tbq4_format_row_bytes(2) == o.BLOCK_BYTES3 == 50       # TBQ3
-    assert L.tbq4_format_row_bytes(3) == 0 and L.tbq4_format_row_bytes(-1) == 0
+    assert L.tbq4_format_row_bytes(3) == o.Q8_ROW_BYTES == 136       # q8_0
+    assert L.tbq4_format_row_bytes(4) == 0 and L.tbq4_format_row_bytes(-1) == 0
 
     def mc(kf=0, vf=2, cap=64, head_dim=128):
         return _lib.MixedCache(FAKE, FAKE, kf, vf, 1, 2, head_dim, cap, 0)
     app = L.tbq4_mixed_append
-    assert app(ctypes.byref(mc(vf=3)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_UNSUPPORTED
+    assert app(ctypes.byref(mc(vf=4)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_UNSUPPORTED
     assert app(ctypes.byref(mc(kf=-1)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_UNSUPPORTED
     assert app(ctypes.byref(mc(cap=60)), FAKE, FAKE, 0, 0, 1, None) == _lib.ERR_ALIGNMENT
     assert app(ctypes.byref(mc()), FAKE, FAKE, 0, 60, 5, None) == _lib.ERR_CAPACITY
@@ -209,6 +210,7 @@ def test_mixed_format_row_bytes_and_argument_errors(L):
     def dec(cache, hq=8, n_ctx=10):
         return L.tbq4_mixed_attn_decode(ctypes.byref(cache), FAKE, 0, hq, n_ctx, 0.1, FAKE, 1, 0,
                                         FAKE, ws, None)
-    assert dec(mc(kf=2, vf=3)) == _lib.ERR_UNSUPPORTED
+    assert dec(mc(kf=2, vf=4)) == _lib.ERR_UNSUPPORTED
+    assert dec(mc(kf=3, vf=0), n_ctx=65) == _lib.ERR_CAPACITY
     assert dec(mc(kf=2, vf=2), n_ctx=65) == _lib.ERR_CAPACITY
     assert dec(mc(kf=2, vf=1), hq=18) == _lib.ERR_UNSUPPORTED

@@ -1,12 +1,13 @@
-"""Mixed K/V cache formats (TBQ4, TBQ3 or fp16 per tensor) against the fp64 oracle.
+"""Mixed K/V cache formats (TBQ4, TBQ3, q8_0 or fp16 per tensor) against the fp64 oracle.
 
 Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
 section "Konfiguracja": the K and the V cache types are chosen separately;
-section "6. Ten sam cache na Apple silicon" adds a TBQ3 cache.  Each tensor is
-stored as TBQ4 or TBQ3 blocks (rotated) or as binary16 rows (not rotated);
-attention is the plain definition on the dequantised tensors.  Bar: stored
-bytes identical to the oracle's; outputs within max-abs 2e-3 (+ half an fp16
-ulp for fp16 output) and relative L2 1e-3.
+section "6. Ten sam cache na Apple silicon" adds a TBQ3 cache; the tgstat.ru
+channel @tech_di page runs a q8_0 cache.  Each tensor is stored as TBQ4 or
+TBQ3 blocks (rotated), q8_0 rows or binary16 rows (not rotated); attention is
+the plain definition on the dequantised tensors.  Bar: stored bytes identical
+to the oracle's; outputs within max-abs 2e-3 (+ half an fp16 ulp for fp16
+output) and relative L2 1e-3.
 """
 
 import itertools
@@ -22,7 +23,7 @@ from _util import check_attn
 
 pytestmark = pytest.mark.gpu
 
-ALL = list(itertools.product([tb.FMT_TBQ4, tb.FMT_F16, tb.FMT_TBQ3], repeat=2))
+ALL = list(itertools.product([tb.FMT_TBQ4, tb.FMT_F16, tb.FMT_TBQ3, tb.FMT_Q8_0], repeat=2))
 MIXED = [f for f in ALL if f != (tb.FMT_TBQ4, tb.FMT_TBQ4)]
 
 
@@ -36,6 +37,9 @@ def _oracle_tensor(x, fmt, seed):
     if fmt == tb.FMT_TBQ3:
         packed = o.quantize_blocks3(xh, seed)[0]
         return packed, o.dequantize_blocks3(packed, seed)
+    if fmt == tb.FMT_Q8_0:
+        rows = o.q8_0_rows(xh)
+        return rows, o.dequantize_q8_0(rows)
     rows = o.f16_rows(xh)
     return rows.view(np.uint8), o.dequantize_f16(rows)
 
@@ -72,7 +76,7 @@ def _case(kf, vf, B, H, G, T, cap, scale, P, seed=0, rng_seed=0, kscale=1.0, jun
 @pytest.mark.parametrize("kf,vf", ALL)
 @pytest.mark.parametrize("P", [0, 3])
 def test_formats(kf, vf, P):
-    out, ref = _case(kf, vf, 2, 2, 8, 700, 712, 1 / math.sqrt(128), P, seed=3, rng_seed=kf + 3 * vf)
+    out, ref = _case(kf, vf, 2, 2, 8, 700, 712, 1 / math.sqrt(128), P, seed=3, rng_seed=kf + 4 * vf)
     check_attn(out, ref, False, f"k{kf} v{vf} P={P}")
 
 
