@@ -43,7 +43,7 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "cf918d0cd7d9efea2d4980fdb5e701b6bc639926e0acb8ea69f14b540b248418",
+TRAFFIC = {"sources_sha256": "d4624b132384f4b12a454cfda08c590d515678134ecc447958aca7f7feb3364f",
            "n_splits": 64, "fetch_kib": 271205.1, "fetch_factor": 2.0,
            "write_kib": 8704.0, "write_factor": 1.0}
 
@@ -123,9 +123,9 @@ class HipEvents:
         self.ev = []
 
 
-def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768, mixed=()):
-    """Append tokens t0 .. t1 of the workload to the TBQ4 cache and to every
-    cache in `mixed` (MixedKVCache) from the same generated K/V rows."""
+def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768, keep=None):
+    """Append tokens t0 .. t1 of the workload to the TBQ4 cache; with `keep`
+    (a list) the fp32 K/V chunks stay resident on the GPU for later caches."""
     from workloads import K, V, kv_tensor
     for a in range(t0, t1, chunk):
         log(f"{w.name}: filling tokens {a}..{min(t1, a + chunk)}")
@@ -133,8 +133,8 @@ def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768, mixed=()):
         k = torch.from_numpy(kv_tensor(w, 0, K, a, b)).cuda()
         v = torch.from_numpy(kv_tensor(w, 0, V, a, b)).cuda()
         tb.quantize_append(cache, k, v, a)
-        for m in mixed:
-            tb.mixed_append(m, k, v, a)
+        if keep is not None:
+            keep.append((a, k, v))
         del k, v
     torch.cuda.synchronize()
 
@@ -144,8 +144,8 @@ def bench_decode(tb, torch, args):
     w = WORKLOADS["decode128k"]
     B, Hkv, Hq, T = w.batch, w.n_kv_heads, w.n_q_heads, w.n_ctx
     cache = tb.KVCache(B, Hkv, T)
-    mixed = [tb.MixedKVCache(B, Hkv, T, kf, vf) for kf, vf in FORMATS] if args.formats else []
-    fill_cache(tb, torch, cache, w, 0, T, mixed=mixed)
+    rows = [] if args.formats else None
+    fill_cache(tb, torch, cache, w, 0, T, keep=rows)
     rng = np.random.default_rng([0, 99])
     k_new = torch.from_numpy(rng.standard_t(5, size=(B, 1, Hkv, 128)).astype(np.float32)).cuda()
     v_new = torch.from_numpy(rng.standard_t(5, size=(B, 1, Hkv, 128)).astype(np.float32)).cuda()
@@ -174,8 +174,14 @@ def bench_decode(tb, torch, args):
     hip.destroy()
     graph = bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w)
     verify = bench_verify(tb, torch, args, cache, w)
-    formats = [bench_format(tb, torch, args, m, q, out, ws, P, w) for m in mixed]
-    del mixed
+    formats = []
+    for kf, vf in (FORMATS if args.formats else ()):
+        m = tb.MixedKVCache(B, Hkv, T, kf, vf)
+        for t0, k, v in rows:
+            tb.mixed_append(m, k, v, t0)
+        formats.append(bench_format(tb, torch, args, m, q, out, ws, P, w))
+        del m
+    del rows
     kv_bytes = B * T * Hkv * 2 * 66
     q_bytes = B * Hq * 128 * 4
     out_bytes = B * Hq * 128 * 2
