@@ -254,6 +254,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[c], sacc, 0, 0, 0);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[c], sacc, 0, 0, 0);
       }
+      // the softmax issues at raised priority: the SIMD's other wavefront,
+      // when it is in its MFMA phase, keeps the matrix core busy meanwhile
+      __builtin_amdgcn_s_setprio(1);
       // element e holds key kb0 + 8 (e/4) + 4 half + e%4
       float s[16];
 #pragma unroll
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       }
       l_run = l_run * alpha + psum;
 
+      __builtin_amdgcn_s_setprio(0);
       // ---- O'^T[dim][row] += V^T P~^T
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
