@@ -257,13 +257,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       // the softmax issues at raised priority: the SIMD's other wavefront,
       // when it is in its MFMA phase, keeps the matrix core busy meanwhile
       __builtin_amdgcn_s_setprio(1);
-      // element e holds key kb0 + 8 (e/4) + 4 half + e%4
+      // element e holds key kb0 + 8 (e/4) + 4 half + e%4.  Scores and the
+      // running maximum stay scaled by the row's 2^ex (q' was normalised by
+      // it); the exact power-of-two scaling back is folded into the
+      // exponent's fused multiply-add.
       float s[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float4v dk4 = *(const float4v *)(&L.sk[buf][kb0 + 8 * m + 4 * half]);
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) s[4 * m + e2] = sacc[4 * m + e2] * (rowscale * dk4[e2]);
+        for (int e2 = 0; e2 < 4; ++e2) s[4 * m + e2] = sacc[4 * m + e2] * dk4[e2];
       }
       if (masked) {
 #pragma unroll
@@ -277,8 +280,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * rowscale);
       m_run = m_new;
+      const float m_log2 = m_new * rowscale;
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 4 * m + e2;
-          const float p = __builtin_amdgcn_exp2f(s[e] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[e], rowscale, -m_log2));
           psum += p;
           pb[e >> 3][e & 7] = (_Float16)(p * dv4[e2]);
         }
