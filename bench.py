@@ -172,6 +172,7 @@ def bench_decode(tb, torch, args):
     wall = time.perf_counter() - t0
     kern_ms = hip.elapsed_ms()
     hip.destroy()
+    sweep = bench_split_sweep(tb, torch, args, cache, q, w)
     graph = bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w)
     verify = bench_verify(tb, torch, args, cache, w)
     formats = []
@@ -198,6 +199,7 @@ def bench_decode(tb, torch, args):
         "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
         "tokens_per_s": B * T / (ms * 1e-3),
         "graph": graph,
+        "sweep": sweep,
         "verify": verify,
         "formats": formats,
     }
@@ -234,6 +236,33 @@ def bench_format(tb, torch, args, cache, q, out, ws, P, w):
             "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(B * T / (ms * 1e-3), 1)}
+
+
+def bench_split_sweep(tb, torch, args, cache, q, w):
+    """The split kernel alone at 98304 and 131072 attended slots of the
+    resident cache, for split counts 16 .. 256 (dispatch-recorded events,
+    mean over the timed calls)."""
+    B, Hkv, Hq = cache.batch, cache.n_kv_heads, q.shape[1]
+    res = []
+    for n in (98304, cache.capacity):
+        for P in (16, 32, 64, 128, 256):
+            ws = torch.empty(tb.decode_workspace_bytes(B, Hkv, Hq, n, P), dtype=torch.uint8,
+                             device="cuda")
+            for _ in range(args.warmup):
+                tb.attn_decode_partial(cache, q, n, w.softmax_scale, n_splits=P, workspace=ws)
+            torch.cuda.synchronize()
+            hip = HipEvents(args.steps)
+            for i in range(args.steps):
+                tb.attn_decode_partial(cache, q, n, w.softmax_scale, n_splits=P, workspace=ws,
+                                       events=hip.pair(i))
+            torch.cuda.synchronize()
+            ms = float(np.mean(hip.elapsed_ms()))
+            hip.destroy()
+            byt = B * n * Hkv * 2 * 66 + B * Hq * 128 * 4
+            res.append({"n_ctx": n, "n_splits": P, "kernel_ms": round(ms, 5),
+                        "gbs": round(byt / (ms * 1e-3) / 1e9, 1)})
+    log("split sweep: " + ", ".join(f"{r['n_ctx']}/{r['n_splits']}: {r['gbs']:.0f}" for r in res))
+    return res
 
 
 def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
@@ -438,6 +467,11 @@ def main():
                         "q8_0 (136 B) or fp16 (256 B) per head vector; one decode call (split "
                         "kernel + merge) over 131072 slots, calls back to back",
             "results": dec["formats"],
+        },
+        "split_sweep": {
+            "workload": "decode128k cache; split kernel alone at 98304 and 131072 attended "
+                        "slots, batch 4, 8 / 64 heads",
+            "results": dec["sweep"],
         },
         "graph_step": {
             "ms_per_step": round(dec["graph"]["ms_per_step"], 5),

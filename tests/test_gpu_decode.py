@@ -140,12 +140,14 @@ def test_decode16k_workload_full():
 
 @pytest.mark.slow
 def test_decode128k_workload_sampled():
-    """Decode at 131072, batch 4, Student-t KV with channel scales: the whole
-    cache is filled on the GPU; two (sequence, KV head) rows are re-quantised
-    by the oracle (bytes compared) and their 16 query heads checked, for the
-    split counts the benchmark sweeps."""
+    """Decode at 131072 and at 98304 slots, batch 4, Student-t KV with channel
+    scales (the decode96k rows are the first 98304 of the same recipe): the
+    whole cache is filled on the GPU; two (sequence, KV head) rows are
+    re-quantised by the oracle (bytes compared) and their 16 query heads
+    checked, for split counts 16 .. 256 and the automatic one."""
     w = WORKLOADS["decode128k"]
     T = w.n_ctx
+    T96 = WORKLOADS["decode96k"].n_ctx
     cache = tb.KVCache(w.batch, w.n_kv_heads, T)
     for t0 in range(0, T, 32768):
         t1 = t0 + 32768
@@ -154,8 +156,8 @@ def test_decode128k_workload_sampled():
         tb.quantize_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), t0)
     q = q_decode(w)
     qt = torch.from_numpy(q).cuda()
-    outs = {P: tb.attn_decode(cache, qt, T, w.softmax_scale, n_splits=P).float().cpu().numpy()
-            for P in (0, 16, 32, 64, 128, 256)}
+    outs = {(n, P): tb.attn_decode(cache, qt, n, w.softmax_scale, n_splits=P).float().cpu().numpy()
+            for n in (T96, T) for P in (0, 16, 32, 64, 128, 256)}
     G = w.n_q_heads // w.n_kv_heads
     for (b, g) in ((0, 0), (3, 5)):
         K = kv_rows(w, 0, 0, b, g, 0, T)
@@ -164,10 +166,11 @@ def test_decode128k_workload_sampled():
         vc = o.quantize_blocks(V)[0]
         assert np.array_equal(cache.k[b, g].cpu().numpy(), kc)
         assert np.array_equal(cache.v[b, g].cpu().numpy(), vc)
-        ref = o.attn_decode_rows_ref(q[b, g * G:(g + 1) * G], o.dequantize_blocks(kc),
-                                     o.dequantize_blocks(vc), w.softmax_scale)
-        for P, out in outs.items():
-            check_attn(out[b, g * G:(g + 1) * G], ref, True, f"128k b={b} g={g} P={P}")
+        Kh, Vh = o.dequantize_blocks(kc), o.dequantize_blocks(vc)
+        for n in (T96, T):
+            ref = o.attn_decode_rows_ref(q[b, g * G:(g + 1) * G], Kh[:n], Vh[:n], w.softmax_scale)
+            for P in (0, 16, 32, 64, 128, 256):
+                check_attn(outs[(n, P)][b, g * G:(g + 1) * G], ref, True, f"n={n} b={b} g={g} P={P}")
 
 
 def test_two_phase_equals_one_call():
