@@ -189,8 +189,8 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
  * (-ctk, -ctv).  The DFlash speed-test page (gptunnel blog), section "Қосымша
  * олжа: кванттталған KV-кэш жылдамдықтың 39%-ын жейді", measures what a
  * quantised cache costs against an fp16 one.  These calls let each tensor be
- * TBQ4 blocks or plain fp16 rows, so the dequantisation cost can be weighed
- * against the bytes saved per tensor.
+ * TBQ4 or TBQ3 blocks, q8_0 rows or plain fp16 rows, so the dequantisation
+ * cost can be weighed against the bytes saved per tensor.
  *
  *   TBQ4_FMT_TBQ4  66-byte blocks as above, rotated by the cache's signs
  *   TBQ4_FMT_F16   head vectors stored as 128 binary16 values (round to
@@ -218,7 +218,8 @@ tbq4_status tbq4_attn_decode_merge(const void *workspace, size_t workspace_bytes
  *                  value.  Inputs must be finite.
  * tbq4_mixed_cache: k, v point at [batch][n_kv_heads][capacity][row bytes of
  * their format] (tbq4_format_row_bytes), 16-byte aligned; the rest as in
- * the TBQ4-only descriptor, capacity a multiple of 8.
+ * tbq4_cache, capacity a multiple of 8.  Unknown formats are
+ * TBQ4_ERR_UNSUPPORTED.
  * tbq4_mixed_append: as tbq4_quantize_append, each tensor in its format.
  * tbq4_mixed_attn_decode: as tbq4_attn_decode (same workspace size, G <= 8):
  *   q is rotated only when K is stored rotated (TBQ4 or TBQ3), and the
