@@ -373,8 +373,9 @@ tbq4_status tbq4_mixed_attn_decode(const tbq4_mixed_cache *cache, const void *q,
 }
 
 int32_t verify_auto_splits(int32_t batch, int32_t n_kv_heads, int32_t n_q, int32_t n_kv) {
-  // the four-query kernel keeps one wavefront per SIMD, the two-query one two
-  const int64_t waves = n_q > 2 ? 1024 : 2048;
+  // two wavefronts per SIMD (both kernels fit: q' waits in LDS)
+  const int64_t waves = 2048;
+  (void)n_q;
   const int64_t n_tiles = (n_kv + tbq4::kDecodeTile - 1) / tbq4::kDecodeTile;
   const int64_t rows = (int64_t)batch * n_kv_heads;
   int64_t p = (waves + rows - 1) / rows;

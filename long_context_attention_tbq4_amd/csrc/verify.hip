@@ -16,7 +16,9 @@
 //     of column group c, G <= 8 heads each -- and one or two column groups
 //     cover n_q <= 2 or n_q <= 4,
 //   * q' is carried as an fp16 high part and the fp16 residual, multiplied
-//     by the same K operand in two MFMAs that accumulate into one score,
+//     by the same K operand in two MFMAs that accumulate into one score; the
+//     q' operands wait in LDS (one 16-byte slot per lane) instead of
+//     registers, which keeps two wavefronts per SIMD for four queries,
 //   * every column is a distinct (query, head), so each lane finishes its
 //     own scores and P~ rows; P~ = p d^V is one fp16, rounded to nearest.
 // Partial states use the decode workspace layout with (sequence, query) as
@@ -39,6 +41,7 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
   __shared__ __attribute__((aligned(16))) float sk[kTile];
   __shared__ __attribute__((aligned(16))) float sv[kTile];
+  __shared__ __attribute__((aligned(16))) half8 qlds[CG][4][2][64];   // q' high / residual
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -110,6 +113,13 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         qhi[c][k][el] = hi;
         qlo[c][k][el] = (_Float16)(x - (float)hi);
       }
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qlds[c][k][0][lane] = qhi[c][k];
+      qlds[c][k][1][lane] = qlo[c][k];
+    }
 
   // ---------------- token range: slots [0, n_past + n_q) in 32-token tiles
   const int n_kv = a.n_past + a.n_q;
@@ -197,20 +207,25 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 
     // ---- scores: S^T[token][(query, head)] = K . (q'_hi + q'_lo)
     float4v acc[CG][kBlk];
+    {
+      half8 kh[kBlk][4];
 #pragma unroll
-    for (int blk = 0; blk < kBlk; ++blk) {
-      half8 kh[4];
+      for (int blk = 0; blk < kBlk; ++blk)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) kh[k] = word_to_half8(kw[blk][k]);
+        for (int k = 0; k < 4; ++k) kh[blk][k] = word_to_half8(kw[blk][k]);
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
-        float4v s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int blk = 0; blk < kBlk; ++blk) acc[c][blk] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[k], qhi[c][k], s4, 0, 0, 0);
-          s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[k], qlo[c][k], s4, 0, 0, 0);
+          const half8 qh = qlds[c][k][0][lane], ql = qlds[c][k][1][lane];
+#pragma unroll
+          for (int blk = 0; blk < kBlk; ++blk) {
+            acc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[blk][k], qh, acc[c][blk], 0, 0, 0);
+            acc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[blk][k], ql, acc[c][blk], 0, 0, 0);
+          }
         }
-        acc[c][blk] = s4;
       }
     }
     __syncthreads();
