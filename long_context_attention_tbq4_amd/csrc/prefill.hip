@@ -6,13 +6,15 @@
 // no F16 buffer in memory.  A prefill chunk: query i of the chunk sits at
 // absolute position n_past + i and attends keys 0 .. n_past + i.
 //
-// A workgroup owns one KV head and a tile of 128/G queries x G heads = 128
-// rows (4 wavefronts x 32 rows); blockIdx.x % n_kv_heads is the KV head, so
-// on an 8-XCD part each XCD streams the cache of its own head.  Per 64-key
-// tile the workgroup
+// A workgroup owns one KV head and a tile of 256/G queries x G heads = 256
+// rows (8 wavefronts x 32 rows, two per SIMD: the whole CU); blockIdx.x %
+// n_kv_heads is the KV head, so on an 8-XCD part each XCD streams the cache
+// of its own head.  Eight wavefronts share each staged tile, so a thread
+// dequantises 16 codes of K and of V per tile and each tile is read by half
+// as many workgroups as with four.  Per 64-key tile the workgroup
 //   * fetches the next tile's packed K and V rows before it computes on the
-//     current one (wavefront w loads quarter w of every key's index bytes;
-//     together the four cover the tile's contiguous bytes) and dequantises
+//     current one (wavefront w loads eighth w of every key's index bytes;
+//     together the eight cover the tile's contiguous bytes) and dequantises
 //     them into the other half of a double-buffered LDS tile: fp16 codebook
 //     values, one fp32 scale per key and tensor,
 //   * S^T = K Q'^T on v_mfma_f32_32x32x16_f16, with q' split into an fp16
@@ -64,23 +66,25 @@ template <typename T> __device__ __forceinline__ float ld(const T *p);
 template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float ld<_Float16>(const _Float16 *p) { return (float)*p; }
 
-// One thread's share of a tile fetch: 16 index bytes of K and V for one key
-// and quarter (5 raw words each), and the key's two scales (quarter 0).
+// One thread's share of a tile fetch: 8 index bytes of K and V for one key
+// (3 raw words each, realigned by 0 or 2 bytes), and the key's two scales
+// (first eighth).
 struct TileRaw {
-  u32x4 k4, v4;
-  uint32_t k1, v1;
+  u32x3 k3, v3;
   uint16_t sk, sv;
 };
 
+constexpr int kWaves = 8;           // wavefronts per workgroup (32 rows each)
+
 template <typename QT, typename OT>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillLds L;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
   const int qpw = 32 / G;                        // queries per wavefront
-  const int qpwg = 4 * qpw;                      // queries per workgroup
+  const int qpwg = kWaves * qpw;                 // queries per workgroup
   const int g = blockIdx.x % a.n_kv_heads;
   const int qt = blockIdx.x / a.n_kv_heads;
   const int b = blockIdx.y;
@@ -163,19 +167,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const rsrc_t rk = make_rsrc(a.k + rowoff, row_bytes);
   const rsrc_t rv = make_rsrc(a.v + rowoff, row_bytes);
 
-  // fetch mapping: thread -> (key, quarter), wavefront w fetching quarter w
-  // of the tile's 64 keys; start offsets are even, so the realignment shift
-  // is 0 or 2 (a per-thread constant)
+  // fetch mapping: thread -> (key, eighth), wavefront w fetching index bytes
+  // 8 w .. 8 w + 7 of the tile's 64 keys; start offsets are even, so the
+  // realignment shift is 0 or 2 (a per-thread constant)
   const int fkey = tid & 63, fq = tid >> 6;
-  const uint32_t foff = (uint32_t)fkey * kBlockBytes + 2 + 16 * fq;
+  const uint32_t foff = (uint32_t)fkey * kBlockBytes + 2 + 8 * fq;
   const uint32_t fshift = foff & 3u;
   auto fetch = [&](TileRaw &r, int t) {
     const uint32_t base = (uint32_t)t * kKT * kBlockBytes;
     const uint32_t a0 = (base + foff) & ~3u;
-    r.k4 = buf_load_x4(rk, a0);
-    r.k1 = buf_load_x1(rk, a0 + 16);
-    r.v4 = buf_load_x4(rv, a0);
-    r.v1 = buf_load_x1(rv, a0 + 16);
+    r.k3 = buf_load_x3(rk, a0);
+    r.v3 = buf_load_x3(rv, a0);
     r.sk = 0;
     r.sv = 0;
     // keys at or past n_past + n_q may hold anything: their scales stay 0 so
@@ -185,24 +187,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       r.sv = buf_load_u16(rv, base + (uint32_t)fkey * kBlockBytes);
     }
   };
-  // dequantise a fetched share into LDS buffer `buf`: 32 fp16 codebook
-  // values of K and of V at row fkey, positions 32 fq .. 32 fq + 31
+  // dequantise a fetched share into LDS buffer `buf`: 16 fp16 codebook
+  // values of K and of V at row fkey, positions 16 fq .. 16 fq + 15
   auto stage = [&](const TileRaw &r, int buf) {
-    const uint32_t kw[4] = {alignbyte(r.k4[1], r.k4[0], fshift), alignbyte(r.k4[2], r.k4[1], fshift),
-                            alignbyte(r.k4[3], r.k4[2], fshift), alignbyte(r.k1, r.k4[3], fshift)};
-    const uint32_t vw[4] = {alignbyte(r.v4[1], r.v4[0], fshift), alignbyte(r.v4[2], r.v4[1], fshift),
-                            alignbyte(r.v4[3], r.v4[2], fshift), alignbyte(r.v1, r.v4[3], fshift)};
-    uint8_t *kr = L.k[buf] + fkey * kRowB + 64 * fq;
+    const uint32_t kw[2] = {alignbyte(r.k3[1], r.k3[0], fshift), alignbyte(r.k3[2], r.k3[1], fshift)};
+    const uint32_t vw[2] = {alignbyte(r.v3[1], r.v3[0], fshift), alignbyte(r.v3[2], r.v3[1], fshift)};
+    uint8_t *kr = L.k[buf] + fkey * kRowB + 32 * fq;
     uint8_t *vr = L.v[buf] + fkey * kVRowB;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
       uint32_t r0, r1, r2, r3;
       nib4_to_f16(kw[c], r0, r1);
       nib4_to_f16(kw[c] >> 4, r2, r3);
       *(u32x4 *)(kr + 16 * c) = u32x4{r0, r1, r2, r3};
       nib4_to_f16(vw[c], r0, r1);
       nib4_to_f16(vw[c] >> 4, r2, r3);
-      *(u32x4 *)(vr + v_swizzle(fkey, 64 * fq + 16 * c)) = u32x4{r0, r1, r2, r3};
+      *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq + 16 * c)) = u32x4{r0, r1, r2, r3};
     }
     if (fq == 0) {
       L.sk[buf][fkey] = half_bits_to_float(r.sk);
@@ -367,19 +367,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
                           hipStream_t stream) {
-  const int qpwg = 4 * (32 / a.group);
+  const int qpwg = kWaves * (32 / a.group);
   const int n_qt = (a.n_q + qpwg - 1) / qpwg;
   const int64_t gx = (int64_t)n_qt * a.n_kv_heads;
   if (gx > 0x7FFFFFFF || batch > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)gx, batch);
   if (q_dtype == 0 && out_dtype == 1)
-    hipLaunchKernelGGL((prefill_kernel<float, _Float16>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<float, _Float16>), grid, dim3(64 * kWaves), 0, stream, a);
   else if (q_dtype == 0)
-    hipLaunchKernelGGL((prefill_kernel<float, float>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<float, float>), grid, dim3(64 * kWaves), 0, stream, a);
   else if (out_dtype == 1)
-    hipLaunchKernelGGL((prefill_kernel<_Float16, _Float16>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<_Float16, _Float16>), grid, dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<_Float16, float>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<_Float16, float>), grid, dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
