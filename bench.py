@@ -43,7 +43,7 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "d4624b132384f4b12a454cfda08c590d515678134ecc447958aca7f7feb3364f",
+TRAFFIC = {"sources_sha256": "36cc36125ee6b2c4b736dd9720073c1ed22ba309d3f9b8b84236b57c17739d99",
            "n_splits": 64, "fetch_kib": 271198.4, "fetch_factor": 2.0,
            "write_kib": 8704.0, "write_factor": 1.0}
 

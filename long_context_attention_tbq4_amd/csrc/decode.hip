@@ -39,11 +39,11 @@ constexpr int kTile = kDecodeTile;  // tokens per loop iteration
 constexpr int kBlk = kTile / 16;    // 16-token MFMA row blocks per tile
 constexpr int kVRow = 80;           // LDS bytes per staged V row (64 + pad)
 
-
-
 // Cache formats of the K and V tensors (template arguments KF, VF): TBQ4
-// blocks, fp16 rows (not rotated), TBQ3 blocks or q8_0 rows (not rotated).
-// q is rotated when K is a TBQ format; the merge applies R^T when V is.
+// blocks (the path described above), fp16 rows (not rotated), TBQ3 blocks or
+// q8_0 rows (not rotated); each format's fetch, operand and staging steps
+// sit beside the TBQ4 ones below.  q is rotated when K is a TBQ format; the
+// merge applies R^T when V is.
 constexpr int kE4Row = 144;         // LDS bytes per staged TBQ3 (e4m3) or q8_0 (int8) V row: 128 bytes + pad
                                     // (36 dwords: the 8 rows of one byte-transposed read
                                     // fall on distinct banks)
