@@ -213,20 +213,24 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
       for (int blk = 0; blk < kBlk; ++blk)
 #pragma unroll
         for (int k = 0; k < 4; ++k) kh[blk][k] = word_to_half8(kw[blk][k]);
+      // consecutive MFMAs rotate through the CG x 2 accumulators, so none
+      // waits for the one before it (each accumulator still takes step k's
+      // high part, then its residual, in order)
 #pragma unroll
-      for (int c = 0; c < CG; ++c) {
+      for (int c = 0; c < CG; ++c)
 #pragma unroll
         for (int blk = 0; blk < kBlk; ++blk) acc[c][blk] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const half8 qh = qlds[c][k][0][lane], ql = qlds[c][k][1][lane];
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-          for (int blk = 0; blk < kBlk; ++blk) {
-            acc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[blk][k], qh, acc[c][blk], 0, 0, 0);
-            acc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[blk][k], ql, acc[c][blk], 0, 0, 0);
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const half8 qo = qlds[c][k][hl][lane];
+#pragma unroll
+            for (int blk = 0; blk < kBlk; ++blk)
+              acc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[blk][k], qo, acc[c][blk], 0, 0, 0);
           }
-        }
-      }
     }
     __syncthreads();
 
