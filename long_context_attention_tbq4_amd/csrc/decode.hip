@@ -626,63 +626,73 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge: o = R^T (sum_p 2^(m_p - M) o'_p / sum_p 2^(m_p - M) l_p), one
-// 256-thread workgroup per (sequence, query head).  The four wavefronts take
-// every fourth split (lane holds dims lane and lane + 64), several splits in
-// flight at once; the partial sums meet in LDS and wavefront 0 normalises,
-// applies the inverse rotation and stores.
+// 256-thread workgroup per (sequence, query head), in one pass over the
+// partials.  Wavefront w takes splits w, w + 4, ... in chunks of 16 (lane
+// holds dims lane and lane + 64), all loads of a chunk in flight together,
+// combined under a running maximum; the four wavefronts' sums meet in LDS,
+// rescaled to the common maximum, and wavefront 0 normalises, applies the
+// inverse rotation and stores.  Empty splits carry m = -inf and weigh 0.
 template <typename OT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ float red[4][130];
-  __shared__ float smax[4];
+  __shared__ float red[4][130];   // o'[128], l, m per wavefront
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int P = a.n_splits;
   const float *base = a.ws + ((size_t)b * a.n_q_heads + h) * P * 130;
 
-  float M = -INFINITY;
-  for (int p = tid; p < P; p += 256) M = fmaxf(M, base[(size_t)p * 130]);
+  float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int p0 = wave; p0 < P; p0 += 64) {
+    float mp[16], lp[16], x0[16], x1[16];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if (lane == 0) smax[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
-  if (M == -INFINITY) M = 0.0f;   // every split empty (a zero-length sequence): output 0
-
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  int p = wave;
-  for (; p + 12 < P; p += 16) {
-    float w[4], lp[4], x0[4], x1[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float *bp = base + (size_t)(p + 4 * u) * 130;
-      w[u] = bp[0];
+    for (int u = 0; u < 16; ++u) {
+      // splits past P reread split p0 (valid: p0 < P) and weigh 0, so that
+      // the 64 loads issue together without branches
+      const int p = p0 + 4 * u;
+      const float *bp = base + (size_t)(p < P ? p : p0) * 130;
+      mp[u] = bp[0];
       lp[u] = bp[1];
       x0[u] = bp[2 + lane];
       x1[u] = bp[66 + lane];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wt = __builtin_amdgcn_exp2f(w[u] - M);
-      L += wt * lp[u];
-      o0 += wt * x0[u];
-      o1 += wt * x1[u];
+    for (int u = 0; u < 16; ++u)
+      if (p0 + 4 * u >= P) mp[u] = -INFINITY;
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cm = fmaxf(cm, mp[u]);
+    if (cm == -INFINITY) continue;   // only empty splits so far (wavefront-uniform)
+    const float al = __builtin_amdgcn_exp2f(M - cm);   // 0 while M is -inf
+    L *= al;
+    o0 *= al;
+    o1 *= al;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float wt = __builtin_amdgcn_exp2f(mp[u] - cm);
+      L = fmaf(wt, lp[u], L);
+      o0 = fmaf(wt, x0[u], o0);
+      o1 = fmaf(wt, x1[u], o1);
     }
-  }
-  for (; p < P; p += 4) {
-    const float *bp = base + (size_t)p * 130;
-    const float wt = __builtin_amdgcn_exp2f(bp[0] - M);
-    L += wt * bp[1];
-    o0 += wt * bp[2 + lane];
-    o1 += wt * bp[66 + lane];
+    M = cm;
   }
   red[wave][lane] = o0;
   red[wave][64 + lane] = o1;
-  if (lane == 0) red[wave][128] = L;
+  if (lane == 0) {
+    red[wave][128] = L;
+    red[wave][129] = M;
+  }
   __syncthreads();
   if (wave != 0) return;
-  o0 = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-  o1 = red[0][64 + lane] + red[1][64 + lane] + red[2][64 + lane] + red[3][64 + lane];
-  L = red[0][128] + red[1][128] + red[2][128] + red[3][128];
+  const float Mx = fmaxf(fmaxf(red[0][129], red[1][129]), fmaxf(red[2][129], red[3][129]));
+  o0 = o1 = L = 0.0f;
+  if (Mx != -INFINITY) {   // every split empty (a zero-length sequence): output 0
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sw = __builtin_amdgcn_exp2f(red[w][129] - Mx);
+      o0 = fmaf(sw, red[w][lane], o0);
+      o1 = fmaf(sw, red[w][64 + lane], o1);
+      L = fmaf(sw, red[w][128], L);
+    }
+  }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   o0 *= inv;
   o1 *= inv;
