@@ -1,0 +1,43 @@
+"""bench.py's host-side contract, on the CPU: more than one GPU is refused with
+a message, and the CPU baseline (the oracle timed on a bounded sample of the
+128K decode workload) reports the fields the result line carries."""
+
+import importlib.util
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench_module():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2",
+                        "--steps", "1", "--warmup", "0"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single MI355X" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_cpu_baseline_fields():
+    bench = _bench_module()
+    cpu = bench.cpu_baseline(budget_s=0.0)   # one (sequence, KV head) row
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s"
+    assert cpu["value"] > 0 and cpu["cores"] >= 1
+    assert cpu["sample"].startswith("1 of 32 (sequence, KV head) rows of decode128k")
+
+
+def test_traffic_only_for_the_measured_split_count():
+    bench = _bench_module()
+    assert bench.measured_traffic(bench.TRAFFIC["n_splits"] + 1) is None
+    t = bench.measured_traffic(bench.TRAFFIC["n_splits"])
+    # either the sources are the measured ones (bytes per launch at least the
+    # algorithmic 553 779 200 B) or they changed since (unknown: None)
+    assert t is None or t >= 553_779_200
