@@ -51,7 +51,7 @@ constexpr int kF16Row = 288;        // LDS bytes per staged fp16 V row (256 + pa
                                     // put the 4 rows of one transposed read on distinct banks)
 
 template <typename QT, int KF, int VF>
-__global__ __launch_bounds__(128) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // bytes per head vector of each tensor
   constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3
                              : KF == kFmtQ8 ? kQ8RowBytes : 2 * kHeadDim;
@@ -66,14 +66,8 @@ __global__ __launch_bounds__(128) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float svq[VF == kFmtQ8 ? 4 * kTile + 32 : 4];
   __shared__ __attribute__((aligned(16))) float sk[kTile];   // d^K * 2^-ex per token
   __shared__ __attribute__((aligned(16))) float sv[kTile + 32];   // d^V per token, then zeros
-  // hand-over from the K wavefront to the V wavefront, double-buffered by
-  // tile parity: each lane's 4 probabilities, the rescale flag and factors
-  __shared__ __attribute__((aligned(16))) float4v pbuf[2][64];
-  __shared__ __attribute__((aligned(16))) float abuf[2][8];
-  __shared__ int fbuf[2];
 
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // 0: K, 1: V
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int quarter = lane >> 4;       // 32-dimension quarter / token sub-group
@@ -81,6 +75,80 @@ __global__ __launch_bounds__(128) void decode_split_kernel(DecodeArgs a) {
   const int head = col & 7;
   const bool lo_part = col >= 8;
   static_assert(kBlk == 2, "the score split between lanes 0-7 and 8-15 pairs two blocks");
+  // lanes of P~ rows 8-15 read zero V scales
+  const float *sv_rd = lo_part ? sv + kTile : sv;
+  if (lane < 32) sv[kTile + lane] = 0.0f;
+  if constexpr (VF == kFmtQ8) {
+    if (lane < 32) svq[4 * kTile + lane] = 0.0f;
+  }
+
+  // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
+  // fp16 K cache), split into fp16 hi + residual
+  float qv[32];
+  {
+    // lane quarter q holds dims 32 q + i; for a q8_0 K cache dims
+    // 32 (i/8) + 8 q + i%8 instead, so that MFMA step c spans q8_0 block c
+    const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim;
+    const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int d = KF == kFmtQ8 ? 32 * (i >> 3) + 8 * quarter + (i & 7) : 32 * quarter + i;
+      float x = head < G ? load_q<QT>(qp + d) : 0.0f;
+      qv[i] = ((sw >> i) & 1u) ? -x : x;
+    }
+    if constexpr (kKRot) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & h) == 0) {
+          const float x = qv[i], y = qv[i + h];
+          qv[i] = x + y;
+          qv[i + h] = x - y;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 16; h <= 32; h <<= 1) {   // dims 32 and 64 apart: lanes 16 / 32 apart
+      const bool upper = (lane & h) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float o = __shfl_xor(qv[i], h, 64);
+        qv[i] = upper ? (o - qv[i]) : (qv[i] + o);
+      }
+    }
+    }
+  }
+  const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    qv[i] *= f;
+    mx = fmaxf(mx, fabsf(qv[i]));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  // one power-of-two normalisation for the whole group: max |q'| in
+  // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
+  // range, and 2^-ex folds into the per-token key scale
+  int ex = 0;
+  if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
+  ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+  const float qs_inv = ldexpf(1.0f, -ex);
+  half8 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int el = 0; el < 8; ++el) {
+      // TBQ4 K operands hold the 4 even then the 4 odd dims of a code word;
+      // fp16, TBQ3 and q8_0 K operands hold 8 consecutive dims
+      const int i = KF == kFmtTbq4 ? 8 * c + (el < 4 ? 2 * el : 2 * el - 7) : 8 * c + el;
+      const float x = ldexpf(qv[i], ex);
+      const _Float16 hi = (_Float16)x;
+      const _Float16 lo = (_Float16)(x - (float)hi);
+      qop[c][el] = lo_part ? lo : hi;
+    }
+  }
 
   // ---------------- token range of this split: this sequence's length (from
   // device memory when given) in 32-token tiles, spread evenly over the splits
@@ -90,20 +158,45 @@ __global__ __launch_bounds__(128) void decode_split_kernel(DecodeArgs a) {
   const int tiles_per_split = (n_tiles + a.n_splits - 1) / a.n_splits;
   const int t_begin = split * tiles_per_split;
   const int t_end = min(t_begin + tiles_per_split, n_tiles);
-  const int t_full = min(t_end, n_ctx / kTile);   // tiles below t_full are full
 
   const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity;
-  const int P = a.n_splits;
-  float *wsb = a.ws + ((size_t)b * a.n_q_heads + (size_t)g * G) * P * 130 + (size_t)split * 130;
+  const rsrc_t rk = make_rsrc(a.k + row * kKBytes, (uint32_t)a.capacity * kKBytes);
+  const rsrc_t rv = make_rsrc(a.v + row * kVBytes, (uint32_t)a.capacity * kVBytes);
 
-  // Raw fetch of one tensor's 32-token tile: per 16-token group, 5 words
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4v o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // transposed-read source address (fixed per lane): lane s of 16-lane group
+  // G4 points at token tau(G4, s/2), byte 8*(s&1) of a 16-byte column group
+  int tr_off;
+  {
+    const int e = col >> 1;
+    const int tok = 16 * (e >> 2) + 4 * quarter + (e & 3);
+    tr_off = tok * kVRow + 8 * (col & 1);
+  }
+  const int tr16_off = (4 * quarter + (col >> 2)) * kF16Row + 8 * (col & 3);
+  // TBQ3 V (e4m3 rows): source lane s of a 16-lane group points at the
+  // token of P~ operand position 8 quarter + s/2 and bytes 8 (s & 1) .. + 7
+  // of a 16-dim block, so a byte-transposed read gives a lane 8 tokens of
+  // dim 16 db + col
+  int tr8_3_off;
+  {
+    const int j = col >> 1;
+    const int tok = j < 4 ? 4 * quarter + j : 16 + 4 * quarter + (j - 4);
+    tr8_3_off = tok * kE4Row + 8 * (col & 1);
+  }
+
+  // Raw fetch of one 32-token tile: per 16-token group, 5 words of K and of V
   // covering this lane's 16 index bytes (start offsets are even, so the words
-  // are realigned by 0 or 2 bytes -- a per-lane constant), plus the scale of
+  // are realigned by 0 or 2 bytes -- a per-lane constant), plus the scales of
   // token `lane`.  The next tile is fetched into the same registers as soon as
-  // the current tile's raw words are consumed, so it is in flight during the
-  // rest of the current tile's work.  A tile past the end of the split is
-  // fetched at an offset beyond the buffer range, which the hardware turns
-  // into zeros without a memory access, so every fetch is issued
+  // the current tile's raw words are consumed (K realigned into registers, V
+  // and the scales staged in LDS), so it is in flight during the scores,
+  // softmax and PV work of the current tile.  A tile past the end of the
+  // split is fetched at an offset beyond the buffer range, which the hardware
+  // turns into zeros without a memory access, so every fetch is issued
   // unconditionally and the wait counts stay exact.
   // (fp16 tensors: a lane fetches its token's 32 dims, 64 aligned bytes, as 4
   // 16-byte loads; no scale.)
@@ -112,6 +205,15 @@ __global__ __launch_bounds__(128) void decode_split_kernel(DecodeArgs a) {
   // (q8_0 K: a lane's 8 codes of each of the token's 4 blocks, 10 words;
   // q8_0 V: the lane's block -- scale and 32 codes -- in 9 words; the K
   // scales come two per lane.)
+  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : VF == kFmtQ8 ? 2 : 1;
+  struct Raw {
+    u32x4 k4[kBlk * kKW], v4[kBlk * kVW];
+    uint32_t k1[kBlk], v1[kBlk];
+    u32x3 kq3[KF == kFmtQ8 ? 2 * kBlk : 1];
+    u32x2 kq2[KF == kFmtQ8 ? 2 * kBlk : 1];
+    uint16_t sk, sv;
+    uint16_t skq[2];
+  };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
   const uint32_t shift = lane_off & 3u;   // (2 col + 2) mod 4: the same for TBQ3
   // word-aligned start of this lane's code bytes of tile t, block blk
@@ -119,578 +221,404 @@ __global__ __launch_bounds__(128) void decode_split_kernel(DecodeArgs a) {
     if (!live) return 0xFFFF0000u;
     return ((uint32_t)(t * kTile + 16 * blk + col) * bb + 2u + per_quarter * quarter) & ~3u;
   };
-  // a workgroup barrier (both wavefronts), and a wavefront-local one that
-  // orders this wavefront's LDS stores before its loads of them
-  auto wg_barrier = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  auto fetch = [&](Raw &r, int t) {
+    const bool live = t < t_end;
+    const uint32_t base = live ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
+#pragma unroll
+    for (int blk = 0; blk < kBlk; ++blk) {
+      const uint32_t a = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
+      if constexpr (KF == kFmtTbq4) {
+        r.k4[blk] = buf_load_x4(rk, a);
+        r.k1[blk] = buf_load_x1(rk, a + 16);
+      } else if constexpr (KF == kFmtTbq3) {
+        r.k4[blk] = buf_load_x4(rk, code_addr(live, t, blk, kBlockBytes3, 12u));
+      } else if constexpr (KF == kFmtQ8) {
+        // codes 8 q .. 8 q + 7 of block c start at byte 34 c + 2 + 8 q of
+        // the token (token rows are 8-byte aligned): 2 bytes into a word for
+        // even c, word-aligned for odd c
+        const uint32_t tb =
+            live ? (uint32_t)(t * kTile + 16 * blk + col) * kQ8RowBytes + 8u * quarter : 0xFFFF0000u;
+        r.kq3[2 * blk] = buf_load_x3(rk, tb);
+        r.kq2[2 * blk] = buf_load_x2(rk, tb + 36);
+        r.kq3[2 * blk + 1] = buf_load_x3(rk, tb + 68);
+        r.kq2[2 * blk + 1] = buf_load_x2(rk, tb + 104);
+      } else {
+        const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kKBytes + 64u * quarter)
+                                : 0xFFFF0000u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.k4[4 * blk + c] = buf_load_x4(rk, f + 16u * c);
+      }
+      if constexpr (VF == kFmtTbq4) {
+        r.v4[blk] = buf_load_x4(rv, a);
+        r.v1[blk] = buf_load_x1(rv, a + 16);
+      } else if constexpr (VF == kFmtTbq3) {
+        r.v4[blk] = buf_load_x4(rv, code_addr(live, t, blk, kBlockBytes3, 12u));
+      } else if constexpr (VF == kFmtQ8) {
+        const uint32_t vb =
+            live ? ((uint32_t)(t * kTile + 16 * blk + col) * kQ8RowBytes + 34u * quarter) & ~3u
+                 : 0xFFFF0000u;
+        r.v4[2 * blk] = buf_load_x4(rv, vb);
+        r.v4[2 * blk + 1] = buf_load_x4(rv, vb + 16);
+        r.v1[blk] = buf_load_x1(rv, vb + 32);
+      } else {
+        const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kVBytes + 64u * quarter)
+                                : 0xFFFF0000u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.v4[4 * blk + c] = buf_load_x4(rv, f + 16u * c);
+      }
+    }
+    const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
+    const uint32_t soff3 = lane < kTile && live ? (uint32_t)(t * kTile + lane) * kBlockBytes3 : 0xFFFF0000u;
+    if constexpr (KF == kFmtTbq4) r.sk = buf_load_u16(rk, soff);
+    if constexpr (KF == kFmtTbq3) r.sk = buf_load_u16(rk, soff3);
+    if constexpr (VF == kFmtTbq4) r.sv = buf_load_u16(rv, soff);
+    if constexpr (VF == kFmtTbq3) r.sv = buf_load_u16(rv, soff3);
+    if constexpr (KF == kFmtQ8) {   // lane: token lane % 32, blocks 2 (lane / 32) + 0, 1
+      const uint32_t so = live ? (uint32_t)(t * kTile + (lane & 31)) * kQ8RowBytes + 68u * (lane >> 5)
+                               : 0xFFFF0000u;
+      r.skq[0] = buf_load_u16(rk, so);
+      r.skq[1] = buf_load_u16(rk, so + 34);
+    }
   };
-  auto wave_sync = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
 
-  // The two wavefronts of the workgroup split each tile's work: wavefront 0
-  // streams K (scores, online softmax) and leaves each tile's probabilities
-  // and rescale factors in pbuf / abuf / fbuf[t & 1]; wavefront 1 streams and
-  // stages V and, after the tile's barrier, forms P~ and accumulates P~ V.
-  // Both run one workgroup barrier per tile, so they stay one phase apart at
-  // most: the V wavefront's P~ V of tile t overlaps the K wavefront's scores
-  // of tile t + 1.  (A buffer is rewritten two barriers after it was read.)
-  if (wave == 0) {
-    // ================================ K wavefront
-    // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
-    // fp16 K cache), split into fp16 hi + residual
-    float qv[32];
-    {
-      // lane quarter q holds dims 32 q + i; for a q8_0 K cache dims
-      // 32 (i/8) + 8 q + i%8 instead, so that MFMA step c spans q8_0 block c
-      const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim;
-      const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
+  // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
+  // context); full tiles carry no masking code at all
+  auto process = [&](Raw &r, int t, auto partial_tag) {
+    constexpr bool kPartial = decltype(partial_tag)::value;
+    const int tok0 = t * kTile;
+    // K words taken out of the fetch registers before the refill: TBQ4 code
+    // words realigned (converted to fp16 operands at the MFMA), or fp16 rows
+    uint32_t kw[kBlk][4];
+    u32x4 kf[KF == kFmtF16 ? kBlk * 4 : 1];
+    uint32_t kq[KF == kFmtQ8 ? kBlk : 1][8];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int d = KF == kFmtQ8 ? 32 * (i >> 3) + 8 * quarter + (i & 7) : 32 * quarter + i;
-        float x = head < G ? load_q<QT>(qp + d) : 0.0f;
-        qv[i] = ((sw >> i) & 1u) ? -x : x;
-      }
-      if constexpr (kKRot) {
+    for (int blk = 0; blk < kBlk; ++blk) {
+      if constexpr (KF == kFmtTbq4) {
+        const u32x4 w = r.k4[blk];
+        kw[blk][0] = alignbyte(w[1], w[0], shift);
+        kw[blk][1] = alignbyte(w[2], w[1], shift);
+        kw[blk][2] = alignbyte(w[3], w[2], shift);
+        kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+      } else if constexpr (KF == kFmtTbq3) {
+        const u32x4 w = r.k4[blk];       // 96 code bits of the lane's 32 dims
+        kw[blk][0] = alignbyte(w[1], w[0], shift);
+        kw[blk][1] = alignbyte(w[2], w[1], shift);
+        kw[blk][2] = alignbyte(w[3], w[2], shift);
+      } else if constexpr (KF == kFmtQ8) {
+        const u32x3 a0 = r.kq3[2 * blk], a2 = r.kq3[2 * blk + 1];
+        const u32x2 a1 = r.kq2[2 * blk], a3 = r.kq2[2 * blk + 1];
+        kq[blk][0] = alignbyte(a0[1], a0[0], 2u);
+        kq[blk][1] = alignbyte(a0[2], a0[1], 2u);
+        kq[blk][2] = a1[0];
+        kq[blk][3] = a1[1];
+        kq[blk][4] = alignbyte(a2[1], a2[0], 2u);
+        kq[blk][5] = alignbyte(a2[2], a2[1], 2u);
+        kq[blk][6] = a3[0];
+        kq[blk][7] = a3[1];
+      } else {
+        // fp16 slots >= n_ctx may hold anything: zero them (a NaN value would
+        // survive the -inf mask)
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;
 #pragma unroll
-      for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          if ((i & h) == 0) {
-            const float x = qv[i], y = qv[i + h];
-            qv[i] = x + y;
-            qv[i + h] = x - y;
-          }
-        }
-      }
-#pragma unroll
-      for (int h = 16; h <= 32; h <<= 1) {   // dims 32 and 64 apart: lanes 16 / 32 apart
-        const bool upper = (lane & h) != 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float o = __shfl_xor(qv[i], h, 64);
-          qv[i] = upper ? (o - qv[i]) : (qv[i] + o);
-        }
-      }
+        for (int c = 0; c < 4; ++c) kf[4 * blk + c] = dead ? u32x4{0u, 0u, 0u, 0u} : r.k4[4 * blk + c];
       }
     }
-    const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
-    float mx = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      qv[i] *= f;
-      mx = fmaxf(mx, fabsf(qv[i]));
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    // one power-of-two normalisation for the whole group: max |q'| in
-    // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
-    // range, and 2^-ex folds into the per-token key scale
-    int ex = 0;
-    if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
-    ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
-    const float qs_inv = ldexpf(1.0f, -ex);
-    half8 qop[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int el = 0; el < 8; ++el) {
-        // TBQ4 K operands hold the 4 even then the 4 odd dims of a code word;
-        // fp16, TBQ3 and q8_0 K operands hold 8 consecutive dims
-        const int i = KF == kFmtTbq4 ? 8 * c + (el < 4 ? 2 * el : 2 * el - 7) : 8 * c + el;
-        const float x = ldexpf(qv[i], ex);
-        const _Float16 hi = (_Float16)x;
-        const _Float16 lo = (_Float16)(x - (float)hi);
-        qop[c][el] = lo_part ? lo : hi;
-      }
-    }
-
-
-    const rsrc_t rk = make_rsrc(a.k + row * kKBytes, (uint32_t)a.capacity * kKBytes);
-    struct RawK {
-      u32x4 k4[kBlk * (KF == kFmtF16 ? 4 : 1)];
-      uint32_t k1[kBlk];
-      u32x3 kq3[KF == kFmtQ8 ? 2 * kBlk : 1];
-      u32x2 kq2[KF == kFmtQ8 ? 2 * kBlk : 1];
-      uint16_t sk;
-      uint16_t skq[2];
-    };
-    auto fetch = [&](RawK &r, int t) {
-      const bool live = t < t_end;
-      const uint32_t base = live ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
-#pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk) {
-        const uint32_t ad = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
-        if constexpr (KF == kFmtTbq4) {
-          r.k4[blk] = buf_load_x4(rk, ad);
-          r.k1[blk] = buf_load_x1(rk, ad + 16);
-        } else if constexpr (KF == kFmtTbq3) {
-          r.k4[blk] = buf_load_x4(rk, code_addr(live, t, blk, kBlockBytes3, 12u));
-        } else if constexpr (KF == kFmtQ8) {
-          // codes 8 q .. 8 q + 7 of block c start at byte 34 c + 2 + 8 q of
-          // the token (token rows are 8-byte aligned): 2 bytes into a word for
-          // even c, word-aligned for odd c
-          const uint32_t tb =
-              live ? (uint32_t)(t * kTile + 16 * blk + col) * kQ8RowBytes + 8u * quarter : 0xFFFF0000u;
-          r.kq3[2 * blk] = buf_load_x3(rk, tb);
-          r.kq2[2 * blk] = buf_load_x2(rk, tb + 36);
-          r.kq3[2 * blk + 1] = buf_load_x3(rk, tb + 68);
-          r.kq2[2 * blk + 1] = buf_load_x2(rk, tb + 104);
-        } else {
-          const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kKBytes + 64u * quarter)
-                                  : 0xFFFF0000u;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) r.k4[4 * blk + c] = buf_load_x4(rk, f + 16u * c);
-        }
-      }
-      if constexpr (KF == kFmtTbq4)
-        r.sk = buf_load_u16(rk, lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u);
-      if constexpr (KF == kFmtTbq3)
-        r.sk = buf_load_u16(rk, lane < kTile && live ? (uint32_t)(t * kTile + lane) * kBlockBytes3
-                                                     : 0xFFFF0000u);
-      if constexpr (KF == kFmtQ8) {   // lane: token lane % 32, blocks 2 (lane / 32) + 0, 1
-        const uint32_t so = live ? (uint32_t)(t * kTile + (lane & 31)) * kQ8RowBytes + 68u * (lane >> 5)
-                                 : 0xFFFF0000u;
-        r.skq[0] = buf_load_u16(rk, so);
-        r.skq[1] = buf_load_u16(rk, so + 34);
-      }
+    auto k_operand = [&](int blk, int c) -> half8 {
+      if constexpr (KF == kFmtTbq4) return word_to_half8(kw[blk][c]);
+      else if constexpr (KF == kFmtTbq3)
+        return tbq3_chunk_to_half8(tbq3_chunk(kw[blk][0], kw[blk][1], kw[blk][2], c));
+      else if constexpr (KF == kFmtQ8) return i8x8_to_half8(kq[blk][2 * c], kq[blk][2 * c + 1]);
+      else return __builtin_bit_cast(half8, kf[4 * blk + c]);
     };
 
-    float m_run = -INFINITY, l_run = 0.0f;
-    RawK r;
-    fetch(r, t_begin);
-    // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
-    // context); full tiles carry no masking code at all
-    auto process = [&](int t, auto partial_tag) {
-      constexpr bool kPartial = decltype(partial_tag)::value;
-      const int tok0 = t * kTile;
-      // K words taken out of the fetch registers before the refill: TBQ4 code
-      // words realigned (converted to fp16 operands at the MFMA), or fp16 rows
-      uint32_t kw[kBlk][4];
-      u32x4 kf[KF == kFmtF16 ? kBlk * 4 : 1];
-      uint32_t kq[KF == kFmtQ8 ? kBlk : 1][8];
+    __syncthreads();   // previous tile's LDS reads are done
 #pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk) {
-        if constexpr (KF == kFmtTbq4) {
-          const u32x4 w = r.k4[blk];
-          kw[blk][0] = alignbyte(w[1], w[0], shift);
-          kw[blk][1] = alignbyte(w[2], w[1], shift);
-          kw[blk][2] = alignbyte(w[3], w[2], shift);
-          kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
-        } else if constexpr (KF == kFmtTbq3) {
-          const u32x4 w = r.k4[blk];       // 96 code bits of the lane's 32 dims
-          kw[blk][0] = alignbyte(w[1], w[0], shift);
-          kw[blk][1] = alignbyte(w[2], w[1], shift);
-          kw[blk][2] = alignbyte(w[3], w[2], shift);
-        } else if constexpr (KF == kFmtQ8) {
-          const u32x3 a0 = r.kq3[2 * blk], a2 = r.kq3[2 * blk + 1];
-          const u32x2 a1 = r.kq2[2 * blk], a3 = r.kq2[2 * blk + 1];
-          kq[blk][0] = alignbyte(a0[1], a0[0], 2u);
-          kq[blk][1] = alignbyte(a0[2], a0[1], 2u);
-          kq[blk][2] = a1[0];
-          kq[blk][3] = a1[1];
-          kq[blk][4] = alignbyte(a2[1], a2[0], 2u);
-          kq[blk][5] = alignbyte(a2[2], a2[1], 2u);
-          kq[blk][6] = a3[0];
-          kq[blk][7] = a3[1];
-        } else {
-          // fp16 slots >= n_ctx may hold anything: zero them (a NaN value would
-          // survive the -inf mask)
-          const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;
+    for (int blk = 0; blk < kBlk; ++blk) {
+      if constexpr (VF == kFmtTbq4) {
+        const u32x4 w = r.v4[blk];
+        const u32x4 a = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
+                         alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
+        *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = a;
+      } else if constexpr (VF == kFmtTbq3) {
+        // the lane's 32 codes -> 32 e4m3 bytes (dims 32 quarter ..) in LDS
+        const u32x4 w = r.v4[blk];
+        const uint32_t w0 = alignbyte(w[1], w[0], shift), w1 = alignbyte(w[2], w[1], shift),
+                       w2 = alignbyte(w[3], w[2], shift);
+        uint32_t e[8];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) kf[4 * blk + c] = dead ? u32x4{0u, 0u, 0u, 0u} : r.k4[4 * blk + c];
-        }
+        for (int c = 0; c < 4; ++c) tbq3_chunk_to_e4m3(tbq3_chunk(w0, w1, w2, c), e[2 * c], e[2 * c + 1]);
+        uint8_t *row = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
+        *(u32x4 *)row = u32x4{e[0], e[1], e[2], e[3]};
+        *(u32x4 *)(row + 16) = u32x4{e[4], e[5], e[6], e[7]};
+      } else if constexpr (VF == kFmtQ8) {
+        // block `quarter` of the token: the scale then 32 codes, from byte
+        // 0 (even quarter: codes 2 bytes into the words) or byte 2 (odd
+        // quarter: codes from the second word on) of the fetched words
+        const u32x4 w0 = r.v4[2 * blk], w1 = r.v4[2 * blk + 1];
+        const uint32_t d[9] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], r.v1[blk]};
+        const bool odd = (quarter & 1) != 0;
+        uint32_t cw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cw[j] = odd ? d[j + 1] : alignbyte(d[j + 1], d[j], 2u);
+        uint8_t *row = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
+        *(u32x4 *)row = u32x4{cw[0], cw[1], cw[2], cw[3]};
+        *(u32x4 *)(row + 16) = u32x4{cw[4], cw[5], cw[6], cw[7]};
+        const uint16_t sbits = (uint16_t)(odd ? d[0] >> 16 : d[0] & 0xFFFFu);
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;   // (NaN guard)
+        svq[quarter * kTile + 16 * blk + col] = dead ? 0.0f : half_bits_to_float(sbits);
+      } else {
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_ctx;   // (as for K)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *(u32x4 *)(vlds + (16 * blk + col) * kF16Row + 64 * quarter + 16 * c) =
+              dead ? u32x4{0u, 0u, 0u, 0u} : r.v4[4 * blk + c];
       }
-      auto k_operand = [&](int blk, int c) -> half8 {
-        if constexpr (KF == kFmtTbq4) return word_to_half8(kw[blk][c]);
-        else if constexpr (KF == kFmtTbq3)
-          return tbq3_chunk_to_half8(tbq3_chunk(kw[blk][0], kw[blk][1], kw[blk][2], c));
-        else if constexpr (KF == kFmtQ8) return i8x8_to_half8(kq[blk][2 * c], kq[blk][2 * c + 1]);
-        else return __builtin_bit_cast(half8, kf[4 * blk + c]);
-      };
-      if (lane < kTile) {
-        float dk = qs_inv;   // (q8_0: per-block scales below)
-        if constexpr (KF == kFmtTbq4 || KF == kFmtTbq3) dk = half_bits_to_float(r.sk) * qs_inv;
-        if constexpr (KF == kFmtQ8) dk = 1.0f;
-        if constexpr (kPartial) {
-          // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
-          if (tok0 + lane >= n_ctx) dk = 0.0f;
-        }
-        sk[lane] = dk;
+    }
+    if (lane < kTile) {
+      float dk = qs_inv, dv = 1.0f;   // (q8_0: per-block scales below)
+      if constexpr (KF == kFmtTbq4 || KF == kFmtTbq3) dk = half_bits_to_float(r.sk) * qs_inv;
+      if constexpr (KF == kFmtQ8) dk = 1.0f;
+      if constexpr (VF == kFmtTbq4 || VF == kFmtTbq3) dv = half_bits_to_float(r.sv);
+      if constexpr (kPartial) {
+        // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
+        if (tok0 + lane >= n_ctx) dk = dv = 0.0f;
       }
-      if constexpr (KF == kFmtQ8) {
-        const int tk = lane & 31, c0 = 2 * (lane >> 5);
-        const bool dead = kPartial && tok0 + tk >= n_ctx;
-        skq[c0 * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[0]) * qs_inv;
-        skq[(c0 + 1) * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[1]) * qs_inv;
-      }
-      fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
+      sk[lane] = dk;
+      sv[lane] = dv;
+    }
+    if constexpr (KF == kFmtQ8) {
+      const int tk = lane & 31, c0 = 2 * (lane >> 5);
+      const bool dead = kPartial && tok0 + tk >= n_ctx;
+      skq[c0 * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[0]) * qs_inv;
+      skq[(c0 + 1) * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[1]) * qs_inv;
+    }
+    fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
 
-      // ---- scores S^T[token][col] = K . q'.  The fp16 high-part (columns
-      // 0-7) and residual (columns 8-15) partial sums of a head are added by a
-      // 16-lane rotation, and the two 16-token blocks share the work: lanes
-      // 0-7 of each row finish block 0, lanes 8-15 block 1, so every lane
-      // carries 4 distinct scores (head `head`, tokens 16 * own + 4 * quarter + e).
-      // (q8_0 K: step c spans block c, whose scale differs per token, so each
-      // step has its own accumulator and the scales are applied in fp32.)
-      float4v acc[kBlk];
-      float4v acq[KF == kFmtQ8 ? kBlk : 1][4];
+    // ---- scores S^T[token][col] = K . q'.  The fp16 high-part (columns
+    // 0-7) and residual (columns 8-15) partial sums of a head are added by a
+    // 16-lane rotation, and the two 16-token blocks share the work: lanes
+    // 0-7 of each row finish block 0, lanes 8-15 block 1, so every lane
+    // carries 4 distinct scores (head `head`, tokens 16 * own + 4 * quarter + e).
+    // (q8_0 K: step c spans block c, whose scale differs per token, so each
+    // step has its own accumulator and the scales are applied in fp32.)
+    float4v acc[kBlk];
+    float4v acq[KF == kFmtQ8 ? kBlk : 1][4];
 #pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk) {
-        acc[blk] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < kBlk; ++blk) {
+      acc[blk] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (KF == kFmtQ8)
+          acq[blk][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c],
+                                                               float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        else
+          acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c], acc[blk],
+                                                            0, 0, 0);
+      }
+    }
+    __syncthreads();   // staged V rows and scales are visible
+    if constexpr (KF == kFmtQ8) {
+#pragma unroll
+      for (int blk = 0; blk < kBlk; ++blk)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if constexpr (KF == kFmtQ8)
-            acq[blk][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c],
-                                                                 float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          else
-            acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(blk, c), qop[c], acc[blk],
-                                                              0, 0, 0);
+          const float4v kd4 = *(const float4v *)(skq + c * kTile + 16 * blk + 4 * quarter);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[blk][e] = fmaf(kd4[e], acq[blk][c][e], acc[blk][e]);
         }
-      }
-      wave_sync();   // the staged K scales are visible
-      if constexpr (KF == kFmtQ8) {
-#pragma unroll
-        for (int blk = 0; blk < kBlk; ++blk)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float4v kd4 = *(const float4v *)(skq + c * kTile + 16 * blk + 4 * quarter);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[blk][e] = fmaf(kd4[e], acq[blk][c][e], acc[blk][e]);
-          }
-      }
-      float sc[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float mine = lo_part ? acc[1][e] : acc[0][e];
-        const float give = lo_part ? acc[0][e] : acc[1][e];   // what the partner lane needs
-        sc[e] = mine + row_ror8(give);
-      }
-
-      // t = score - m_ref with the running max updated lazily: m_ref is the
-      // running max (0 before the first tile), and only a tile holding a score
-      // above it -- and the first tile -- takes the rescaling path, which
-      // recovers the scores as t + m_ref.
-      const int own = lo_part ? 1 : 0;
-      const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
-      float t4[4];
-      float tmax = -INFINITY;
-      {
-        const float4v kd = *(const float4v *)(sk + 16 * own + 4 * quarter);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          t4[e] = fmaf(sc[e], kd[e], -m_ref);
-          tmax = fmaxf(tmax, t4[e]);
-        }
-      }
-      if constexpr (kPartial) {
-        tmax = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          t4[e] += (tok0 + 16 * own + 4 * quarter + e < n_ctx) ? 0.0f : -INFINITY;
-          tmax = fmaxf(tmax, t4[e]);
-        }
-      }
-      const int buf = t & 1;
-      int flag = 0;
-      if (__any(tmax > 0.0f || m_run == -INFINITY)) {
-        float smax = tmax + m_ref;
-        smax = fmaxf(smax, __shfl_xor(smax, 8, 64));
-        smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
-        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-        const float m_new = fmaxf(m_run, smax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        if (lane < 8) abuf[buf][lane] = alpha;   // the V wavefront rescales O' by it
-        flag = 1;
-        const float shift_t = m_ref - m_new;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t4[e] += shift_t;
-      }
-      float4v p4;
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p4[e] = __builtin_amdgcn_exp2f(t4[e]);
-        psum += p4[e];
-      }
-      l_run += psum;
-      pbuf[buf][lane] = p4;
-      if (lane == 0) fbuf[buf] = flag;
-      wg_barrier();   // tile t's probabilities are handed over
-    };
-    int t = t_begin;
-    for (; t < t_full; ++t) process(t, std::false_type{});
-    for (; t < t_end; ++t) process(t, std::true_type{});
-
-    // ---------------- this split's (m, l) per query head
-    l_run += __shfl_xor(l_run, 8, 64);
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    if (lane < G) {
-      wsb[(size_t)lane * P * 130 + 0] = m_run;
-      wsb[(size_t)lane * P * 130 + 1] = l_run;
     }
-  } else {
-    // ================================ V wavefront
-    // lanes of P~ rows 8-15 read zero V scales
-    const float *sv_rd = lo_part ? sv + kTile : sv;
-    if (lane < 32) sv[kTile + lane] = 0.0f;
+    float sc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mine = lo_part ? acc[1][e] : acc[0][e];
+      const float give = lo_part ? acc[0][e] : acc[1][e];   // what the partner lane needs
+      sc[e] = mine + row_ror8(give);
+    }
+
+    // t = score - m_ref with the running max updated lazily: m_ref is the
+    // running max (0 before the first tile), and only a tile holding a score
+    // above it -- and the first tile -- takes the rescaling path, which
+    // recovers the scores as t + m_ref.
+    const int own = lo_part ? 1 : 0;
+    const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
+    float t4[4];
+    float tmax = -INFINITY;
+    {
+      const float4v kd = *(const float4v *)(sk + 16 * own + 4 * quarter);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t4[e] = fmaf(sc[e], kd[e], -m_ref);
+        tmax = fmaxf(tmax, t4[e]);
+      }
+    }
+    if constexpr (kPartial) {
+      tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t4[e] += (tok0 + 16 * own + 4 * quarter + e < n_ctx) ? 0.0f : -INFINITY;
+        tmax = fmaxf(tmax, t4[e]);
+      }
+    }
+    if (__any(tmax > 0.0f || m_run == -INFINITY)) {
+      float smax = tmax + m_ref;
+      smax = fmaxf(smax, __shfl_xor(smax, 8, 64));
+      smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+      const float m_new = fmaxf(m_run, smax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      float al[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, (4 * quarter + e) & 7, 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[i][e] *= al[e];
+      const float shift_t = m_ref - m_new;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t4[e] += shift_t;
+    }
+
+    // ---- probabilities and P~ = p d^V in fp16.  P~ rows 0-7 (lanes 0-7 of
+    // each row) hold the heads; rows 8-15 are zero (their lanes read the V
+    // scales from a zero block).  A row needs both blocks' tokens: its own
+    // block from itself, the other from the partner lane.
+    float psum = 0.0f;
+    float p4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p4[e] = __builtin_amdgcn_exp2f(t4[e]);
+      psum += p4[e];
+    }
+    l_run += psum;
+    const float4v vd0 = *(const float4v *)(sv_rd + 4 * quarter);        // block 0
+    const float4v vd1 = *(const float4v *)(sv_rd + 16 + 4 * quarter);   // block 1
+    float pt[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pt[e] = p4[e] * vd0[e];                 // lanes 0-7: own block 0
+      pt[4 + e] = row_ror8(p4[e]) * vd1[e];   // partner's block 1
+    }
+    uint32_t pw[4];   // round to nearest (v_cvt_pk_f16_f32): no truncation bias
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
+    half8 pa[kBlk / 2];
+    pa[0] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    // q8_0 V: one P~ per 32-dim block c, p times that block's scale
+    half8 paq[VF == kFmtQ8 ? 4 : 1];
     if constexpr (VF == kFmtQ8) {
-      if (lane < 32) svq[4 * kTile + lane] = 0.0f;
-    }
-    float4v o[8];
+      float pr[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = float4v{0.f, 0.f, 0.f, 0.f};
-
-    // transposed-read source address (fixed per lane): lane s of 16-lane group
-    // G4 points at token tau(G4, s/2), byte 8*(s&1) of a 16-byte column group
-    int tr_off;
-    {
-      const int e = col >> 1;
-      const int tok = 16 * (e >> 2) + 4 * quarter + (e & 3);
-      tr_off = tok * kVRow + 8 * (col & 1);
-    }
-    const int tr16_off = (4 * quarter + (col >> 2)) * kF16Row + 8 * (col & 3);
-    // TBQ3 V (e4m3 rows): source lane s of a 16-lane group points at the
-    // token of P~ operand position 8 quarter + s/2 and bytes 8 (s & 1) .. + 7
-    // of a 16-dim block, so a byte-transposed read gives a lane 8 tokens of
-    // dim 16 db + col
-    int tr8_3_off;
-    {
-      const int j = col >> 1;
-      const int tok = j < 4 ? 4 * quarter + j : 16 + 4 * quarter + (j - 4);
-      tr8_3_off = tok * kE4Row + 8 * (col & 1);
-    }
-
-    const rsrc_t rv = make_rsrc(a.v + row * kVBytes, (uint32_t)a.capacity * kVBytes);
-    constexpr int kVW = VF == kFmtF16 ? 4 : VF == kFmtQ8 ? 2 : 1;
-    struct RawV {
-      u32x4 v4[kBlk * kVW];
-      uint32_t v1[kBlk];
-      uint16_t sv;
-    };
-    auto fetch = [&](RawV &r, int t) {
-      const bool live = t < t_end;
-      const uint32_t base = live ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
+      for (int e = 0; e < 4; ++e) pr[e] = row_ror8(p4[e]);
 #pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk) {
-        const uint32_t ad = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
-        if constexpr (VF == kFmtTbq4) {
-          r.v4[blk] = buf_load_x4(rv, ad);
-          r.v1[blk] = buf_load_x1(rv, ad + 16);
-        } else if constexpr (VF == kFmtTbq3) {
-          r.v4[blk] = buf_load_x4(rv, code_addr(live, t, blk, kBlockBytes3, 12u));
-        } else if constexpr (VF == kFmtQ8) {
-          const uint32_t vb =
-              live ? ((uint32_t)(t * kTile + 16 * blk + col) * kQ8RowBytes + 34u * quarter) & ~3u
-                   : 0xFFFF0000u;
-          r.v4[2 * blk] = buf_load_x4(rv, vb);
-          r.v4[2 * blk + 1] = buf_load_x4(rv, vb + 16);
-          r.v1[blk] = buf_load_x1(rv, vb + 32);
-        } else {
-          const uint32_t f = live ? ((uint32_t)(t * kTile + 16 * blk + col) * kVBytes + 64u * quarter)
-                                  : 0xFFFF0000u;
+      for (int c = 0; c < 4; ++c) {
+        const float *svc = lo_part ? svq + 4 * kTile : svq + c * kTile;
+        const float4v q0 = *(const float4v *)(svc + 4 * quarter);
+        const float4v q1 = *(const float4v *)(svc + 16 + 4 * quarter);
+        uint32_t qw[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) r.v4[4 * blk + c] = buf_load_x4(rv, f + 16u * c);
+        for (int j = 0; j < 2; ++j) {
+          qw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(p4[2 * j] * q0[2 * j]),
+                                                      (_Float16)(p4[2 * j + 1] * q0[2 * j + 1])});
+          qw[2 + j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(pr[2 * j] * q1[2 * j]),
+                                                          (_Float16)(pr[2 * j + 1] * q1[2 * j + 1])});
         }
+        paq[c] = __builtin_bit_cast(half8, u32x4{qw[0], qw[1], qw[2], qw[3]});
       }
-      if constexpr (VF == kFmtTbq4)
-        r.sv = buf_load_u16(rv, lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u);
-      if constexpr (VF == kFmtTbq3)
-        r.sv = buf_load_u16(rv, lane < kTile && live ? (uint32_t)(t * kTile + lane) * kBlockBytes3
-                                                     : 0xFFFF0000u);
-    };
+    }
 
-    RawV r;
-    fetch(r, t_begin);
-    for (int t = t_begin; t < t_end; ++t) {
-      const int tok0 = t * kTile;
-      const bool partial = t >= t_full;
-      // ---- stage the tile's V rows (and scales) in LDS
+    // ---- O'^T += P~ V
+    if constexpr (VF == kFmtTbq4) {
+      // V read back transposed: 8 tokens x 1 byte (2 dims) per lane
 #pragma unroll
-      for (int blk = 0; blk < kBlk; ++blk) {
-        if constexpr (VF == kFmtTbq4) {
-          const u32x4 w = r.v4[blk];
-          const u32x4 av = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
-                            alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
-          *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = av;
-        } else if constexpr (VF == kFmtTbq3) {
-          // the lane's 32 codes -> 32 e4m3 bytes (dims 32 quarter ..) in LDS
-          const u32x4 w = r.v4[blk];
-          const uint32_t w0 = alignbyte(w[1], w[0], shift), w1 = alignbyte(w[2], w[1], shift),
-                         w2 = alignbyte(w[3], w[2], shift);
-          uint32_t e[8];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) tbq3_chunk_to_e4m3(tbq3_chunk(w0, w1, w2, c), e[2 * c], e[2 * c + 1]);
-          uint8_t *rowp = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
-          *(u32x4 *)rowp = u32x4{e[0], e[1], e[2], e[3]};
-          *(u32x4 *)(rowp + 16) = u32x4{e[4], e[5], e[6], e[7]};
-        } else if constexpr (VF == kFmtQ8) {
-          // block `quarter` of the token: the scale then 32 codes, from byte
-          // 0 (even quarter: codes 2 bytes into the words) or byte 2 (odd
-          // quarter: codes from the second word on) of the fetched words
-          const u32x4 w0 = r.v4[2 * blk], w1 = r.v4[2 * blk + 1];
-          const uint32_t d[9] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], r.v1[blk]};
-          const bool odd = (quarter & 1) != 0;
-          uint32_t cw[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) cw[j] = odd ? d[j + 1] : alignbyte(d[j + 1], d[j], 2u);
-          uint8_t *rowp = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
-          *(u32x4 *)rowp = u32x4{cw[0], cw[1], cw[2], cw[3]};
-          *(u32x4 *)(rowp + 16) = u32x4{cw[4], cw[5], cw[6], cw[7]};
-          const uint16_t sbits = (uint16_t)(odd ? d[0] >> 16 : d[0] & 0xFFFFu);
-          const bool dead = partial && tok0 + 16 * blk + col >= n_ctx;   // (NaN guard)
-          svq[quarter * kTile + 16 * blk + col] = dead ? 0.0f : half_bits_to_float(sbits);
-        } else {
-          // fp16 slots >= n_ctx may hold anything: zero them
-          const bool dead = partial && tok0 + 16 * blk + col >= n_ctx;
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            *(u32x4 *)(vlds + (16 * blk + col) * kF16Row + 64 * quarter + 16 * c) =
-                dead ? u32x4{0u, 0u, 0u, 0u} : r.v4[4 * blk + c];
-        }
-      }
-      if (lane < kTile) {
-        float dv = 1.0f;   // (q8_0: per-block scales above)
-        if constexpr (VF == kFmtTbq4 || VF == kFmtTbq3) dv = half_bits_to_float(r.sv);
-        // slots >= n_ctx may hold anything (a NaN scale would survive p = 0)
-        if (partial && tok0 + lane >= n_ctx) dv = 0.0f;
-        sv[lane] = dv;
-      }
-      fetch(r, t + 1);   // the raw words are consumed: refill with the next tile
-      wave_sync();       // the staged rows and scales are visible
-
-      // ---- V operands (read back transposed and converted) before the
-      // hand-over; MFMA j of the PV step takes vop[j] into O' block j
-      half8 vop[8];
-      if constexpr (VF == kFmtTbq4) {
-        // V read back transposed: 8 tokens x 1 byte (2 dims) per lane
+      for (int kk = 0; kk < kBlk / 2; ++kk) {
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
           typedef __attribute__((address_space(3))) int2v lds_i2;
-          const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr_off + 16 * cg));
-          const uint32_t w0 = (uint32_t)rr[0], w1 = (uint32_t)rr[1];
-          vop[2 * cg] = lo_nibbles_to_half8(w0, w1);
-          vop[2 * cg + 1] = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
-        }
-      } else if constexpr (VF == kFmtQ8) {
-        // q8_0 V staged as int8 codes: one byte-transposed read per 16 dims
-        // (dims 16 db .. lie in block db / 2)
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          typedef __attribute__((address_space(3))) int2v lds_i2;
-          const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
-          vop[db] = i8x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]);
-        }
-      } else if constexpr (VF == kFmtTbq3) {
-        // TBQ3 V staged as e4m3 bytes: one byte-transposed read per 16 dims
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          typedef __attribute__((address_space(3))) int2v lds_i2;
-          const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
-          vop[db] = e4m3x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]);
-        }
-      } else {
-        // fp16 V: two 16-bit transposed reads give a lane 8 tokens of one dim
-        // (dim 16 db + col); source lanes point at token 4 quarter + col / 4
-        // (+ 16 for the second read) and dims 4 (col % 4) .. + 3 of the block
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          typedef __attribute__((address_space(3))) short4v lds_s4;
-          const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vlds + tr16_off + 32 * db));
-          const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s4 *)(vlds + tr16_off + 16 * kF16Row + 32 * db));
-          const short8v vv = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-          vop[db] = __builtin_bit_cast(half8, vv);
+          const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i2 *)(vlds + tr_off + 32 * kk * kVRow + 16 * cg));
+          const uint32_t w0 = (uint32_t)r[0], w1 = (uint32_t)r[1];
+          const half8 ve = lo_nibbles_to_half8(w0, w1);
+          const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
+          o[2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], ve, o[2 * cg], 0, 0, 0);
+          o[2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[kk], vo, o[2 * cg + 1], 0, 0, 0);
         }
       }
-      const float4v vd0 = *(const float4v *)(sv_rd + 4 * quarter);        // block 0
-      const float4v vd1 = *(const float4v *)(sv_rd + 16 + 4 * quarter);   // block 1
-
-      wg_barrier();   // tile t's probabilities are in pbuf / abuf / fbuf[t & 1]
-      const int buf = t & 1;
-      if (fbuf[buf]) {   // the running max moved: O' *= 2^(m_old - m_new) per head
-        float al[4];
+    } else if constexpr (VF == kFmtQ8) {
+      // q8_0 V staged as int8 codes: one byte-transposed read per 16 dims
+      // (dims 16 db .. lie in block db / 2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) al[e] = abuf[buf][(4 * quarter + e) & 7];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[i][e] *= al[e];
+      for (int db = 0; db < 8; ++db) {
+        typedef __attribute__((address_space(3))) int2v lds_i2;
+        const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            paq[db >> 1], i8x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]), o[db], 0, 0, 0);
       }
-
-      // ---- P~ = p d^V in fp16.  P~ rows 0-7 (lanes 0-7 of each row) hold
-      // the heads; rows 8-15 are zero (their lanes read the V scales from a
-      // zero block).  A row needs both blocks' tokens: its own block from its
-      // own lane, the other from the partner lane (col ^ 8).
-      const float4v p4 = pbuf[buf][lane];
-      const float4v pp = pbuf[buf][lane ^ 8];
-      float pt[8];
+    } else if constexpr (VF == kFmtTbq3) {
+      // TBQ3 V staged as e4m3 bytes: one byte-transposed read per 16 dims
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pt[e] = p4[e] * vd0[e];         // lanes 0-7: own block 0
-        pt[4 + e] = pp[e] * vd1[e];     // partner's block 1
+      for (int db = 0; db < 8; ++db) {
+        typedef __attribute__((address_space(3))) int2v lds_i2;
+        const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            pa[0], e4m3x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]), o[db], 0, 0, 0);
       }
-      uint32_t pw[4];   // round to nearest (v_cvt_pk_f16_f32): no truncation bias
+    } else {
+      // fp16 V: two 16-bit transposed reads give a lane 8 tokens of one dim
+      // (dim 16 db + col); source lanes point at token 4 quarter + col / 4
+      // (+ 16 for the second read) and dims 4 (col % 4) .. + 3 of the block
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
-      const half8 pa = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      // q8_0 V: one P~ per 32-dim block c, p times that block's scale
-      half8 paq[VF == kFmtQ8 ? 4 : 1];
-      if constexpr (VF == kFmtQ8) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float *svc = lo_part ? svq + 4 * kTile : svq + c * kTile;
-          const float4v q0 = *(const float4v *)(svc + 4 * quarter);
-          const float4v q1 = *(const float4v *)(svc + 16 + 4 * quarter);
-          uint32_t qw[4];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            qw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(p4[2 * j] * q0[2 * j]),
-                                                        (_Float16)(p4[2 * j + 1] * q0[2 * j + 1])});
-            qw[2 + j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(pp[2 * j] * q1[2 * j]),
-                                                            (_Float16)(pp[2 * j + 1] * q1[2 * j + 1])});
-          }
-          paq[c] = __builtin_bit_cast(half8, u32x4{qw[0], qw[1], qw[2], qw[3]});
-        }
-      }
-
-      // ---- O'^T += P~ V
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const half8 pj = VF == kFmtQ8 ? paq[VF == kFmtQ8 ? j >> 1 : 0] : pa;
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pj, vop[j], o[j], 0, 0, 0);
+      for (int db = 0; db < 8; ++db) {
+        typedef __attribute__((address_space(3))) short4v lds_s4;
+        const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vlds + tr16_off + 32 * db));
+        const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4 *)(vlds + tr16_off + 16 * kF16Row + 32 * db));
+        const short8v vv = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0], __builtin_bit_cast(half8, vv), o[db],
+                                                       0, 0, 0);
       }
     }
+  };
 
-    // ---------------- this split's O' per query head
+  Raw r;
+  fetch(r, t_begin);
+  const int t_full = min(t_end, n_ctx / kTile);   // tiles below t_full are full
+  int t = t_begin;
+  for (; t < t_full; ++t) process(r, t, std::false_type{});
+  for (; t < t_end; ++t) process(r, t, std::true_type{});
+
+  // ---------------- partial state of this split
+  l_run += __shfl_xor(l_run, 8, 64);
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[i][e] += __shfl_xor(o[i][e], 32, 64);
-    if (lane < 32) {
+    for (int e = 0; e < 4; ++e) o[i][e] += __shfl_xor(o[i][e], 32, 64);
+
+  const int P = a.n_splits;
+  float *wsb = a.ws + ((size_t)b * a.n_q_heads + (size_t)g * G) * P * 130 + (size_t)split * 130;
+  if (lane < G) {
+    wsb[(size_t)lane * P * 130 + 0] = m_run;
+    wsb[(size_t)lane * P * 130 + 1] = l_run;
+  }
+  if (lane < 32) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = 4 * quarter + e;   // query head within the group
-        if (rr < G) {
-          float *dst = wsb + (size_t)rr * P * 130 + 2;
-          if constexpr (VF == kFmtTbq4) {
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * quarter + e;   // query head within the group
+      if (r < G) {
+        float *dst = wsb + (size_t)r * P * 130 + 2;
+        if constexpr (VF == kFmtTbq4) {
 #pragma unroll
-            for (int cg = 0; cg < 4; ++cg) {
-              dst[32 * cg + 2 * col] = o[2 * cg][e];
-              dst[32 * cg + 2 * col + 1] = o[2 * cg + 1][e];
-            }
-          } else {
-#pragma unroll
-            for (int db = 0; db < 8; ++db) dst[16 * db + col] = o[db][e];
+          for (int cg = 0; cg < 4; ++cg) {
+            dst[32 * cg + 2 * col] = o[2 * cg][e];
+            dst[32 * cg + 2 * col + 1] = o[2 * cg + 1][e];
           }
+        } else {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) dst[16 * db + col] = o[db][e];
         }
       }
     }
@@ -814,8 +742,8 @@ hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hi
   DecodeArgs arg = a;
   void *params[] = {&arg};
   if (start || stop)
-    return hipExtLaunchKernel(fn, grid, dim3(128), params, 0, stream, start, stop, 0);
-  return hipLaunchKernel(fn, grid, dim3(128), params, 0, stream);
+    return hipExtLaunchKernel(fn, grid, dim3(64), params, 0, stream, start, stop, 0);
+  return hipLaunchKernel(fn, grid, dim3(64), params, 0, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream) {
