@@ -14,7 +14,8 @@ queries on 131072 cached tokens, 8 KV / 64 query heads, append of the chunk's
 K/V then causal attention) is timed in the same run and reported under
 "prefill" in TFLOP/s (4 * 128 * 64 FLOPs per unmasked (query, key) pair).
 The same decode rows stored as TBQ3, q8_0 or fp16 K / V tensors (mixed
-formats) are timed under "formats" (one decode call per format pair, KV GB/s).
+formats) are timed under "formats" (one decode call per format pair, KV GB/s),
+and the prefill chunk over TBQ3 and fp16 caches under "prefill"."formats".
 
 Before the W warm-up steps, 60 untimed steps (~8 ms) let the clocks settle:
 the first milliseconds of sustained load run faster, then the clocks dip and
@@ -227,6 +228,8 @@ SETTLE_STEPS = 60
 # (K format, V format) pairs timed beside the TBQ4 cache on the same rows
 FORMAT_NAMES = {0: "tbq4", 1: "f16", 2: "tbq3", 3: "q8_0"}
 FORMATS = ((2, 2), (0, 2), (0, 1), (1, 0), (0, 3), (3, 0), (3, 3), (1, 1))
+# (K format, V format) pairs of the prefill chunk timed beside TBQ4
+PREFILL_FORMATS = ((2, 2), (1, 1))
 
 
 def bench_format(tb, torch, args, cache, q, out, ws, P, w):
@@ -351,7 +354,8 @@ def bench_prefill(tb, torch, args):
     w = WORKLOADS["prefill"]
     n_past, n_q, Hkv, Hq = w.n_ctx, w.n_q, w.n_kv_heads, w.n_q_heads
     cache = tb.KVCache(1, Hkv, n_past + n_q)
-    fill_cache(tb, torch, cache, w, 0, n_past)
+    rows = [] if args.formats else None
+    fill_cache(tb, torch, cache, w, 0, n_past, keep=rows)
     k_new = torch.from_numpy(kv_tensor(w, 0, K, n_past, n_past + n_q)).cuda()
     v_new = torch.from_numpy(kv_tensor(w, 0, V, n_past, n_past + n_q)).cuda()
     q = torch.from_numpy(q_prefill(w)).cuda()
@@ -381,6 +385,30 @@ def bench_prefill(tb, torch, args):
     pairs = sum(n_past + i + 1 for i in range(n_q))
     flops = 4 * 128 * Hq * pairs
     assert torch.isfinite(out.float()).all()
+    # the same chunk on caches whose K and V are TBQ3 or fp16 rows
+    formats = []
+    for kf, vf in (PREFILL_FORMATS if args.formats else ()):
+        m = tb.MixedKVCache(1, Hkv, n_past + n_q, kf, vf)
+        for t0, kc, vc in rows + [(n_past, k_new, v_new)]:
+            tb.mixed_append(m, kc, vc, t0)
+        for _ in range(2):
+            tb.mixed_attn_prefill_chunk(m, q, n_past, w.softmax_scale, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            tb.mixed_attn_prefill_chunk(m, q, n_past, w.softmax_scale, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        assert torch.isfinite(out.float()).all()
+        name = f"K {FORMAT_NAMES[kf]} / V {FORMAT_NAMES[vf]}"
+        log(f"prefill {name}: {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        formats.append({"formats": name, "attention_ms": round(ms, 4),
+                        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                        "frac_of_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)})
+        del m
+    del rows
     return {
         "workload": "prefill: 2048 new queries on 131072 cached tokens, batch 1, 8 KV / 64 Q "
                     "heads, head_dim 128; step = append of the chunk's K/V + causal attention",
@@ -388,6 +416,7 @@ def bench_prefill(tb, torch, args):
         "tflops": flops / (att_ms * 1e-3) / 1e12,
         "frac_of_mfma_peak": flops / (att_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
         "algorithmic_tflop": flops / 1e12, "query_tokens_per_s": n_q / (att_ms * 1e-3),
+        "formats": formats,
     }
 
 

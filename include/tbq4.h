@@ -321,6 +321,19 @@ tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4
                                     float softmax_scale, void *out, tbq4_dtype out_dtype,
                                     void *hip_stream);
 
+/* Prefill-chunk attention on a mixed-format cache (section "6. Ten sam cache
+ * na Apple silicon" runs the same attention over a TBQ3 cache; section
+ * "Konfiguracja" chooses the K and V types separately): as
+ * tbq4_attn_prefill_chunk, with K and V each stored as TBQ4, TBQ3 or fp16
+ * rows (tbq4_mixed_cache).  q is rotated only when K is stored rotated (TBQ4
+ * or TBQ3), the output rotated back only when V is.  A q8_0 tensor is
+ * TBQ4_ERR_UNSUPPORTED here (the decode calls read it); other errors as
+ * tbq4_attn_prefill_chunk. */
+tbq4_status tbq4_mixed_attn_prefill_chunk(const tbq4_mixed_cache *cache, const void *q,
+                                          tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_past,
+                                          int32_t n_q, float softmax_scale, void *out,
+                                          tbq4_dtype out_dtype, void *hip_stream);
+
 /* Static description of a status code. */
 const char *tbq4_status_str(tbq4_status s);
 

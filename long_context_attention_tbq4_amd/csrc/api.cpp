@@ -499,12 +499,12 @@ tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4
   return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
 }
 
-tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
-                                    int32_t n_q_heads, int32_t n_past, int32_t n_q,
-                                    float softmax_scale, void *out, tbq4_dtype out_dtype,
-                                    void *hip_stream) {
-  tbq4_status s = check_cache(cache);
-  if (s != TBQ4_OK) return s;
+// Prefill on K / V tensors in the given formats (TBQ4, fp16 or TBQ3); the
+// cache view has been checked.
+static tbq4_status prefill_formats(const tbq4_cache *cache, int32_t k_fmt, int32_t v_fmt,
+                                   const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                                   int32_t n_past, int32_t n_q, float softmax_scale, void *out,
+                                   tbq4_dtype out_dtype, void *hip_stream) {
   if (!q || !out) return TBQ4_ERR_INVALID_ARG;
   if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
   if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
@@ -529,8 +529,33 @@ tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4
   a.n_q = n_q;
   a.qscale = softmax_scale * 1.4426950408889634f;
   sign_words(cache->sign_seed, a.sign);
+  a.k_fmt = k_fmt;
+  a.v_fmt = v_fmt;
   return from_hip(tbq4::launch_prefill(a, cache->batch, (int)q_dtype, (int)out_dtype,
                                        (hipStream_t)hip_stream));
+}
+
+tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                    int32_t n_q_heads, int32_t n_past, int32_t n_q,
+                                    float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                    void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  return prefill_formats(cache, TBQ4_FMT_TBQ4, TBQ4_FMT_TBQ4, q, q_dtype, n_q_heads, n_past, n_q,
+                         softmax_scale, out, out_dtype, hip_stream);
+}
+
+tbq4_status tbq4_mixed_attn_prefill_chunk(const tbq4_mixed_cache *cache, const void *q,
+                                          tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_past,
+                                          int32_t n_q, float softmax_scale, void *out,
+                                          tbq4_dtype out_dtype, void *hip_stream) {
+  tbq4_cache view;
+  tbq4_status s = mixed_view(cache, view);
+  if (s != TBQ4_OK) return s;
+  if (cache->k_format == TBQ4_FMT_Q8_0 || cache->v_format == TBQ4_FMT_Q8_0)
+    return TBQ4_ERR_UNSUPPORTED;
+  return prefill_formats(&view, cache->k_format, cache->v_format, q, q_dtype, n_q_heads, n_past,
+                         n_q, softmax_scale, out, out_dtype, hip_stream);
 }
 
 const char *tbq4_status_str(tbq4_status s) {

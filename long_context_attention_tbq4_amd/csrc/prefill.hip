@@ -32,6 +32,8 @@
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
 
+#include <type_traits>
+
 namespace tbq4 {
 
 constexpr int kKT = 64;             // keys per tile
@@ -66,19 +68,39 @@ template <typename T> __device__ __forceinline__ float ld(const T *p);
 template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float ld<_Float16>(const _Float16 *p) { return (float)*p; }
 
-// One thread's share of a tile fetch: 8 index bytes of K and V for one key
-// (3 raw words each, realigned by 0 or 2 bytes), and the key's two scales
-// (first eighth).
-struct TileRaw {
-  u32x3 k3, v3;
-  uint16_t sk, sv;
+// Cache formats (K and V independently): TBQ4 blocks (the path described
+// above), TBQ3 blocks (50 bytes: scale + 3-bit codes) or fp16 rows (256
+// bytes, not rotated).  Every format is staged into the same LDS tiles of
+// fp16 values and per-key scales; TBQ4 rows keep the nibble order, TBQ3 and
+// fp16 rows the natural dimension order, and q' and the epilogue follow the
+// order of the tensor they meet.
+template <int F> __device__ __forceinline__ int pos_to_dim_f(int p) {
+  return F == kFmtTbq4 ? pos_to_dim(p) : p;
+}
+template <int F> constexpr uint32_t row_bytes_of() {
+  return F == kFmtTbq4 ? kBlockBytes : F == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+}
+
+// One thread's share of a tile fetch for one tensor: the 16 values at
+// positions 16 fq .. 16 fq + 15 of key fkey -- TBQ4: 8 index bytes in 3 raw
+// words (realigned by 0 or 2 bytes); TBQ3: 6 code bytes in 2 words; fp16: 32
+// bytes -- and the key's scale (threads with fq = 0).
+template <int F> struct RawPart;
+template <> struct RawPart<kFmtTbq4> { u32x3 w; uint16_t s; };
+template <> struct RawPart<kFmtTbq3> { u32x2 w; uint16_t s; };
+template <> struct RawPart<kFmtF16> { u32x4 w[2]; };
+template <int KF, int VF> struct TileRaw {
+  RawPart<KF> k;
+  RawPart<VF> v;
 };
 
 constexpr int kWaves = 8;           // wavefronts per workgroup (32 rows each)
 
-template <typename QT, typename OT>
+template <typename QT, typename OT, int KF, int VF>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillLds L;
+  constexpr bool kKRot = KF != kFmtF16;   // stored rotated: q is rotated to meet it
+  constexpr bool kVRot = VF != kFmtF16;   // stored rotated: the output is rotated back
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -109,12 +131,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = pos_to_dim(16 * c + 8 * half + e);
+        const int d = pos_to_dim_f<KF>(16 * c + 8 * half + e);
         const float v = ld<QT>(qp + d);
-        x[8 * c + e] = ((a.sign[d >> 5] >> (d & 31)) & 1u) ? -v : v;
+        x[8 * c + e] = (kKRot && ((a.sign[d >> 5] >> (d & 31)) & 1u)) ? -v : v;
       }
     // Walsh-Hadamard over the 7 position bits: bits 0-2 = e, bit 3 = half
     // (lanes 32 apart), bits 4-6 = c
+    if constexpr (kKRot) {
 #pragma unroll
     for (int h = 1; h < 64; h <<= 1) {
 #pragma unroll
@@ -130,7 +153,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       const float o = __shfl_xor(x[i], 32, 64);
       x[i] = half ? (o - x[i]) : (x[i] + o);
     }
-    const float f = 0.08838834764831845f * a.qscale;
+    }
+    const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
     float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
@@ -162,51 +186,88 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   const int kv_end = a.n_past + q_last + 1;                  // keys the workgroup needs
   const int n_tiles = (kv_end + kKT - 1) / kKT;
 
-  const size_t rowoff = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
-  const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
-  const rsrc_t rk = make_rsrc(a.k + rowoff, row_bytes);
-  const rsrc_t rv = make_rsrc(a.v + rowoff, row_bytes);
+  constexpr uint32_t kKB = row_bytes_of<KF>(), kVB = row_bytes_of<VF>();
+  const size_t rowi = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity;
+  const rsrc_t rk = make_rsrc(a.k + rowi * kKB, (uint32_t)a.capacity * kKB);
+  const rsrc_t rv = make_rsrc(a.v + rowi * kVB, (uint32_t)a.capacity * kVB);
 
-  // fetch mapping: thread -> (key, eighth), wavefront w fetching index bytes
-  // 8 w .. 8 w + 7 of the tile's 64 keys; start offsets are even, so the
-  // realignment shift is 0 or 2 (a per-thread constant)
+  // fetch mapping: thread -> (key, sixteenth of its values), wavefront w
+  // fetching values 16 w .. 16 w + 15 of the tile's 64 keys; packed start
+  // offsets are even, so the realignment shift is 0 or 2 (per thread)
   const int fkey = tid & 63, fq = tid >> 6;
-  const uint32_t foff = (uint32_t)fkey * kBlockBytes + 2 + 8 * fq;
-  const uint32_t fshift = foff & 3u;
-  auto fetch = [&](TileRaw &r, int t) {
-    const uint32_t base = (uint32_t)t * kKT * kBlockBytes;
-    const uint32_t a0 = (base + foff) & ~3u;
-    r.k3 = buf_load_x3(rk, a0);
-    r.v3 = buf_load_x3(rv, a0);
-    r.sk = 0;
-    r.sv = 0;
-    // keys at or past n_past + n_q may hold anything: their scales stay 0 so
-    // that a NaN there cannot survive the mask (p = 0)
-    if (fq == 0 && t * kKT + fkey < a.n_past + a.n_q) {
-      r.sk = buf_load_u16(rk, base + (uint32_t)fkey * kBlockBytes);
-      r.sv = buf_load_u16(rv, base + (uint32_t)fkey * kBlockBytes);
+  const int n_keys = a.n_past + a.n_q;   // keys at or past this may hold anything
+  // fetch one tensor's share of tile t (format F, buffer resource r)
+  auto fetch_part = [&](auto &part, const rsrc_t &rs, int t, auto fmt_tag) {
+    constexpr int F = decltype(fmt_tag)::value;
+    const bool live = t * kKT + fkey < n_keys;
+    if constexpr (F == kFmtTbq4) {
+      const uint32_t base = (uint32_t)t * kKT * kBlockBytes;
+      part.w = buf_load_x3(rs, (base + (uint32_t)fkey * kBlockBytes + 2 + 8 * fq) & ~3u);
+      // a NaN scale of an unwritten slot must not survive the mask (p = 0)
+      part.s = 0;
+      if (fq == 0 && live) part.s = buf_load_u16(rs, base + (uint32_t)fkey * kBlockBytes);
+    } else if constexpr (F == kFmtTbq3) {
+      const uint32_t base = (uint32_t)t * kKT * kBlockBytes3;
+      part.w = buf_load_x2(rs, (base + (uint32_t)fkey * kBlockBytes3 + 2 + 6 * fq) & ~3u);
+      part.s = 0;
+      if (fq == 0 && live) part.s = buf_load_u16(rs, base + (uint32_t)fkey * kBlockBytes3);
+    } else {
+      // fp16 rows: an unwritten slot may hold NaN values, so it reads as zeros
+      const uint32_t f = live ? (uint32_t)(t * kKT + fkey) * (2 * kHeadDim) + 32 * fq : 0xFFFF0000u;
+      part.w[0] = buf_load_x4(rs, f);
+      part.w[1] = buf_load_x4(rs, f + 16);
     }
   };
-  // dequantise a fetched share into LDS buffer `buf`: 16 fp16 codebook
-  // values of K and of V at row fkey, positions 16 fq .. 16 fq + 15
-  auto stage = [&](const TileRaw &r, int buf) {
-    const uint32_t kw[2] = {alignbyte(r.k3[1], r.k3[0], fshift), alignbyte(r.k3[2], r.k3[1], fshift)};
-    const uint32_t vw[2] = {alignbyte(r.v3[1], r.v3[0], fshift), alignbyte(r.v3[2], r.v3[1], fshift)};
-    uint8_t *kr = L.k[buf] + fkey * kRowB + 32 * fq;
-    uint8_t *vr = L.v[buf] + fkey * kVRowB;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
+  auto fetch = [&](TileRaw<KF, VF> &r, int t) {
+    fetch_part(r.k, rk, t, std::integral_constant<int, KF>{});
+    fetch_part(r.v, rv, t, std::integral_constant<int, VF>{});
+  };
+  // the 16 fp16 values of a fetched share, in the tensor's position order,
+  // as two 16-byte chunks; and the key's scale
+  auto expand = [&](const auto &part, u32x4 &c0, u32x4 &c1, auto fmt_tag) {
+    constexpr int F = decltype(fmt_tag)::value;
+    if constexpr (F == kFmtTbq4) {
+      const uint32_t sh = ((uint32_t)fkey * kBlockBytes + 2 + 8 * fq) & 3u;
+      const uint32_t w0 = alignbyte(part.w[1], part.w[0], sh), w1 = alignbyte(part.w[2], part.w[1], sh);
       uint32_t r0, r1, r2, r3;
-      nib4_to_f16(kw[c], r0, r1);
-      nib4_to_f16(kw[c] >> 4, r2, r3);
-      *(u32x4 *)(kr + 16 * c) = u32x4{r0, r1, r2, r3};
-      nib4_to_f16(vw[c], r0, r1);
-      nib4_to_f16(vw[c] >> 4, r2, r3);
-      *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq + 16 * c)) = u32x4{r0, r1, r2, r3};
+      nib4_to_f16(w0, r0, r1);
+      nib4_to_f16(w0 >> 4, r2, r3);
+      c0 = u32x4{r0, r1, r2, r3};
+      nib4_to_f16(w1, r0, r1);
+      nib4_to_f16(w1 >> 4, r2, r3);
+      c1 = u32x4{r0, r1, r2, r3};
+    } else if constexpr (F == kFmtTbq3) {
+      // 16 codes = 48 bits from the (even) start byte
+      const uint32_t sh = ((uint32_t)fkey * kBlockBytes3 + 2 + 6 * fq) & 3u;
+      const uint32_t lo = alignbyte(part.w[1], part.w[0], sh);
+      const uint32_t hi = part.w[1] >> (8 * sh);
+      c0 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(lo & 0xFFFFFFu));
+      c1 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(((lo >> 24) | (hi << 8)) & 0xFFFFFFu));
+    } else {
+      c0 = part.w[0];
+      c1 = part.w[1];
     }
+  };
+  auto scale_of = [&](const auto &part, auto fmt_tag) -> float {
+    constexpr int F = decltype(fmt_tag)::value;
+    if constexpr (F == kFmtF16) return 1.0f;
+    else return half_bits_to_float(part.s);
+  };
+  // dequantise a fetched share into LDS buffer `buf`: 16 fp16 values of K
+  // and of V at row fkey, positions 16 fq .. 16 fq + 15
+  auto stage = [&](const TileRaw<KF, VF> &r, int buf) {
+    u32x4 c0, c1;
+    expand(r.k, c0, c1, std::integral_constant<int, KF>{});
+    uint8_t *kr = L.k[buf] + fkey * kRowB + 32 * fq;
+    *(u32x4 *)kr = c0;
+    *(u32x4 *)(kr + 16) = c1;
+    expand(r.v, c0, c1, std::integral_constant<int, VF>{});
+    uint8_t *vr = L.v[buf] + fkey * kVRowB;
+    *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq)) = c0;
+    *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq + 16)) = c1;
     if (fq == 0) {
-      L.sk[buf][fkey] = half_bits_to_float(r.sk);
-      L.sv[buf][fkey] = half_bits_to_float(r.sv);
+      L.sk[buf][fkey] = scale_of(r.k, std::integral_constant<int, KF>{});
+      L.sv[buf][fkey] = scale_of(r.v, std::integral_constant<int, VF>{});
     }
   };
 
@@ -224,7 +285,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   const int tr_col = 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
 
   {
-    TileRaw r0;
+    TileRaw<KF, VF> r0;
     fetch(r0, 0);
     stage(r0, 0);
   }
@@ -233,7 +294,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
     const int key0 = kt * kKT;
-    TileRaw nxt;
+    TileRaw<KF, VF> nxt;
     const bool more = kt + 1 < n_tiles;
     if (more) fetch(nxt, kt + 1);
 
@@ -336,6 +397,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) y[16 * db + e] = o[db][e] * inv;
   // position bits 0,1 = e bits 0,1; bits 3,4 = e bits 2,3; bits 5,6 = db
+  if constexpr (kVRot) {
 #pragma unroll
   for (int h = 1; h < 64; h <<= 1) {
 #pragma unroll
@@ -351,16 +413,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     const float t = __shfl_xor(y[i], 32, 64);
     y[i] = half ? (t - y[i]) : (y[i] + t);
   }
+  }
   if (row_valid) {
     OT *dst = (OT *)a.out + (((size_t)b * a.n_q + qi) * a.n_q_heads + hq) * kHeadDim;
-    const float r = 0.08838834764831845f;
+    const float r = kVRot ? 0.08838834764831845f : 1.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       const int db = i >> 4, e = i & 15;
       const int p = 32 * db + 8 * (e >> 2) + 4 * half + (e & 3);
-      const int d = pos_to_dim(p);
+      const int d = pos_to_dim_f<VF>(p);
       const float v = y[i] * r;
-      dst[d] = (OT)(((a.sign[d >> 5] >> (d & 31)) & 1u) ? -v : v);
+      dst[d] = (OT)((kVRot && ((a.sign[d >> 5] >> (d & 31)) & 1u)) ? -v : v);
     }
   }
 }
@@ -372,15 +435,22 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_
   const int64_t gx = (int64_t)n_qt * a.n_kv_heads;
   if (gx > 0x7FFFFFFF || batch > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)gx, batch);
-  if (q_dtype == 0 && out_dtype == 1)
-    hipLaunchKernelGGL((prefill_kernel<float, _Float16>), grid, dim3(64 * kWaves), 0, stream, a);
-  else if (q_dtype == 0)
-    hipLaunchKernelGGL((prefill_kernel<float, float>), grid, dim3(64 * kWaves), 0, stream, a);
-  else if (out_dtype == 1)
-    hipLaunchKernelGGL((prefill_kernel<_Float16, _Float16>), grid, dim3(64 * kWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<_Float16, float>), grid, dim3(64 * kWaves), 0, stream, a);
-  return hipGetLastError();
+  // (q dtype, output dtype, K format, V format) -> kernel instance; formats
+  // TBQ4 (0), fp16 (1), TBQ3 (2)
+#define TBQ4_PF(QT, OT, KF, VF) reinterpret_cast<const void *>(&prefill_kernel<QT, OT, KF, VF>)
+#define TBQ4_PF_K(QT, OT, KF) {TBQ4_PF(QT, OT, KF, 0), TBQ4_PF(QT, OT, KF, 1), TBQ4_PF(QT, OT, KF, 2)}
+#define TBQ4_PF_Q(QT, OT) {TBQ4_PF_K(QT, OT, 0), TBQ4_PF_K(QT, OT, 1), TBQ4_PF_K(QT, OT, 2)}
+  static const void *const kernels[2][2][3][3] = {
+      {TBQ4_PF_Q(float, float), TBQ4_PF_Q(float, _Float16)},
+      {TBQ4_PF_Q(_Float16, float), TBQ4_PF_Q(_Float16, _Float16)}};
+#undef TBQ4_PF_Q
+#undef TBQ4_PF_K
+#undef TBQ4_PF
+  if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
+  const void *fn = kernels[q_dtype == 0 ? 0 : 1][out_dtype == 1 ? 1 : 0][a.k_fmt][a.v_fmt];
+  PrefillArgs arg = a;
+  void *params[] = {&arg};
+  return hipLaunchKernel(fn, grid, dim3(64 * kWaves), params, 0, stream);
 }
 
 }  // namespace tbq4

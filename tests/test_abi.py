@@ -214,3 +214,13 @@ def test_mixed_format_row_bytes_and_argument_errors(L):
     assert dec(mc(kf=3, vf=0), n_ctx=65) == _lib.ERR_CAPACITY
     assert dec(mc(kf=2, vf=2), n_ctx=65) == _lib.ERR_CAPACITY
     assert dec(mc(kf=2, vf=1), hq=18) == _lib.ERR_UNSUPPORTED
+
+    def pre(cache, hq=8, n_past=10, n_q=5):
+        return L.tbq4_mixed_attn_prefill_chunk(ctypes.byref(cache), FAKE, 0, hq, n_past, n_q, 0.1,
+                                               FAKE, 1, None)
+    assert pre(mc(kf=3, vf=0)) == _lib.ERR_UNSUPPORTED    # q8_0: decode-only
+    assert pre(mc(kf=0, vf=3)) == _lib.ERR_UNSUPPORTED
+    assert pre(mc(kf=2, vf=4)) == _lib.ERR_UNSUPPORTED
+    assert pre(mc(kf=2, vf=1), n_past=60, n_q=5) == _lib.ERR_CAPACITY
+    assert pre(mc(kf=1, vf=2), hq=6) == _lib.ERR_UNSUPPORTED   # G = 3
+    assert pre(mc(kf=1, vf=1), n_q=0) == _lib.ERR_CAPACITY

@@ -132,3 +132,48 @@ def test_append_block_counts_not_multiple_of_four(kf, vf, B, H, n_new):
     assert np.array_equal(cache.k[:, :, 5:5 + n_new].cpu().numpy(), kb)
     assert np.array_equal(cache.v[:, :, 5:5 + n_new].cpu().numpy(), vb)
     assert not cache.k[:, :, :5].any() and not cache.k[:, :, 5 + n_new:].any()
+
+
+PREFILL_FORMATS = list(itertools.product([tb.FMT_TBQ4, tb.FMT_F16, tb.FMT_TBQ3], repeat=2))
+
+
+@pytest.mark.parametrize("kf,vf", PREFILL_FORMATS)
+def test_prefill_formats(kf, vf):
+    """Prefill chunk (query i at n_past + i sees slots 0 .. n_past + i) on K
+    and V stored as TBQ4, TBQ3 or fp16, against the fp64 definition on the
+    dequantised tensors; unused slots hold 0xFF bytes (NaN fp16 values, NaN
+    scales) that must not leak."""
+    rng = np.random.default_rng(40 + kf + 4 * vf)
+    B, H, G, n_past, n_q, cap, seed, scale = 2, 2, 4, 301, 97, 424, 5, 0.09
+    T = n_past + n_q
+    k = rng.standard_normal((B, T, H, 128)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, 128)).astype(np.float32)
+    q = rng.standard_normal((B, n_q, H * G, 128)).astype(np.float32)
+    cache = tb.MixedKVCache(B, H, cap, kf, vf, sign_seed=seed)
+    cache.k.fill_(0xFF)
+    cache.v.fill_(0xFF)
+    tb.mixed_append(cache, torch.from_numpy(k[:, :n_past].copy()).cuda(),
+                    torch.from_numpy(v[:, :n_past].copy()).cuda(), 0)
+    tb.mixed_append(cache, torch.from_numpy(k[:, n_past:].copy()).cuda(),
+                    torch.from_numpy(v[:, n_past:].copy()).cuda(), n_past)
+    kb, kh = _oracle_tensor(k, kf, seed)
+    vb, vh = _oracle_tensor(v, vf, seed)
+    assert np.array_equal(cache.k[:, :, :T].cpu().numpy(), kb), "K bytes"
+    assert np.array_equal(cache.v[:, :, :T].cpu().numpy(), vb), "V bytes"
+    out = tb.mixed_attn_prefill_chunk(cache, torch.from_numpy(q).cuda(), n_past, scale,
+                                      out_dtype=torch.float32).cpu().numpy()
+    ref = np.empty(out.shape, np.float64)
+    for b in range(B):
+        for g in range(H):
+            for i in range(n_q):
+                n = n_past + i + 1
+                ref[b, i, g * G:(g + 1) * G] = o.attn_decode_rows_ref(
+                    q[b, i, g * G:(g + 1) * G], kh[b, g, :n], vh[b, g, :n], scale)
+    check_attn(out, ref, False, f"prefill k{kf} v{vf}")
+    if (kf, vf) == (tb.FMT_TBQ4, tb.FMT_TBQ4):   # the TBQ4 call computes the same
+        plain = tb.KVCache(B, H, cap, sign_seed=seed)
+        plain.k.copy_(cache.k)
+        plain.v.copy_(cache.v)
+        same = tb.attn_prefill_chunk(plain, torch.from_numpy(q).cuda(), n_past, scale,
+                                     out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(same, out)
