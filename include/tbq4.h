@@ -334,6 +334,21 @@ tbq4_status tbq4_mixed_attn_prefill_chunk(const tbq4_mixed_cache *cache, const v
                                           int32_t n_q, float softmax_scale, void *out,
                                           tbq4_dtype out_dtype, void *hip_stream);
 
+/* Multi-query verify attention on a mixed-format cache (the drafted-token
+ * verify of page "Kontekst 262K na jednej RTX 4090: co dodałem do
+ * llama.cpp-turboq" over the per-tensor types of its section "Konfiguracja"
+ * and the TBQ3 cache of section "6. Ten sam cache na Apple silicon"): as
+ * tbq4_attn_verify, with K and V each stored as TBQ4, TBQ3 or fp16 rows
+ * (tbq4_mixed_cache).  q is rotated only when K is stored rotated, the output
+ * rotated back only when V is.  The workspace size is
+ * tbq4_verify_workspace_bytes as for TBQ4.  A q8_0 tensor is
+ * TBQ4_ERR_UNSUPPORTED here; other errors as tbq4_attn_verify. */
+tbq4_status tbq4_mixed_attn_verify(const tbq4_mixed_cache *cache, const void *q,
+                                   tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_past,
+                                   int32_t n_q, float softmax_scale, void *out,
+                                   tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+
 /* Static description of a status code. */
 const char *tbq4_status_str(tbq4_status s);
 

@@ -23,7 +23,7 @@ __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
     "attn_decode_partial", "attn_decode_merge", "quantize_append_at", "attn_decode_varlen",
     "attn_verify", "verify_workspace_bytes", "MixedKVCache", "mixed_append",
-    "mixed_attn_decode", "mixed_attn_prefill_chunk", "FMT_TBQ4", "FMT_F16", "FMT_TBQ3", "FMT_Q8_0",
+    "mixed_attn_decode", "mixed_attn_prefill_chunk", "mixed_attn_verify", "FMT_TBQ4", "FMT_F16", "FMT_TBQ3", "FMT_Q8_0",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
     "decode_workspace_bytes", "version", "HEAD_DIM", "BLOCK_BYTES", "MAX_SPLITS",
 ]
@@ -169,6 +169,26 @@ def mixed_attn_prefill_chunk(cache, q, n_past, softmax_scale, out=None, out_dtyp
     _check(_lib.lib().tbq4_mixed_attn_prefill_chunk(
         ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_past, n_q, float(softmax_scale), _ptr(out),
         _dtype(out), _stream(q.device)), "tbq4_mixed_attn_prefill_chunk")
+    return out
+
+
+def mixed_attn_verify(cache, q, n_past, softmax_scale, n_splits=0, out=None,
+                      out_dtype=torch.float16, workspace=None):
+    """Multi-query verify attention over a MixedKVCache whose K and V are
+    TBQ4, TBQ3 or fp16 (q8_0 is decode-only); same shapes as attn_verify."""
+    _require(q, "q")
+    B, n_q, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, n_q, Hq, D))
+    need = verify_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, n_past, n_q, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_mixed_attn_verify(
+        ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_past, n_q, float(softmax_scale), _ptr(out),
+        _dtype(out), n_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device)), "tbq4_mixed_attn_verify")
     return out
 
 

@@ -24,6 +24,7 @@ EXPORTS = (
     "tbq4_attn_prefill_chunk", "tbq4_quantize_append_at", "tbq4_attn_decode_varlen",
     "tbq4_verify_workspace_bytes", "tbq4_attn_verify", "tbq4_format_row_bytes",
     "tbq4_mixed_append", "tbq4_mixed_attn_decode", "tbq4_mixed_attn_prefill_chunk",
+    "tbq4_mixed_attn_verify",
     "tbq4_status_str", "tbq4_version",
 )
 
@@ -109,6 +110,8 @@ def lib():
     L.tbq4_mixed_attn_decode.restype = i32
     L.tbq4_mixed_attn_prefill_chunk.argtypes = [pm, vp, i32, i32, i32, i32, f32, vp, i32, vp]
     L.tbq4_mixed_attn_prefill_chunk.restype = i32
+    L.tbq4_mixed_attn_verify.argtypes = [pm, vp, i32, i32, i32, i32, f32, vp, i32, i32, vp, sz, vp]
+    L.tbq4_mixed_attn_verify.restype = i32
     L.tbq4_attn_prefill_chunk.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, vp]
     L.tbq4_attn_prefill_chunk.restype = i32
     L.tbq4_status_str.argtypes = [i32]

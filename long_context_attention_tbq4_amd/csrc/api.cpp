@@ -396,12 +396,14 @@ size_t tbq4_verify_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_
   return round256((size_t)batch * n_q * n_q_heads * p * 130 * sizeof(float));
 }
 
-tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
-                             int32_t n_q_heads, int32_t n_past, int32_t n_q, float softmax_scale,
-                             void *out, tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
-                             size_t workspace_bytes, void *hip_stream) {
-  tbq4_status s = check_cache(cache);
-  if (s != TBQ4_OK) return s;
+// Verify over a cache view whose K and V tensors are stored in k_fmt / v_fmt
+// (TBQ4, fp16 or TBQ3); the caller has checked the view.
+static tbq4_status verify_formats(const tbq4_cache *cache, int32_t k_fmt, int32_t v_fmt,
+                                  const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                                  int32_t n_past, int32_t n_q, float softmax_scale, void *out,
+                                  tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+  tbq4_status s;
   if (!q || !out) return TBQ4_ERR_INVALID_ARG;
   if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
   if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
@@ -437,6 +439,8 @@ tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype 
   a.n_splits = P;
   a.qscale = softmax_scale * 1.4426950408889634f;
   sign_words(cache->sign_seed, a.sign);
+  a.k_fmt = k_fmt;
+  a.v_fmt = v_fmt;
   hipStream_t st = (hipStream_t)hip_stream;
   s = from_hip(tbq4::launch_verify_partial(a, cache->batch, (int)q_dtype, st));
   if (s != TBQ4_OK) return s;
@@ -447,9 +451,35 @@ tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype 
   m.out = out;
   m.n_q_heads = n_q_heads;
   m.n_splits = P;
-  m.rotate_out = 1;
+  m.rotate_out = v_fmt == TBQ4_FMT_TBQ4 || v_fmt == TBQ4_FMT_TBQ3 ? 1 : 0;
   memcpy(m.sign, a.sign, sizeof(a.sign));
   return from_hip(tbq4::launch_decode_merge(m, cache->batch * n_q, (int)out_dtype, st));
+}
+
+tbq4_status tbq4_attn_verify(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                             int32_t n_q_heads, int32_t n_past, int32_t n_q, float softmax_scale,
+                             void *out, tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                             size_t workspace_bytes, void *hip_stream) {
+  tbq4_status s = check_cache(cache);
+  if (s != TBQ4_OK) return s;
+  return verify_formats(cache, TBQ4_FMT_TBQ4, TBQ4_FMT_TBQ4, q, q_dtype, n_q_heads, n_past, n_q,
+                        softmax_scale, out, out_dtype, n_splits, workspace, workspace_bytes,
+                        hip_stream);
+}
+
+tbq4_status tbq4_mixed_attn_verify(const tbq4_mixed_cache *cache, const void *q,
+                                   tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_past,
+                                   int32_t n_q, float softmax_scale, void *out,
+                                   tbq4_dtype out_dtype, int32_t n_splits, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream) {
+  tbq4_cache view;
+  tbq4_status s = mixed_view(cache, view);
+  if (s != TBQ4_OK) return s;
+  if (cache->k_format == TBQ4_FMT_Q8_0 || cache->v_format == TBQ4_FMT_Q8_0)
+    return TBQ4_ERR_UNSUPPORTED;
+  return verify_formats(&view, cache->k_format, cache->v_format, q, q_dtype, n_q_heads, n_past,
+                        n_q, softmax_scale, out, out_dtype, n_splits, workspace, workspace_bytes,
+                        hip_stream);
 }
 
 tbq4_status tbq4_quantize_append_at(const tbq4_cache *cache, const void *k_new, const void *v_new,

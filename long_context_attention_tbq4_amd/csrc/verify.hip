@@ -23,6 +23,11 @@
 //     own scores and P~ rows; P~ = p d^V is one fp16, rounded to nearest.
 // Partial states use the decode workspace layout with (sequence, query) as
 // the row index, so the decode merge kernel finishes them.
+//
+// K and V may each be stored as TBQ4 blocks, TBQ3 blocks or fp16 rows
+// (template arguments KF, VF); the fetch, operand and staging steps of each
+// format are the decode kernel's.  q is rotated only when K is stored
+// rotated, and the merge rotates the output back only when V is.
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
 
@@ -33,12 +38,18 @@ namespace tbq4 {
 namespace {
 constexpr int kTile = 32;
 constexpr int kBlk = kTile / 16;
-constexpr int kVRow = 80;
+constexpr int kVRow = 80;           // staged TBQ4 V row: 64 index bytes + pad
+constexpr int kE4Row = 144;         // staged TBQ3 V row: 128 e4m3 bytes + pad
+constexpr int kF16Row = 288;        // staged fp16 V row: 256 bytes + pad
 }  // namespace
 
-template <typename QT, int CG>
+template <typename QT, int CG, int KF, int VF>
 __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t vlds[kTile * kVRow];
+  constexpr bool kKRot = KF != kFmtF16;
+  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : VF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+  __shared__ __attribute__((aligned(16))) uint8_t
+      vlds[kTile * (VF == kFmtTbq4 ? kVRow : VF == kFmtTbq3 ? kE4Row : kF16Row)];
   __shared__ __attribute__((aligned(16))) float sk[kTile];
   __shared__ __attribute__((aligned(16))) float sv[kTile];
   __shared__ __attribute__((aligned(16))) half8 qlds[CG][4][2][64];   // q' high / residual
@@ -60,12 +71,13 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     const QT *qp = (const QT *)a.q +
                    (((size_t)b * a.n_q + (live ? qi : 0)) * a.n_q_heads + (size_t)g * G +
                     (live ? head : 0)) * kHeadDim + quarter * 32;
-    const uint32_t sw = a.sign[quarter];
+    const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const float x = live ? load_q<QT>(qp + i) : 0.0f;
       qv[c][i] = ((sw >> i) & 1u) ? -x : x;
     }
+    if constexpr (kKRot) {
 #pragma unroll
     for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
@@ -84,8 +96,9 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         qv[c][i] = upper ? (o - qv[c][i]) : (qv[c][i] + o);
       }
     }
+    }
   }
-  const float f = 0.08838834764831845f * a.qscale;
+  const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
   float mx = 0.0f;
 #pragma unroll
   for (int c = 0; c < CG; ++c)
@@ -107,7 +120,9 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int el = 0; el < 8; ++el) {
-        const int i = 8 * k + (el < 4 ? 2 * el : 2 * el - 7);
+        // TBQ4 K operands hold the 4 even then the 4 odd dims of a code
+        // word; TBQ3 and fp16 K operands hold 8 consecutive dims
+        const int i = KF == kFmtTbq4 ? 8 * k + (el < 4 ? 2 * el : 2 * el - 7) : 8 * k + el;
         const float x = ldexpf(qv[c][i], ex);
         const _Float16 hi = (_Float16)x;
         qhi[c][k][el] = hi;
@@ -128,10 +143,9 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
   const int t_begin = split * tiles_per_split;
   const int t_end = min(t_begin + tiles_per_split, n_tiles);
 
-  const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity * kBlockBytes;
-  const uint32_t row_bytes = (uint32_t)a.capacity * kBlockBytes;
-  const rsrc_t rk = make_rsrc(a.k + row, row_bytes);
-  const rsrc_t rv = make_rsrc(a.v + row, row_bytes);
+  const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.capacity;
+  const rsrc_t rk = make_rsrc(a.k + row * kKBytes, (uint32_t)a.capacity * kKBytes);
+  const rsrc_t rv = make_rsrc(a.v + row * kVBytes, (uint32_t)a.capacity * kVBytes);
 
   float m_run[CG], l_run[CG];
   float4v o[CG][8];
@@ -143,33 +157,69 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     for (int i = 0; i < 8; ++i) o[c][i] = float4v{0.f, 0.f, 0.f, 0.f};
   }
 
+  // transposed-read source addresses (fixed per lane): TBQ4 rows (index
+  // bytes), TBQ3 rows (e4m3 bytes) and fp16 rows, as in the decode kernel
   int tr_off;
   {
     const int e = col >> 1;
     const int tok = 16 * (e >> 2) + 4 * quarter + (e & 3);
     tr_off = tok * kVRow + 8 * (col & 1);
   }
+  int tr8_3_off;
+  {
+    const int j = col >> 1;
+    const int tok = j < 4 ? 4 * quarter + j : 16 + 4 * quarter + (j - 4);
+    tr8_3_off = tok * kE4Row + 8 * (col & 1);
+  }
+  const int tr16_off = (4 * quarter + (col >> 2)) * kF16Row + 8 * (col & 3);
 
+  // raw fetch of one tile: per 16-token group this lane's 16 index bytes
+  // (TBQ4: 5 words realigned by 0 or 2 bytes; TBQ3: 12 code bytes in one
+  // 16-byte load) or its token's 32 fp16 dims (4 aligned 16-byte loads), and
+  // the scales of token `lane`; a tile past the split reads as zeros
+  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : 1;
   struct Raw {
-    u32x4 k4[kBlk], v4[kBlk];
+    u32x4 k4[kBlk * kKW], v4[kBlk * kVW];
     uint32_t k1[kBlk], v1[kBlk];
     uint16_t sk, sv;
   };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
-  const uint32_t shift = lane_off & 3u;
+  const uint32_t shift = lane_off & 3u;   // (2 col + 2) mod 4: the same for TBQ3
   auto fetch = [&](Raw &r, int t) {
-    const uint32_t base = t < t_end ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
+    const bool live = t < t_end;
+    const uint32_t base = live ? (uint32_t)t * kTile * kBlockBytes : 0xFFFF0000u;
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       const uint32_t ad = (base + (uint32_t)(16 * blk) * kBlockBytes + lane_off) & ~3u;
-      r.k4[blk] = buf_load_x4(rk, ad);
-      r.k1[blk] = buf_load_x1(rk, ad + 16);
-      r.v4[blk] = buf_load_x4(rv, ad);
-      r.v1[blk] = buf_load_x1(rv, ad + 16);
+      const uint32_t tok = (uint32_t)(t * kTile + 16 * blk + col);
+      const uint32_t a3 = live ? (tok * kBlockBytes3 + 2u + 12u * quarter) & ~3u : 0xFFFF0000u;
+      if constexpr (KF == kFmtTbq4) {
+        r.k4[blk] = buf_load_x4(rk, ad);
+        r.k1[blk] = buf_load_x1(rk, ad + 16);
+      } else if constexpr (KF == kFmtTbq3) {
+        r.k4[blk] = buf_load_x4(rk, a3);
+      } else {
+        const uint32_t fo = live ? tok * kKBytes + 64u * quarter : 0xFFFF0000u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.k4[4 * blk + c] = buf_load_x4(rk, fo + 16u * c);
+      }
+      if constexpr (VF == kFmtTbq4) {
+        r.v4[blk] = buf_load_x4(rv, ad);
+        r.v1[blk] = buf_load_x1(rv, ad + 16);
+      } else if constexpr (VF == kFmtTbq3) {
+        r.v4[blk] = buf_load_x4(rv, a3);
+      } else {
+        const uint32_t fo = live ? tok * kVBytes + 64u * quarter : 0xFFFF0000u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.v4[4 * blk + c] = buf_load_x4(rv, fo + 16u * c);
+      }
     }
     const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
-    r.sk = buf_load_u16(rk, soff);
-    r.sv = buf_load_u16(rv, soff);
+    const uint32_t soff3 = lane < kTile && live ? (uint32_t)(t * kTile + lane) * kBlockBytes3 : 0xFFFF0000u;
+    if constexpr (KF == kFmtTbq4) r.sk = buf_load_u16(rk, soff);
+    if constexpr (KF == kFmtTbq3) r.sk = buf_load_u16(rk, soff3);
+    if constexpr (VF == kFmtTbq4) r.sv = buf_load_u16(rv, soff);
+    if constexpr (VF == kFmtTbq3) r.sv = buf_load_u16(rv, soff3);
   };
 
   // kPartial: the tile holds slots a draft query must not see (or slots past
@@ -178,24 +228,57 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     constexpr bool kPartial = decltype(partial_tag)::value;
     const int tok0 = t * kTile;
     uint32_t kw[kBlk][4];
+    u32x4 kf[KF == kFmtF16 ? kBlk * 4 : 1];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       const u32x4 w = r.k4[blk];
-      kw[blk][0] = alignbyte(w[1], w[0], shift);
-      kw[blk][1] = alignbyte(w[2], w[1], shift);
-      kw[blk][2] = alignbyte(w[3], w[2], shift);
-      kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+      if constexpr (KF == kFmtTbq4) {
+        kw[blk][0] = alignbyte(w[1], w[0], shift);
+        kw[blk][1] = alignbyte(w[2], w[1], shift);
+        kw[blk][2] = alignbyte(w[3], w[2], shift);
+        kw[blk][3] = alignbyte(r.k1[blk], w[3], shift);
+      } else if constexpr (KF == kFmtTbq3) {   // 96 code bits of the lane's 32 dims
+        kw[blk][0] = alignbyte(w[1], w[0], shift);
+        kw[blk][1] = alignbyte(w[2], w[1], shift);
+        kw[blk][2] = alignbyte(w[3], w[2], shift);
+      } else {
+        // fp16 slots past the drafted tokens may hold anything: zero them
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_kv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[4 * blk + c] = dead ? u32x4{0u, 0u, 0u, 0u} : r.k4[4 * blk + c];
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
-      const u32x4 w = r.v4[blk];
-      const u32x4 al = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
-                        alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
-      *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = al;
+      if constexpr (VF == kFmtTbq4) {
+        const u32x4 w = r.v4[blk];
+        const u32x4 al = {alignbyte(w[1], w[0], shift), alignbyte(w[2], w[1], shift),
+                          alignbyte(w[3], w[2], shift), alignbyte(r.v1[blk], w[3], shift)};
+        *(u32x4 *)(vlds + (16 * blk + col) * kVRow + 16 * quarter) = al;
+      } else if constexpr (VF == kFmtTbq3) {
+        // the lane's 32 codes -> 32 e4m3 bytes (dims 32 quarter ..) in LDS
+        const u32x4 w = r.v4[blk];
+        const uint32_t w0 = alignbyte(w[1], w[0], shift), w1 = alignbyte(w[2], w[1], shift),
+                       w2 = alignbyte(w[3], w[2], shift);
+        uint32_t e[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tbq3_chunk_to_e4m3(tbq3_chunk(w0, w1, w2, c), e[2 * c], e[2 * c + 1]);
+        uint8_t *rowp = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
+        *(u32x4 *)rowp = u32x4{e[0], e[1], e[2], e[3]};
+        *(u32x4 *)(rowp + 16) = u32x4{e[4], e[5], e[6], e[7]};
+      } else {
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_kv;   // (as for K)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *(u32x4 *)(vlds + (16 * blk + col) * kF16Row + 64 * quarter + 16 * c) =
+              dead ? u32x4{0u, 0u, 0u, 0u} : r.v4[4 * blk + c];
+      }
     }
     if (lane < kTile) {
-      float dk = half_bits_to_float(r.sk) * qs_inv, dv = half_bits_to_float(r.sv);
+      float dk = qs_inv, dv = 1.0f;
+      if constexpr (KF != kFmtF16) dk = half_bits_to_float(r.sk) * qs_inv;
+      if constexpr (VF != kFmtF16) dv = half_bits_to_float(r.sv);
       if constexpr (kPartial) {
         // slots past the drafted tokens may hold anything (NaN survives p = 0)
         if (tok0 + lane >= n_kv) dk = dv = 0.0f;
@@ -212,7 +295,12 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 #pragma unroll
       for (int blk = 0; blk < kBlk; ++blk)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) kh[blk][k] = word_to_half8(kw[blk][k]);
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (KF == kFmtTbq4) kh[blk][k] = word_to_half8(kw[blk][k]);
+          else if constexpr (KF == kFmtTbq3)
+            kh[blk][k] = tbq3_chunk_to_half8(tbq3_chunk(kw[blk][0], kw[blk][1], kw[blk][2], k));
+          else kh[blk][k] = __builtin_bit_cast(half8, kf[4 * blk + k]);
+        }
       // consecutive MFMAs rotate through the CG x 2 accumulators, so none
       // waits for the one before it (each accumulator still takes step k's
       // high part, then its residual, in order)
@@ -295,17 +383,41 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     }
 
     // ---- O'^T += P~ V for every column group (V dequantised once)
+    if constexpr (VF == kFmtTbq4) {
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      typedef __attribute__((address_space(3))) int2v lds_i2;
-      const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr_off + 16 * cg));
-      const uint32_t w0 = (uint32_t)rr[0], w1 = (uint32_t)rr[1];
-      const half8 ve = lo_nibbles_to_half8(w0, w1);
-      const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
+      for (int cg = 0; cg < 4; ++cg) {
+        typedef __attribute__((address_space(3))) int2v lds_i2;
+        const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr_off + 16 * cg));
+        const uint32_t w0 = (uint32_t)rr[0], w1 = (uint32_t)rr[1];
+        const half8 ve = lo_nibbles_to_half8(w0, w1);
+        const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
 #pragma unroll
-      for (int c = 0; c < CG; ++c) {
-        o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], ve, o[c][2 * cg], 0, 0, 0);
-        o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vo, o[c][2 * cg + 1], 0, 0, 0);
+        for (int c = 0; c < CG; ++c) {
+          o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], ve, o[c][2 * cg], 0, 0, 0);
+          o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vo, o[c][2 * cg + 1], 0, 0, 0);
+        }
+      }
+    } else {
+      // TBQ3: e4m3 bytes, one byte-transposed read per 16 dims; fp16: two
+      // 16-bit transposed reads per 16 dims (dim 16 db + col)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        half8 vv;
+        if constexpr (VF == kFmtTbq3) {
+          typedef __attribute__((address_space(3))) int2v lds_i2;
+          const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+          vv = e4m3x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]);
+        } else {
+          typedef __attribute__((address_space(3))) short4v lds_s4;
+          const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vlds + tr16_off + 32 * db));
+          const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4 *)(vlds + tr16_off + 16 * kF16Row + 32 * db));
+          const short8v s8 = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+          vv = __builtin_bit_cast(half8, s8);
+        }
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+          o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vv, o[c][db], 0, 0, 0);
       }
     }
   };
@@ -338,10 +450,15 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
       if (rq < a.n_q && rh < G) {
         float *dst = a.ws + (((size_t)b * a.n_q + rq) * a.n_q_heads + (size_t)g * G + rh) * P * 130 +
                      (size_t)split * 130 + 2;
+        if constexpr (VF == kFmtTbq4) {
 #pragma unroll
-        for (int cg = 0; cg < 4; ++cg) {
-          dst[32 * cg + 2 * col] = o[c][2 * cg][e];
-          dst[32 * cg + 2 * col + 1] = o[c][2 * cg + 1][e];
+          for (int cg = 0; cg < 4; ++cg) {
+            dst[32 * cg + 2 * col] = o[c][2 * cg][e];
+            dst[32 * cg + 2 * col + 1] = o[c][2 * cg + 1][e];
+          }
+        } else {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) dst[16 * db + col] = o[c][db][e];
         }
       }
     }
@@ -350,15 +467,21 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 
 hipError_t launch_verify_partial(const VerifyArgs &a, int batch, int q_dtype, hipStream_t stream) {
   dim3 grid(a.n_splits, a.n_kv_heads, batch);
-  const bool two = a.n_q > 2;
-  if (q_dtype == 0) {
-    if (two) hipLaunchKernelGGL((verify_split_kernel<float, 2>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((verify_split_kernel<float, 1>), grid, dim3(64), 0, stream, a);
-  } else {
-    if (two) hipLaunchKernelGGL((verify_split_kernel<_Float16, 2>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((verify_split_kernel<_Float16, 1>), grid, dim3(64), 0, stream, a);
-  }
-  return hipGetLastError();
+  // (q dtype, column groups, K format, V format) -> kernel instance;
+  // formats TBQ4 (0), fp16 (1), TBQ3 (2)
+#define TBQ4_VF(QT, CG, KF, VF) reinterpret_cast<const void *>(&verify_split_kernel<QT, CG, KF, VF>)
+#define TBQ4_VF_K(QT, CG, KF) {TBQ4_VF(QT, CG, KF, 0), TBQ4_VF(QT, CG, KF, 1), TBQ4_VF(QT, CG, KF, 2)}
+#define TBQ4_VF_C(QT, CG) {TBQ4_VF_K(QT, CG, 0), TBQ4_VF_K(QT, CG, 1), TBQ4_VF_K(QT, CG, 2)}
+  static const void *const kernels[2][2][3][3] = {{TBQ4_VF_C(float, 1), TBQ4_VF_C(float, 2)},
+                                                  {TBQ4_VF_C(_Float16, 1), TBQ4_VF_C(_Float16, 2)}};
+#undef TBQ4_VF_C
+#undef TBQ4_VF_K
+#undef TBQ4_VF
+  if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
+  const void *fn = kernels[q_dtype == 0 ? 0 : 1][a.n_q > 2 ? 1 : 0][a.k_fmt][a.v_fmt];
+  VerifyArgs arg = a;
+  void *params[] = {&arg};
+  return hipLaunchKernel(fn, grid, dim3(64), params, 0, stream);
 }
 
 }  // namespace tbq4

@@ -224,3 +224,15 @@ def test_mixed_format_row_bytes_and_argument_errors(L):
     assert pre(mc(kf=2, vf=1), n_past=60, n_q=5) == _lib.ERR_CAPACITY
     assert pre(mc(kf=1, vf=2), hq=6) == _lib.ERR_UNSUPPORTED   # G = 3
     assert pre(mc(kf=1, vf=1), n_q=0) == _lib.ERR_CAPACITY
+
+    def ver(cache, hq=8, n_past=10, n_q=3, p=0, wb=ws):
+        return L.tbq4_mixed_attn_verify(ctypes.byref(cache), FAKE, 0, hq, n_past, n_q, 0.1, FAKE,
+                                        1, p, FAKE, wb, None)
+    assert ver(mc(kf=3, vf=0)) == _lib.ERR_UNSUPPORTED    # q8_0: decode-only
+    assert ver(mc(kf=1, vf=3)) == _lib.ERR_UNSUPPORTED
+    assert ver(mc(kf=4, vf=1)) == _lib.ERR_UNSUPPORTED
+    assert ver(mc(kf=2, vf=1), n_past=62, n_q=3) == _lib.ERR_CAPACITY
+    assert ver(mc(kf=1, vf=2), n_q=5) == _lib.ERR_UNSUPPORTED
+    assert ver(mc(kf=2, vf=2), hq=18) == _lib.ERR_UNSUPPORTED  # G = 9
+    assert ver(mc(kf=1, vf=1), wb=16) == _lib.ERR_WORKSPACE
+    assert ver(mc(kf=2, vf=0), p=1025) == _lib.ERR_INVALID_ARG

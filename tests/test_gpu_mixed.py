@@ -177,3 +177,51 @@ def test_prefill_formats(kf, vf):
         same = tb.attn_prefill_chunk(plain, torch.from_numpy(q).cuda(), n_past, scale,
                                      out_dtype=torch.float32).cpu().numpy()
         assert np.array_equal(same, out)
+
+
+VERIFY_SHAPES = [   # B, H, G, n_past, n_q, cap, P
+    (2, 2, 4, 301, 3, 320, 0),
+    (1, 1, 8, 5, 4, 16, 1),
+    (3, 2, 1, 70, 1, 80, 3),
+]
+
+
+@pytest.mark.parametrize("kf,vf", PREFILL_FORMATS)
+@pytest.mark.parametrize("shape", range(len(VERIFY_SHAPES)))
+def test_verify_formats(kf, vf, shape):
+    """Multi-query verify (query i at n_past + i sees slots 0 .. n_past + i)
+    on K and V stored as TBQ4, TBQ3 or fp16, against the fp64 definition on
+    the dequantised tensors; unused slots hold 0xFF bytes that must not
+    leak."""
+    B, H, G, n_past, n_q, cap, P = VERIFY_SHAPES[shape]
+    rng = np.random.default_rng(70 + kf + 4 * vf + 16 * shape)
+    seed, scale = 9 + shape, 0.1
+    T = n_past + n_q
+    k = rng.standard_normal((B, T, H, 128)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, 128)).astype(np.float32)
+    q = rng.standard_normal((B, n_q, H * G, 128)).astype(np.float32)
+    cache = tb.MixedKVCache(B, H, cap, kf, vf, sign_seed=seed)
+    cache.k.fill_(0xFF)
+    cache.v.fill_(0xFF)
+    tb.mixed_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    kb, kh = _oracle_tensor(k, kf, seed)
+    vb, vh = _oracle_tensor(v, vf, seed)
+    assert np.array_equal(cache.k[:, :, :T].cpu().numpy(), kb), "K bytes"
+    assert np.array_equal(cache.v[:, :, :T].cpu().numpy(), vb), "V bytes"
+    out = tb.mixed_attn_verify(cache, torch.from_numpy(q).cuda(), n_past, scale, n_splits=P,
+                               out_dtype=torch.float32).cpu().numpy()
+    ref = np.empty(out.shape, np.float64)
+    for b in range(B):
+        for g in range(H):
+            for i in range(n_q):
+                n = n_past + i + 1
+                ref[b, i, g * G:(g + 1) * G] = o.attn_decode_rows_ref(
+                    q[b, i, g * G:(g + 1) * G], kh[b, g, :n], vh[b, g, :n], scale)
+    check_attn(out, ref, False, f"verify k{kf} v{vf} shape {VERIFY_SHAPES[shape]}")
+    if (kf, vf) == (tb.FMT_TBQ4, tb.FMT_TBQ4):   # the TBQ4 call computes the same
+        plain = tb.KVCache(B, H, cap, sign_seed=seed)
+        plain.k.copy_(cache.k)
+        plain.v.copy_(cache.v)
+        same = tb.attn_verify(plain, torch.from_numpy(q).cuda(), n_past, scale, n_splits=P,
+                              out_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(same, out)
