@@ -49,7 +49,7 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "3e302e048ee21bfe96b008107581fb1ecd9b7d0af5e5dd524ee28df52716e5bc",
+TRAFFIC = {"sources_sha256": "6e2223fa1661e083fcc64eb49fa4240ac759f0914d28729f78c704dcea210364",
            "n_splits": 64, "fetch_kib": 271191.9, "fetch_factor": 2.0,
            "write_kib": 8704.0, "write_factor": 1.0}
 
