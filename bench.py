@@ -49,7 +49,7 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "6e2223fa1661e083fcc64eb49fa4240ac759f0914d28729f78c704dcea210364",
+TRAFFIC = {"sources_sha256": "fff67196a051cd10627606c9e6e88320477475794c0f0ceb8c5f166641bcb3a2",
            "n_splits": 64, "fetch_kib": 271191.9, "fetch_factor": 2.0,
            "write_kib": 8704.0, "write_factor": 1.0}
 
@@ -77,6 +77,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-contexts", action="store_true",
+                   help="skip the 16K and 262K decode measurements")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-formats", dest="formats", action="store_false",
                    help="skip the decode timings of the TBQ3 / fp16 cache formats")
@@ -349,6 +351,111 @@ def bench_verify(tb, torch, args, cache, w, n_q=4):
             "query_tokens_per_s": B * n_q / (ms * 1e-3)}
 
 
+def bench_contexts(tb, torch, args):
+    """Decode steps at the two other context lengths of the workloads: 16384
+    slots (batch 1, one layer; step = append one token + decode, 200 steps)
+    and the long decode (batch 1, 4 layers, prefix 262080 slots, then 64
+    steps that each append one token per layer and decode it over pos + 1
+    slots, layers back to back).  Automatic split counts; every call goes
+    through the library's decode entry point (split kernel + merge)."""
+    from workloads import WORKLOADS, K, V, kv_tensor, q_decode
+    res = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def kv_step_bytes(n_kv, H, Hq):
+        # packed K+V attended, q in, fp16 out, the appended token (fp32 in, blocks out)
+        return n_kv * H * 2 * 66 + Hq * 128 * 4 + Hq * 128 * 2 + 2 * H * (128 * 4 + 66)
+
+    # 16K: one layer, the appended token is the workload's last row
+    w = WORKLOADS["decode16k"]
+    H, Hq, T = w.n_kv_heads, w.n_q_heads, w.n_ctx
+    cache = tb.KVCache(1, H, T)
+    k = torch.from_numpy(kv_tensor(w, 0, K, 0, T)).cuda()
+    v = torch.from_numpy(kv_tensor(w, 0, V, 0, T)).cuda()
+    tb.quantize_append(cache, k, v, 0)
+    k_new, v_new = k[:, T - 1:].contiguous(), v[:, T - 1:].contiguous()
+    q = torch.from_numpy(q_decode(w)).cuda()
+    out = torch.empty((1, Hq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.empty(tb.decode_workspace_bytes(1, H, Hq, T, 0), dtype=torch.uint8, device="cuda")
+    n = 200
+
+    def step16():
+        tb.quantize_append(cache, k_new, v_new, T - 1)
+        tb.attn_decode(cache, q, T, w.softmax_scale, out=out, workspace=ws)
+
+    for _ in range(max(args.warmup, 20)):
+        step16()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        step16()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    assert torch.isfinite(out.float()).all()
+    byt = kv_step_bytes(T, H, Hq)
+    res.append({"workload": "decode16k: batch 1, 8 KV / 64 query heads, 16384 slots, one layer; "
+                            "step = append one token + decode",
+                "n_splits": tb.decode_auto_splits(1, H, T), "steps": n, "ms_per_step": round(ms, 5),
+                "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tokens_per_s": round(1 / (ms * 1e-3), 1)})
+    log(f"decode16k: {ms:.4f} ms/step, {byt / (ms * 1e-3) / 1e9:.0f} GB/s")
+    del cache, k, v, k_new, v_new, ws
+
+    # 262K: four layers, prefix filled, then the 64 steps in the workload's order
+    w = WORKLOADS["longdecode"]
+    H, Hq, T0 = w.n_kv_heads, w.n_q_heads, w.n_ctx
+    T = T0 + w.steps
+    caches, new_k, new_v = [], [], []
+    for layer in range(w.layers):
+        log(f"longdecode: layer {layer}: drawing and appending {T} rows")
+        c = tb.KVCache(1, H, T)
+        xk = kv_tensor(w, layer, K, 0, T)
+        xv = kv_tensor(w, layer, V, 0, T)
+        new_k.append(torch.from_numpy(xk[:, T0:].copy()).cuda())
+        new_v.append(torch.from_numpy(xv[:, T0:].copy()).cuda())
+        for a in range(0, T0, 32768):
+            b = min(T0, a + 32768)
+            tb.quantize_append(c, torch.from_numpy(np.ascontiguousarray(xk[:, a:b])).cuda(),
+                               torch.from_numpy(np.ascontiguousarray(xv[:, a:b])).cuda(), a)
+        del xk, xv
+        caches.append(c)
+    torch.cuda.synchronize()
+    qs = [[torch.from_numpy(q_decode(w, layer, st)).cuda() for st in range(w.steps)]
+          for layer in range(w.layers)]
+    out = torch.empty((1, Hq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.empty(tb.decode_workspace_bytes(1, H, Hq, T, 0), dtype=torch.uint8, device="cuda")
+    for _ in range(max(args.warmup, 5)):          # warm-up on the prefix (no append)
+        for layer in range(w.layers):
+            tb.attn_decode(caches[layer], qs[layer][0], T0, w.softmax_scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for st in range(w.steps):
+        pos = T0 + st
+        for layer in range(w.layers):
+            tb.quantize_append(caches[layer], new_k[layer][:, st:st + 1], new_v[layer][:, st:st + 1],
+                               pos)
+            tb.attn_decode(caches[layer], qs[layer][st], pos + 1, w.softmax_scale, out=out,
+                           workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / w.steps
+    assert torch.isfinite(out.float()).all()
+    byt = sum(w.layers * kv_step_bytes(T0 + st + 1, H, Hq) for st in range(w.steps)) / w.steps
+    res.append({"workload": "longdecode: batch 1, 8 KV / 64 query heads, 4 layers, prefix 262080 "
+                            "slots, 64 steps of (append one token, decode) per layer, layers back "
+                            "to back; step = all 4 layers",
+                "n_splits": tb.decode_auto_splits(1, H, T), "steps": w.steps,
+                "ms_per_step": round(ms, 5), "ms_per_layer": round(ms / w.layers, 5),
+                "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "tokens_per_s": round(1 / (ms * 1e-3), 1)})
+    log(f"longdecode: {ms:.4f} ms/step (4 layers), {byt / (ms * 1e-3) / 1e9:.0f} GB/s")
+    del caches, new_k, new_v, qs, ws
+    return res
+
+
 def bench_prefill(tb, torch, args):
     from workloads import WORKLOADS, K, V, kv_tensor, q_prefill
     w = WORKLOADS["prefill"]
@@ -477,6 +584,7 @@ def main():
     dec = bench_decode(tb, torch, args)
     log(f"decode: {dec['ms']:.4f} ms/step, kernel {dec['kernel_ms']:.4f} ms, "
         f"{dec['achieved']:.0f} GB/s")
+    ctx = None if args.no_contexts else bench_contexts(tb, torch, args)
     pre = None if args.no_prefill else bench_prefill(tb, torch, args)
     if pre:
         log(f"prefill: {pre['attention_ms']:.3f} ms, {pre['tflops']:.1f} TFLOP/s")
@@ -543,6 +651,7 @@ def main():
                       "steps, run after the event-free loop that gives ms_per_step",
         },
         "cpu_baseline": cpu,
+        "contexts": ctx,
         "prefill": pre,
     }
     print(json.dumps(line), flush=True)

@@ -626,28 +626,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge: o = R^T (sum_p 2^(m_p - M) o'_p / sum_p 2^(m_p - M) l_p), one
-// 256-thread workgroup per (sequence, query head), in one pass over the
-// partials.  Wavefront w takes splits w, w + 4, ... in chunks of 16 (lane
+// workgroup of NW wavefronts per (sequence, query head), in one pass over the
+// partials.  Wavefront w takes splits w, w + NW, ... in chunks of 16 (lane
 // holds dims lane and lane + 64), all loads of a chunk in flight together,
-// combined under a running maximum; the four wavefronts' sums meet in LDS,
+// combined under a running maximum; the wavefronts' sums meet in LDS,
 // rescaled to the common maximum, and wavefront 0 normalises, applies the
 // inverse rotation and stores.  Empty splits carry m = -inf and weigh 0.
-template <typename OT>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  __shared__ float red[4][130];   // o'[128], l, m per wavefront
+// NW grows with the split count (16 NW splits per round) so that up to 256
+// splits are read in one round of loads.
+template <typename OT, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float red[NW][130];   // o'[128], l, m per wavefront
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int P = a.n_splits;
   const float *base = a.ws + ((size_t)b * a.n_q_heads + h) * P * 130;
 
   float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int p0 = wave; p0 < P; p0 += 64) {
+  for (int p0 = wave; p0 < P; p0 += 16 * NW) {
     float mp[16], lp[16], x0[16], x1[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       // splits past P reread split p0 (valid: p0 < P) and weigh 0, so that
       // the 64 loads issue together without branches
-      const int p = p0 + 4 * u;
+      const int p = p0 + NW * u;
       const float *bp = base + (size_t)(p < P ? p : p0) * 130;
       mp[u] = bp[0];
       lp[u] = bp[1];
@@ -656,7 +658,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      if (p0 + 4 * u >= P) mp[u] = -INFINITY;
+      if (p0 + NW * u >= P) mp[u] = -INFINITY;
     float cm = M;
 #pragma unroll
     for (int u = 0; u < 16; ++u) cm = fmaxf(cm, mp[u]);
@@ -682,11 +684,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (wave != 0) return;
-  const float Mx = fmaxf(fmaxf(red[0][129], red[1][129]), fmaxf(red[2][129], red[3][129]));
+  float Mx = red[0][129];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) Mx = fmaxf(Mx, red[w][129]);
   o0 = o1 = L = 0.0f;
   if (Mx != -INFINITY) {   // every split empty (a zero-length sequence): output 0
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float sw = __builtin_amdgcn_exp2f(red[w][129] - Mx);
       o0 = fmaf(sw, red[w][lane], o0);
       o1 = fmaf(sw, red[w][64 + lane], o1);
@@ -748,11 +752,19 @@ hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hi
 
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream) {
   dim3 grid(a.n_q_heads, batch);
-  if (out_dtype == 0)
-    hipLaunchKernelGGL(decode_merge_kernel<float>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<_Float16>, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  // wavefronts per workgroup: all splits in one round of 16 per wavefront
+  const int nw = a.n_splits <= 64 ? 4 : a.n_splits <= 128 ? 8 : 16;
+  static const void *const kernels[2][3] = {
+      {reinterpret_cast<const void *>(&decode_merge_kernel<float, 4>),
+       reinterpret_cast<const void *>(&decode_merge_kernel<float, 8>),
+       reinterpret_cast<const void *>(&decode_merge_kernel<float, 16>)},
+      {reinterpret_cast<const void *>(&decode_merge_kernel<_Float16, 4>),
+       reinterpret_cast<const void *>(&decode_merge_kernel<_Float16, 8>),
+       reinterpret_cast<const void *>(&decode_merge_kernel<_Float16, 16>)}};
+  const void *fn = kernels[out_dtype == 0 ? 0 : 1][nw == 4 ? 0 : nw == 8 ? 1 : 2];
+  DecodeArgs arg = a;
+  void *params[] = {&arg};
+  return hipLaunchKernel(fn, grid, dim3(64 * nw), params, 0, stream);
 }
 
 }  // namespace tbq4
