@@ -37,17 +37,30 @@ __device__ __forceinline__ double half_value(int h) {
 // Pattern of the binary16 value nearest sqrt(ms): the largest h in
 // [0, 0x7BFF] whose lower midpoint mid(h) = (value(h-1)+value(h))/2 lies
 // below sqrt(ms) -- or equals it with h even.  mid(h) has <= 12 significant
-// bits, so mid(h)^2 is exact and the test never takes a square root.
+// bits, so mid(h)^2 is exact and the test takes no square root.
+__device__ __forceinline__ bool below_sqrt(int h, double ms) {   // 1 <= h <= 0x7BFF
+  const double m = (half_value(h - 1) + half_value(h)) * 0.5;
+  const double m2 = m * m;
+  return (m2 < ms) || (m2 == ms && (h & 1) == 0);
+}
+
+// The search starts from sqrt(ms) rounded through binary32 to binary16,
+// which is never more than one pattern away from the answer (the rounding
+// near every midpoint was checked exhaustively), and moves by the exact test
+// above, up to two patterns each way; zero, NaN and overflow give the
+// patterns the full search gives (0, 0, 0x7BFF).
 __device__ __forceinline__ int half_round_sqrt(double ms) {
-  int lo = 0, hi = 0x7BFF;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const double m = (half_value(mid - 1) + half_value(mid)) * 0.5;
-    const double m2 = m * m;
-    const bool ok = (m2 < ms) || (m2 == ms && (mid & 1) == 0);
-    if (ok) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+  if (!(ms > 0.0)) return 0;
+  const _Float16 c = (_Float16)(float)sqrt(ms);
+  int h = (int)(__builtin_bit_cast(uint16_t, c) & 0x7FFFu);
+  if (h > 0x7BFF) h = 0x7BFF;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (h > 0 && !below_sqrt(h, ms)) --h;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (h < 0x7BFF && below_sqrt(h + 1, ms)) ++h;
+  return h;
 }
 
 template <typename T> __device__ __forceinline__ double load_exact(const T *p);
@@ -63,7 +76,7 @@ template <typename T, int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   constexpr int64_t kBB = FMT == kFmtTbq3 ? kBlockBytes3 : kBlockBytes;   // bytes per block
   const int lane = threadIdx.x & 63;
-  const int64_t gblock = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t gblock = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tensor = gblock >= a.blocks_per_tensor ? 1 : 0;
   const int64_t i = gblock - (int64_t)tensor * a.blocks_per_tensor;
   // the grid is rounded up to whole 4-wavefront workgroups: wavefronts past
@@ -78,9 +91,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     dst = a.dst[0] + i * kBB;
   } else {
     // source [batch][n_new][n_kv_heads][128]; cache [batch][n_kv_heads][capacity][66]
-    const int64_t h = i % a.n_kv_heads;
-    const int64_t t = (i / a.n_kv_heads) % a.n_new;
-    const int64_t b = i / ((int64_t)a.n_kv_heads * a.n_new);
+    int64_t h, t, b;
+    if (a.blocks_per_tensor <= 0x7FFFFFFF) {   // 32-bit index arithmetic
+      const uint32_t i32 = (uint32_t)i, nh = (uint32_t)a.n_kv_heads, nn = (uint32_t)a.n_new;
+      const uint32_t q = i32 / nh;
+      h = i32 - q * nh;
+      t = q % nn;
+      b = q / nn;
+    } else {
+      h = i % a.n_kv_heads;
+      t = (i / a.n_kv_heads) % a.n_new;
+      b = i / ((int64_t)a.n_kv_heads * a.n_new);
+    }
     // first slot of this sequence: a host value, or per sequence from device
     // memory (slots outside [0, capacity) are skipped; the whole wavefront
     // leaves together)
