@@ -1,7 +1,7 @@
 """Benchmark of the TBQ4 attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--splits P]
-                    [--no-prefill] [--no-cpu-baseline] [--no-formats]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--splits P] [--settle S]
+                    [--no-prefill] [--no-cpu-baseline] [--no-formats] [--no-contexts]
 
 One step = one pass of the whole decode hot path over the decode128k workload
 (batch 4 independent sequences, 8 KV / 64 query heads, head_dim 128, 131072
@@ -16,10 +16,12 @@ K/V then causal attention) is timed in the same run and reported under
 The same decode rows stored as TBQ3, q8_0 or fp16 K / V tensors (mixed
 formats) are timed under "formats" (one decode call per format pair, KV GB/s),
 and the prefill chunk over TBQ3 and fp16 caches under "prefill"."formats".
+Decode at 16384 slots (batch 1) and the 4-layer long decode at 262144 slots
+(batch 1, 64 append + decode steps per layer) are timed under "contexts".
 
-Before the W warm-up steps, 60 untimed steps (~8 ms) let the clocks settle:
-the first milliseconds of sustained load run faster, then the clocks dip and
-settle.  The step value is timed over K steps without any event markers.  The
+Before the W warm-up steps, S untimed steps (default 1000, ~0.12 s) let the
+clocks settle: the first milliseconds of sustained load run faster, then the
+clocks dip and recover over tens of milliseconds.  The step value is timed over K steps without any event markers.  The
 dominant kernel's roofline entry uses HIP events on the stream the kernels run
 on, recorded by the dispatch of every decode-partial launch (start and end of
 that kernel's execution) in a second timed loop of the same K steps, run right
@@ -49,9 +51,9 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "fff67196a051cd10627606c9e6e88320477475794c0f0ceb8c5f166641bcb3a2",
-           "n_splits": 64, "fetch_kib": 271191.9, "fetch_factor": 2.0,
-           "write_kib": 8704.0, "write_factor": 1.0}
+TRAFFIC = {"sources_sha256": "0a079e35d8b9883805b2351d872aaa86816c1e5263d9b72a1cf02c2bc8400577",
+           "n_splits": 64, "fetch_kib": 271200.9, "fetch_factor": 2.0,
+           "write_kib": 8704.1, "write_factor": 1.0}
 
 
 def measured_traffic(n_splits):
@@ -76,6 +78,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--settle", type=int, default=SETTLE_STEPS,
+                   help="untimed decode steps before the warm-up steps (clock settling)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-contexts", action="store_true",
                    help="skip the 16K and 262K decode measurements")
@@ -170,10 +174,10 @@ def bench_decode(tb, torch, args):
                                events=None if i is None else hip.pair(i))
         tb.attn_decode_merge(ws, B, Hq, P, cache.sign_seed, out=out)
 
-    # Under sustained load the clocks dip within ~3 ms and settle after
-    # ~8 ms; the settle steps run the step long enough that both timed loops
-    # see the settled state rather than that transient.
-    for _ in range(SETTLE_STEPS):
+    # Under sustained load the clocks dip within ~4 ms and recover over tens
+    # of ms; the settle steps run the step long enough that both timed loops
+    # see the steady state rather than that transient.
+    for _ in range(args.settle):
         step()
     for _ in range(args.warmup):
         step()
@@ -224,8 +228,10 @@ def bench_decode(tb, torch, args):
     }
 
 
-# untimed decode steps run before the warm-up steps (clock settling)
-SETTLE_STEPS = 60
+# untimed decode steps run before the warm-up steps: under sustained load the
+# clocks dip within a few ms and take tens of ms to recover, so the timed steps
+# start after ~0.1 s of decode (the steady state of a decode loop)
+SETTLE_STEPS = 1000
 
 # (K format, V format) pairs timed beside the TBQ4 cache on the same rows
 FORMAT_NAMES = {0: "tbq4", 1: "f16", 2: "tbq3", 3: "q8_0"}
@@ -309,7 +315,7 @@ def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    for _ in range(args.warmup):
+    for _ in range(args.settle + args.warmup):   # the same clock settling as the eager loop
         g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -386,6 +386,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       sk[lane] = dk;
       sv[lane] = dv;
     }
+    // a V scale of 256 or more (or an unused slot's bits) keeps the running
+    // maximum exact for this tile: P~ = p d^V must stay below the fp16 range
+    bool vbig = VF == kFmtQ8;
+    if constexpr (VF == kFmtTbq4 || VF == kFmtTbq3) vbig = __any(r.sv > 0x5BFFu);
     if constexpr (KF == kFmtQ8) {
       const int tk = lane & 31, c0 = 2 * (lane >> 5);
       const bool dead = kPartial && tok0 + tk >= n_ctx;
@@ -436,9 +440,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
 
     // t = score - m_ref with the running max updated lazily: m_ref is the
-    // running max (0 before the first tile), and only a tile holding a score
-    // above it -- and the first tile -- takes the rescaling path, which
-    // recovers the scores as t + m_ref.
+    // reference maximum (0 before the first tile), and only a tile holding a
+    // score more than kLag above it -- and the first tile -- takes the
+    // rescaling path, which recovers the scores as t + m_ref and moves the
+    // reference to the true maximum.  In between, p = 2^t <= 2^kLag: the
+    // partial state (m_ref, l, O') is exact for any reference, and P~ = p d^V
+    // <= 256 * 255.875 = 65504 stays finite in fp16 (tiles with a larger V
+    // scale, and q8_0 V, use lag 0).  A reference that trails the scores by
+    // up to kLag spares the rescale on data whose scores drift upward.
     const int own = lo_part ? 1 : 0;
     const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
     float t4[4];
@@ -459,7 +468,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         tmax = fmaxf(tmax, t4[e]);
       }
     }
-    if (__any(tmax > 0.0f || m_run == -INFINITY)) {
+    constexpr float kLag = 8.0f;
+    if (__any(tmax > (vbig ? 0.0f : kLag) || m_run == -INFINITY)) {
       float smax = tmax + m_ref;
       smax = fmaxf(smax, __shfl_xor(smax, 8, 64));
       smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
