@@ -286,6 +286,12 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
       sk[lane] = dk;
       sv[lane] = dv;
     }
+    // the decode kernel's lagged reference maximum: a tile rescales a column
+    // group only when a score exceeds the reference by more than 8 (log2), so
+    // p <= 256 and P~ = p d^V <= 65504 while every V scale is below 256; a
+    // tile with a larger scale (or an unused slot's bits) uses lag 0
+    bool vbig = false;
+    if constexpr (VF != kFmtF16) vbig = __any(r.sv > 0x5BFFu);
     fetch(r, t + 1);
 
     // ---- scores: S^T[token][(query, head)] = K . (q'_hi + q'_lo)
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
           tmax = fmaxf(tmax, t4[blk][e]);
         }
       }
-      if (__any(tmax > 0.0f || m_run[c] == -INFINITY)) {
+      if (__any(tmax > (vbig ? 0.0f : 8.0f) || m_run[c] == -INFINITY)) {
         float smax = tmax + m_ref;
         smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
         smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
