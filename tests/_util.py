@@ -28,3 +28,20 @@ def check_attn(got, ref, out_is_f16, what=""):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e} > {REL_L2}"
     return float(d.max()), float(rel)
+
+
+def rising_scores_inputs(rng, B, T, H, G, n_q, vmag):
+    """fp32 q [B][n_q][H*G][128], k, v [B][T][H][128] whose scores rise along
+    the sequence: every key carries a growing multiple (0 .. 100) of one unit
+    direction that the query heads point along (the normalised sum of the
+    queries), so new score maxima keep arriving; V rows of every other run of
+    512 positions are scaled by vmag (block scales above 256 when vmag is
+    large)."""
+    q = rng.standard_normal((B, n_q, H * G, 128))
+    u = q.reshape(-1, 128).sum(axis=0)
+    u /= np.linalg.norm(u)
+    ramp = 100.0 * np.arange(T) / T
+    k = rng.standard_normal((B, T, H, 128)) + ramp[None, :, None, None] * u
+    v = rng.standard_normal((B, T, H, 128))
+    v[:, (np.arange(T) // 512) % 2 == 1] *= vmag
+    return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)

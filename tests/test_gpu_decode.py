@@ -16,7 +16,7 @@ import torch
 import long_context_attention_tbq4_amd as tb
 from oracle import tbq4_oracle as o
 from workloads import WORKLOADS, kv_rows, kv_tensor, q_decode, tiny_inputs
-from _util import check_attn
+from _util import check_attn, rising_scores_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -244,3 +244,24 @@ def test_unused_slots_with_nan_scales_do_not_leak(n_ctx):
         out = tb.attn_decode(cache, torch.from_numpy(q).cuda(), n_ctx, 0.1, n_splits=P,
                              out_dtype=torch.float32)
         check_attn(out.cpu().numpy(), ref, False, f"nan tail n_ctx={n_ctx} P={P}")
+
+
+@pytest.mark.parametrize("vmag", [1.0, 300.0, 5000.0])
+@pytest.mark.parametrize("P", [2, 16])
+def test_rising_scores_and_large_v_scales(vmag, P):
+    """Scores that keep rising make the running maximum move through the
+    whole context, so the reference maximum trails the scores by up to its
+    lag; V blocks with scales above 256 (vmag 300, 5000) are where the lag
+    must fall back to exact maxima, or P~ = p d^V would leave the fp16 range.
+    Outputs are compared after dividing by vmag: the bar relative to the V
+    values being averaged."""
+    rng = np.random.default_rng(int(vmag) + P)
+    B, H, G, T = 1, 2, 8, 4096
+    q, k, v = rising_scores_inputs(rng, B, T, H, G, 1, vmag)
+    cache = tb.KVCache(B, H, T, sign_seed=3)
+    _fill(cache, k, v)
+    kc, vc = _oracle_cache(k, v, 3)
+    out = tb.attn_decode(cache, torch.from_numpy(q[:, 0]).cuda(), T, 1 / math.sqrt(128),
+                         n_splits=P, out_dtype=torch.float32).cpu().numpy()
+    ref = o.attn_decode_ref(q[:, 0], kc, vc, T, 1 / math.sqrt(128), 3)
+    check_attn(out / vmag, ref / vmag, False, f"vmag={vmag} P={P}")

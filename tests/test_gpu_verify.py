@@ -18,7 +18,7 @@ import torch
 import long_context_attention_tbq4_amd as tb
 from oracle import tbq4_oracle as o
 from workloads import WORKLOADS, kv_rows, kv_tensor
-from _util import check_attn
+from _util import check_attn, rising_scores_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -114,3 +114,22 @@ def test_decode128k_verify_sampled():
             n = n_past + i + 1
             ref = o.attn_decode_rows_ref(q[b, i, g * G:(g + 1) * G], Kh[:n], Vh[:n], w.softmax_scale)
             check_attn(out[b, i, g * G:(g + 1) * G], ref, True, f"128k verify b={b} g={g} i={i}")
+
+
+@pytest.mark.parametrize("vmag", [1.0, 300.0, 5000.0])
+def test_rising_scores_and_large_v_scales(vmag):
+    """As the decode test of the same name, for 4 queries per sequence: the
+    lagged reference maximum per column group, exact maxima in tiles with V
+    scales above 256; compared after dividing by vmag."""
+    rng = np.random.default_rng(50 + int(vmag))
+    B, H, G, n_q, n_past = 1, 2, 8, 4, 4092
+    T = n_past + n_q
+    q, k, v = rising_scores_inputs(rng, B, T, H, G, n_q, vmag)
+    cache = tb.KVCache(B, H, T, sign_seed=3)
+    tb.quantize_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    kc = o.quantize_blocks(k.transpose(0, 2, 1, 3), 3)[0]
+    vc = o.quantize_blocks(v.transpose(0, 2, 1, 3), 3)[0]
+    out = tb.attn_verify(cache, torch.from_numpy(q).cuda(), n_past, 1 / math.sqrt(128), n_splits=2,
+                         out_dtype=torch.float32).cpu().numpy()
+    ref = o.attn_prefill_ref(q, kc, vc, n_past, 1 / math.sqrt(128), 3)
+    check_attn(out / vmag, ref / vmag, False, f"vmag={vmag}")
