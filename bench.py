@@ -585,7 +585,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X)", file=sys.stderr)
+              "(the library runs on a single MI355X; sharding is a design note only)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import long_context_attention_tbq4_amd as tb
