@@ -150,8 +150,10 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
  * tbq4_attn_decode_partial: same arguments and checks as tbq4_attn_decode
  * minus the output; writes, for every (sequence b, query head h, split p),
  * 130 fp32 values at workspace + ((b * n_q_heads + h) * n_splits + p) * 130:
- *   [0] m  = max over the split's keys of the score, in log2 units
- *          (softmax_scale * log2(e) * q.k); -inf for an empty split
+ *   [0] m  = the split's reference score, in log2 units (softmax_scale *
+ *          log2(e) * q.k): one of its scores, at most 8 below the split's
+ *          maximum (max - 8 <= m <= max; the kernel moves it only when a
+ *          score exceeds it by more than 8); -inf for an empty split
  *   [1] l  = sum over the split's keys of 2^(score - m)
  *   [2 + i] = sum over the split's keys of 2^(score - m) * v'_i, i = 0..127,
  *          in the ROTATED domain (v' = R v, unnormalised).
