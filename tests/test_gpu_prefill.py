@@ -146,3 +146,9 @@ def test_unused_slots_with_nan_scales_do_not_leak():
                                 out_dtype=torch.float32)
     ref = o.attn_prefill_ref(q, kc, vc, n_past, 0.1, 0)
     check_attn(out.cpu().numpy(), ref, False, "nan tail prefill")
+
+
+def test_bf16_queries():
+    out, ref = _case(2, 2, 8, 300, 70, 376, 1 / math.sqrt(128), seed=4, rng_seed=11,
+                     q_dtype=torch.bfloat16, out_dtype=torch.float16)
+    check_attn(out, ref, True, "bf16 q")

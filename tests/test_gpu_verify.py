@@ -133,3 +133,9 @@ def test_rising_scores_and_large_v_scales(vmag):
                          out_dtype=torch.float32).cpu().numpy()
     ref = o.attn_prefill_ref(q, kc, vc, n_past, 1 / math.sqrt(128), 3)
     check_attn(out / vmag, ref / vmag, False, f"vmag={vmag}")
+
+
+def test_bf16_queries():
+    out, ref = _case(2, 2, 8, 900, 4, 912, 1 / math.sqrt(128), P=3, q_dtype=torch.bfloat16,
+                     rng_seed=9)
+    check_attn(out, ref, False, "bf16 q")
