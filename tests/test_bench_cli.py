@@ -41,3 +41,14 @@ def test_traffic_only_for_the_measured_split_count():
     # either the sources are the measured ones (bytes per launch at least the
     # algorithmic 553 779 200 B) or they changed since (unknown: None)
     assert t is None or t >= 553_779_200
+
+
+def test_defaults_settle_and_switches(monkeypatch):
+    bench = _bench_module()
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert (a.gpus, a.steps, a.warmup, a.splits) == (1, 20, 5, 0)
+    assert a.settle == bench.SETTLE_STEPS >= 600   # timed steps start after the clock dip
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--settle", "60", "--no-contexts", "--no-prefill"])
+    a = bench.parse()
+    assert a.settle == 60 and a.no_contexts and a.no_prefill
