@@ -262,7 +262,7 @@ def bench_format(tb, torch, args, cache, q, out, ws, P, w):
     def call():
         tb.mixed_attn_decode(cache, q, T, w.softmax_scale, n_splits=P, out=out, workspace=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(args.warmup + args.settle // 10):   # clock settling, as for the step
         call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -355,7 +355,7 @@ def bench_verify(tb, torch, args, cache, w, n_q=4):
     n_past = T - n_q
     ws = torch.empty(tb.verify_workspace_bytes(B, cache.n_kv_heads, Hq, n_past, n_q),
                      dtype=torch.uint8, device="cuda")
-    for _ in range(args.warmup):
+    for _ in range(args.warmup + args.settle // 4):   # clock settling, as for the step
         tb.attn_verify(cache, q, n_past, w.softmax_scale, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
