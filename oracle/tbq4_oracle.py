@@ -439,6 +439,31 @@ def attn_decode_rows_ref(q_rows, K, V, softmax_scale):
     return p @ V
 
 
+def attn_prefill_rows_ref(q_rows, K, V, n_past, rows, softmax_scale, chunk=64):
+    """Causal prefill attention for some query rows of one KV-head group,
+    against dequantised K, V (fp64).
+
+    q_rows (r, G, 128): the G query heads of chunk queries ``rows`` (r
+    indices); K, V (n, 128) with n >= n_past + max(rows) + 1.  Query i sits at
+    absolute position n_past + i and attends keys 0 .. n_past + i: its scores
+    against later keys are -inf before the softmax (weight exactly 0).  Rows
+    are taken ``chunk`` at a time so that K is read once per chunk.  Returns
+    (r, G, 128)."""
+    q_rows = np.asarray(q_rows, np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    r, G, D = q_rows.shape
+    out = np.empty((r, G, D), dtype=np.float64)
+    for c0 in range(0, r, chunk):
+        idx = rows[c0:c0 + chunk]
+        n_keys = n_past + idx + 1                          # keys each row sees
+        top = int(n_keys.max())
+        s = softmax_scale * (q_rows[c0:c0 + chunk].reshape(-1, D) @ K[:top].T)
+        s = s.reshape(len(idx), G, top)
+        s = np.where(np.arange(top)[None, None, :] < n_keys[:, None, None], s, -np.inf)
+        out[c0:c0 + chunk] = _softmax_rows(s) @ V[:top]
+    return out
+
+
 def attn_prefill_ref(q, k_cache, v_cache, n_past, softmax_scale, seed=0,
                      rows=None, kv_heads=None):
     """Causal prefill-chunk attention.

@@ -97,3 +97,74 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes_fail_the_pin(name):
     assert _pin(MUTANTS[name]) != [], f"the pin does not catch: {name}"
+
+
+# --------------------------------------------------------------------------
+# attn_prefill_rows_ref: causal rows of one head group, batched.  Pinned
+# against torch SDPA with a lower-right causal mask (fp64, grouped heads) and
+# against the oracle's whole-cache attn_prefill_ref.
+# --------------------------------------------------------------------------
+def _pin_prefill_rows(fn):
+    from torch.nn.attention.bias import causal_lower_right
+    failed = []
+    rng = np.random.default_rng(32)
+    for (G, n_past, n_q, rows, chunk) in ((4, 20, 9, range(9), 64), (8, 0, 70, range(70), 16),
+                                          (2, 130, 40, [0, 5, 39, 17, 3], 2)):
+        T = n_past + n_q
+        K = rng.standard_normal((T + 3, 128)) * 1.5        # keys past T must not count
+        V = rng.standard_normal((T + 3, 128))
+        q = rng.standard_normal((n_q, G, 128))
+        want = F.scaled_dot_product_attention(
+            torch.from_numpy(q).transpose(0, 1)[None], torch.from_numpy(K[:T])[None, None],
+            torch.from_numpy(V[:T])[None, None], attn_mask=causal_lower_right(n_q, T),
+            scale=0.2, enable_gqa=True)[0].transpose(0, 1).numpy()
+        rows = list(rows)
+        try:
+            got = fn(q[rows], K, V, n_past, rows, 0.2, chunk)
+        except Exception:
+            failed.append(f"sdpa G={G}")
+            continue
+        if got.shape != (len(rows), G, 128) or not np.allclose(got, want[rows], rtol=1e-12,
+                                                               atol=1e-13):
+            failed.append(f"sdpa G={G} n_past={n_past}")
+    # against attn_prefill_ref on a packed cache
+    n_past, n_q, Hkv, G = 33, 20, 2, 4
+    x = rng.standard_normal((2, 1, Hkv, n_past + n_q, 128)).astype(np.float32)
+    kc, vc = o.quantize_blocks(x[0], seed=5)[0], o.quantize_blocks(x[1], seed=5)[0]
+    q = rng.standard_normal((1, n_q, Hkv * G, 128))
+    ref = o.attn_prefill_ref(q, kc, vc, n_past, 0.09, seed=5)
+    for g in range(Hkv):
+        Kd, Vd = o.dequantize_blocks(kc[0, g], 5), o.dequantize_blocks(vc[0, g], 5)
+        rows = list(range(n_q))
+        got = fn(q[0, :, g * G:(g + 1) * G], Kd, Vd, n_past, rows, 0.09, 8)
+        if not np.allclose(got, ref[0, :, g * G:(g + 1) * G], rtol=1e-12, atol=1e-13):
+            failed.append(f"whole-cache g={g}")
+    return failed
+
+
+def test_prefill_rows_ref_matches_sdpa_and_whole_cache_reference():
+    assert _pin_prefill_rows(o.attn_prefill_rows_ref) == []
+
+
+def _masked(q_rows, K, V, n_past, rows, sc, chunk, off):
+    """attention with keys 0 .. n_past + i + off (off = 0 is the right rule)"""
+    out = []
+    for j, i in enumerate(rows):
+        n = max(1, n_past + int(i) + 1 + off)
+        out.append(o.attn_decode_rows_ref(q_rows[j], K[:n], V[:n], sc))
+    return np.stack(out)
+
+
+PREFILL_MUTANTS = {
+    "diagonal excluded": lambda q, K, V, n_past, rows, sc, ch: _masked(q, K, V, n_past, rows, sc, ch, -1),
+    "one key past the diagonal": lambda q, K, V, n_past, rows, sc, ch: _masked(q, K, V, n_past, rows, sc, ch, 1),
+    "no causal mask": lambda q, K, V, n_past, rows, sc, ch: _masked(q, K, V, n_past, rows, sc, ch,
+                                                                    10 ** 6),
+    "rows ignored": lambda q, K, V, n_past, rows, sc, ch: _masked(q, K, V, n_past,
+                                                                  list(range(len(rows))), sc, ch, 0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_planted_prefill_mistakes_fail_the_pin(name):
+    assert _pin_prefill_rows(PREFILL_MUTANTS[name]) != [], f"the pin does not catch: {name}"
