@@ -24,8 +24,8 @@
 //     take the first 16-token block, those of columns 8-15 the second,
 //   * stages the V index bytes in LDS and reads them back transposed with
 //     ds_read_b64_tr_b8 (8 tokens x 1 byte per lane), dequantises them the
-//     same way and runs O'^T += P~ V on MFMA, with P~ = p d^V rounded to
-//     fp16 (rows 8-15 of the P~ operand are zero),
+//     same way and runs O'^T += P~ V on MFMA, with P~ = p d^V as an fp16
+//     value (rows 0-7 of the P~ operand) plus its fp16 residual (rows 8-15),
 //   * keeps the online-softmax state in the log2 domain.
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
@@ -49,6 +49,16 @@ constexpr int kE4Row = 144;         // LDS bytes per staged TBQ3 (e4m3) or q8_0 
                                     // fall on distinct banks)
 constexpr int kF16Row = 288;        // LDS bytes per staged fp16 V row (256 + pad; 72 dwords
                                     // put the 4 rows of one transposed read on distinct banks)
+
+// Word of the P~ operand for two weights (x0, x1) of a head: lanes 0-7 of
+// each 16-lane row get the fp16 pair nearest (x0, x1); lanes 8-15, whose own
+// weights are zero, get the fp16 pair of what that rounding left out in the
+// lane 8 below.
+__device__ __forceinline__ uint32_t split_f16x2(float x0, float x1) {
+  const uint32_t hw = pk_f16(x0, x1);
+  const int rw = (int)pk_f16_residual(hw, x0, x1);
+  return hw | (uint32_t)__builtin_amdgcn_update_dpp(0, rw, 0x128, 0xF, 0xF, true);
+}
 
 template <typename QT, int KF, int VF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
@@ -75,7 +85,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int head = col & 7;
   const bool lo_part = col >= 8;
   static_assert(kBlk == 2, "the score split between lanes 0-7 and 8-15 pairs two blocks");
-  // lanes of P~ rows 8-15 read zero V scales
+  // lanes of P~ rows 8-15 read zero V scales (their rows carry the residual
+  // of rows 0-7, moved in from lanes 0-7)
   const float *sv_rd = lo_part ? sv + kTile : sv;
   if (lane < 32) sv[kTile + lane] = 0.0f;
   if constexpr (VF == kFmtQ8) {
@@ -490,10 +501,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) t4[e] += shift_t;
     }
 
-    // ---- probabilities and P~ = p d^V in fp16.  P~ rows 0-7 (lanes 0-7 of
-    // each row) hold the heads; rows 8-15 are zero (their lanes read the V
-    // scales from a zero block).  A row needs both blocks' tokens: its own
-    // block from itself, the other from the partner lane.
+    // ---- probabilities and P~ = p d^V, carried as an fp16 value (rows 0-7
+    // of the P~ operand, lanes 0-7 of each row) plus the fp16 rounding of
+    // what that value leaves out (rows 8-15, the same head's row + 8): the
+    // MFMA accumulates both, and the final cross-lane sum adds row h + 8 to
+    // row h, so each weight carries ~22 bits.  A single fp16 would move the
+    // output by up to 2^-11 of the dominant V rows when few keys carry the
+    // weight.  A row needs both blocks' tokens: its own block from itself,
+    // the other from the partner lane.  Lanes 8-15 compute zeros here (they
+    // read the V scales from a zero block) and receive the residual words of
+    // lanes 0-7.
     float psum = 0.0f;
     float p4[4];
 #pragma unroll
@@ -504,16 +521,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     l_run += psum;
     const float4v vd0 = *(const float4v *)(sv_rd + 4 * quarter);        // block 0
     const float4v vd1 = *(const float4v *)(sv_rd + 16 + 4 * quarter);   // block 1
-    float pt[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pt[e] = p4[e] * vd0[e];                 // lanes 0-7: own block 0
-      pt[4 + e] = row_ror8(p4[e]) * vd1[e];   // partner's block 1
-    }
     uint32_t pw[4];   // round to nearest (v_cvt_pk_f16_f32): no truncation bias
+    {
+      float pt[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
+      for (int e = 0; e < 4; ++e) {
+        pt[e] = p4[e] * vd0[e];                 // lanes 0-7: own block 0
+        pt[4 + e] = row_ror8(p4[e]) * vd1[e];   // partner's block 1
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pw[j] = split_f16x2(pt[2 * j], pt[2 * j + 1]);
+    }
     half8 pa[kBlk / 2];
     pa[0] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
     // q8_0 V: one P~ per 32-dim block c, p times that block's scale
@@ -527,13 +545,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         const float *svc = lo_part ? svq + 4 * kTile : svq + c * kTile;
         const float4v q0 = *(const float4v *)(svc + 4 * quarter);
         const float4v q1 = *(const float4v *)(svc + 16 + 4 * quarter);
-        uint32_t qw[4];
+        uint32_t qw[4];   // fp16 value and residual rows, as for the other formats
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          qw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(p4[2 * j] * q0[2 * j]),
-                                                      (_Float16)(p4[2 * j + 1] * q0[2 * j + 1])});
-          qw[2 + j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)(pr[2 * j] * q1[2 * j]),
-                                                          (_Float16)(pr[2 * j + 1] * q1[2 * j + 1])});
+          qw[j] = split_f16x2(p4[2 * j] * q0[2 * j], p4[2 * j + 1] * q0[2 * j + 1]);
+          qw[2 + j] = split_f16x2(pr[2 * j] * q1[2 * j], pr[2 * j + 1] * q1[2 * j + 1]);
         }
         paq[c] = __builtin_bit_cast(half8, u32x4{qw[0], qw[1], qw[2], qw[3]});
       }

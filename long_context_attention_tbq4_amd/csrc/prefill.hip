@@ -20,7 +20,9 @@
 //   * S^T = K Q'^T on v_mfma_f32_32x32x16_f16, with q' split into an fp16
 //     high part and the fp16 residual that both accumulate into the same
 //     fp32 scores (~22 bits of q'), then scales by d^K per key,
-//   * online softmax in the log2 domain, P~ = p d^V in fp16,
+//   * online softmax in the log2 domain, P~ = p d^V in fp16 (plus its fp16
+//     residual as a second PV product in blocks where one key carries more
+//     than 1/32 of a row's running weight),
 //   * O'^T += V^T P~^T on v_mfma_f32_32x32x16_f16 with V^T read straight out
 //     of the row-major LDS tile by ds_read_b64_tr_b16.
 // The epilogue divides by the row sum, applies R^T and stores.
@@ -98,6 +100,9 @@ template <int KF, int VF> struct TileRaw {
 };
 
 constexpr int kWaves = 8;           // wavefronts per workgroup (32 rows each)
+// A 32-key block takes the fp16 residual of P~ as a second PV product when one
+// of its keys carries more than 1/kShareInv of a row's running weight sum.
+constexpr float kShareInv = 32.0f;
 
 template <typename QT, typename OT, int KF, int VF>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
           for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       }
       float psum = 0.0f;
-      half8 pb[2];
+      float pt[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float4v dv4 = *(const float4v *)(&L.sv[buf][kb0 + 8 * m + 4 * half]);
@@ -363,28 +368,49 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
           const int e = 4 * m + e2;
           const float p = __builtin_amdgcn_exp2f(fmaf(s[e], rowscale, -m_log2));
           psum += p;
-          pb[e >> 3][e & 7] = (_Float16)(p * dv4[e2]);
+          pt[e] = p * dv4[e2];
         }
       }
       l_run = l_run * alpha + psum;
+      // A key whose weight is more than 1/kShareInv of the row's running sum
+      // (this lane's half of it: a lower bound) makes the block take the
+      // fp16 residual of P~ as a second PV product.  Keys below that share
+      // enter with one fp16 rounding each, and those roundings average out
+      // over the many keys that then carry the weight.
+      const float p_top = __builtin_amdgcn_exp2f(fmaf(tmax, rowscale, -m_log2));
+      const bool fine = __any(p_top * kShareInv > l_run);
+
+      uint32_t pw[8], rw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
+      if (fine) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+      }
 
       __builtin_amdgcn_s_setprio(0);
-      // ---- O'^T[dim][row] += V^T P~^T
+      // ---- O'^T[dim][row] += V^T P~^T (then V^T times the residual of P~)
+      auto pv = [&](const uint32_t *w) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = kb0 + 16 * ks + tr_row;     // (rows r0 and r0 + 8 share bit 2)
-        const uint8_t *vbase = vb + r0 * kVRowB;
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = kb0 + 16 * ks + tr_row;     // (rows r0 and r0 + 8 share bit 2)
+          const uint8_t *vbase = vb + r0 * kVRowB;
+          const half8 pb = __builtin_bit_cast(half8, u32x4{w[4 * ks], w[4 * ks + 1], w[4 * ks + 2],
+                                                           w[4 * ks + 3]});
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          typedef __attribute__((address_space(3))) short4v lds_s4;
-          const int col = v_swizzle(r0, tr_col + 64 * db);
-          const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
-          const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
-          const short8v vs = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, vs), pb[ks], o[db],
-                                                         0, 0, 0);
+          for (int db = 0; db < 4; ++db) {
+            typedef __attribute__((address_space(3))) short4v lds_s4;
+            const int col = v_swizzle(r0, tr_col + 64 * db);
+            const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
+            const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
+            const half8 vs = __builtin_bit_cast(
+                half8, short8v{ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]});
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vs, pb, o[db], 0, 0, 0);
+          }
         }
-      }
+      };
+      pv(pw);
+      if (fine) pv(rw);
     }
 
     if (more) stage(nxt, buf ^ 1);

@@ -208,6 +208,34 @@ __device__ __forceinline__ void load16_unaligned(rsrc_t r, uint32_t start, uint3
   out[3] = alignbyte(w4, w[3], s);
 }
 
+// ---------------------------------------------------------------------------
+// Weights carried as an fp16 value plus an fp16 residual.  P~ = p d^V enters
+// the PV product as an fp16 MFMA operand; one fp16 rounding (relative 2^-11,
+// the same for all 128 values of a V row) moves the output by up to 2^-11 of
+// the V rows that carry the weight, which matters when few keys dominate.  The
+// residual x - fp16(x) (exact in fp32) rounded to fp16 restores ~22 bits when
+// it is accumulated by a second operand.  Both are written out as
+// instructions -- v_cvt_pk_f16_f32, then v_fma_mix with the fp16 halves as
+// sources -- so that the compiler cannot round the exact product straight to
+// fp16 for the residual while the operand holds the rounding of the fp32
+// product: the operand's value and the one the residual is taken from must be
+// the same number.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pk_f16(float x0, float x1) {
+  uint32_t hw;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hw) : "v"(x0), "v"(x1));
+  return hw;
+}
+// fp16 pair of (x0 - h0, x1 - h1), h = the fp16 halves of hw, each difference
+// rounded once
+__device__ __forceinline__ uint32_t pk_f16_residual(uint32_t hw, float x0, float x1) {
+  uint32_t rw;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(rw) : "v"(hw), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(rw) : "v"(hw), "v"(x1));
+  return rw;
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }

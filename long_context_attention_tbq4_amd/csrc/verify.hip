@@ -20,7 +20,9 @@
 //     q' operands wait in LDS (one 16-byte slot per lane) instead of
 //     registers, which keeps two wavefronts per SIMD for four queries,
 //   * every column is a distinct (query, head), so each lane finishes its
-//     own scores and P~ rows; P~ = p d^V is one fp16, rounded to nearest.
+//     own scores and P~ rows; P~ = p d^V is one fp16, rounded to nearest,
+//     plus its fp16 residual as a second PV product in tiles where one key
+//     carries more than 1/32 of a column's running weight.
 // Partial states use the decode workspace layout with (sequence, query) as
 // the row index, so the decode merge kernel finishes them.
 //
@@ -41,6 +43,9 @@ constexpr int kBlk = kTile / 16;
 constexpr int kVRow = 80;           // staged TBQ4 V row: 64 index bytes + pad
 constexpr int kE4Row = 144;         // staged TBQ3 V row: 128 e4m3 bytes + pad
 constexpr int kF16Row = 288;        // staged fp16 V row: 256 bytes + pad
+// A tile takes the fp16 residual of P~ as a second PV product when one of its
+// keys carries more than 1/kShareInv of a column's running weight sum.
+constexpr float kShareInv = 32.0f;
 }  // namespace
 
 template <typename QT, int CG, int KF, int VF>
@@ -328,7 +333,8 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     }
     __syncthreads();
 
-    half8 pa[CG];
+    half8 pa[CG], pr[CG];
+    bool fine = false;
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
       const int qi = 2 * c + qsub;
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) t4[blk][e] += shift_t;
       }
-      float psum = 0.0f;
+      float psum = 0.0f, p_top = 0.0f;
       float pt[8];
 #pragma unroll
       for (int blk = 0; blk < kBlk; ++blk) {
@@ -377,19 +383,32 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(t4[blk][e]);
           psum += p;
+          p_top = fmaxf(p_top, p);
           pt[4 * blk + e] = p * vd[e];
         }
       }
       l_run[c] += psum;
       uint32_t pw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pw[j] = __builtin_bit_cast(uint32_t, fp16x2{(_Float16)pt[2 * j], (_Float16)pt[2 * j + 1]});
+      for (int j = 0; j < 4; ++j) pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
       pa[c] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      // a key with more than 1/kShareInv of its column's running weight sum
+      // (this lane's quarter of it: a lower bound) sends the residual of P~
+      // through a second PV product
+      pr[c] = half8{};
+      if (__any(p_top * kShareInv > l_run[c])) {
+        fine = true;
+        uint32_t rw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+        pr[c] = __builtin_bit_cast(half8, u32x4{rw[0], rw[1], rw[2], rw[3]});
+      }
     }
 
-    // ---- O'^T += P~ V for every column group (V dequantised once)
-    if constexpr (VF == kFmtTbq4) {
+    // ---- O'^T += P~ V for every column group (V dequantised once); in a
+    // tile where the residual of P~ is carried, a second pass over the
+    // staged V takes it
+    auto pv_tbq4 = [&](const half8 *w) {
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
         typedef __attribute__((address_space(3))) int2v lds_i2;
@@ -399,10 +418,14 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
-          o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], ve, o[c][2 * cg], 0, 0, 0);
-          o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vo, o[c][2 * cg + 1], 0, 0, 0);
+          o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[c], ve, o[c][2 * cg], 0, 0, 0);
+          o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[c], vo, o[c][2 * cg + 1], 0, 0, 0);
         }
       }
+    };
+    if constexpr (VF == kFmtTbq4) {
+      pv_tbq4(pa);
+      if (fine) pv_tbq4(pr);
     } else {
       // TBQ3: e4m3 bytes, one byte-transposed read per 16 dims; fp16: two
       // 16-bit transposed reads per 16 dims (dim 16 db + col)
@@ -424,6 +447,28 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 #pragma unroll
         for (int c = 0; c < CG; ++c)
           o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vv, o[c][db], 0, 0, 0);
+      }
+      if (fine) {
+        // the residual of P~ through a second pass over the staged V
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          half8 vv;
+          if constexpr (VF == kFmtTbq3) {
+            typedef __attribute__((address_space(3))) int2v lds_i2;
+            const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+            vv = e4m3x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]);
+          } else {
+            typedef __attribute__((address_space(3))) short4v lds_s4;
+            const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vlds + tr16_off + 32 * db));
+            const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4 *)(vlds + tr16_off + 16 * kF16Row + 32 * db));
+            const short8v s8 = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+            vv = __builtin_bit_cast(half8, s8);
+          }
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr[c], vv, o[c][db], 0, 0, 0);
+        }
       }
     }
   };

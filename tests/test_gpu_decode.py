@@ -134,21 +134,29 @@ def test_decode16k_workload_full():
     for scale in (w.softmax_scale, 1 / math.sqrt(128)):
         ref = o.attn_decode_ref(q, kc, vc, T, scale)
         for P in (0, 16, 64):
-            out = tb.attn_decode(cache, torch.from_numpy(q).cuda(), T, scale, n_splits=P)
-            check_attn(out.float().cpu().numpy(), ref, True, f"16k scale={scale} P={P}")
+            for od in (torch.float16, torch.float32):
+                out = tb.attn_decode(cache, torch.from_numpy(q).cuda(), T, scale, n_splits=P,
+                                     out_dtype=od)
+                check_attn(out.float().cpu().numpy(), ref, od == torch.float16,
+                           f"16k scale={scale} P={P} {od}")
 
 
 @pytest.mark.slow
-def test_decode128k_workload_sampled():
+@pytest.mark.timeout(900)
+def test_decode128k_workload_full():
     """Decode at 131072 and at 98304 slots, batch 4, Student-t KV with channel
     scales (the decode96k rows are the first 98304 of the same recipe): the
-    whole cache is filled on the GPU; two (sequence, KV head) rows are
-    re-quantised by the oracle (bytes compared) and their 16 query heads
-    checked, for split counts 16 .. 256 and the automatic one."""
+    whole cache is filled on the GPU; every (sequence, KV head) row is
+    re-quantised by the oracle in worker processes (all appended bytes
+    compared) and every output of every query head is checked, for split
+    counts 16 .. 256 and the automatic one, with fp16 output and with fp32
+    output at the bare bound."""
+    from _rows import decode_row, pool_map
     w = WORKLOADS["decode128k"]
     T = w.n_ctx
     T96 = WORKLOADS["decode96k"].n_ctx
-    cache = tb.KVCache(w.batch, w.n_kv_heads, T)
+    B, H, G = w.batch, w.n_kv_heads, w.n_q_heads // w.n_kv_heads
+    cache = tb.KVCache(B, H, T)
     for t0 in range(0, T, 32768):
         t1 = t0 + 32768
         k = kv_tensor(w, 0, 0, t0, t1)
@@ -156,21 +164,24 @@ def test_decode128k_workload_sampled():
         tb.quantize_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), t0)
     q = q_decode(w)
     qt = torch.from_numpy(q).cuda()
-    outs = {(n, P): tb.attn_decode(cache, qt, n, w.softmax_scale, n_splits=P).float().cpu().numpy()
-            for n in (T96, T) for P in (0, 16, 32, 64, 128, 256)}
-    G = w.n_q_heads // w.n_kv_heads
-    for (b, g) in ((0, 0), (3, 5)):
-        K = kv_rows(w, 0, 0, b, g, 0, T)
-        V = kv_rows(w, 0, 1, b, g, 0, T)
-        kc = o.quantize_blocks(K)[0]
-        vc = o.quantize_blocks(V)[0]
-        assert np.array_equal(cache.k[b, g].cpu().numpy(), kc)
-        assert np.array_equal(cache.v[b, g].cpu().numpy(), vc)
-        Kh, Vh = o.dequantize_blocks(kc), o.dequantize_blocks(vc)
+    splits = (0, 16, 32, 64, 128, 256)
+    outs = {(n, P, od): tb.attn_decode(cache, qt, n, w.softmax_scale, n_splits=P,
+                                       out_dtype=od).float().cpu().numpy()
+            for n in (T96, T) for P in splits for od in (torch.float16, torch.float32)}
+    kg, vg = cache.k.cpu().numpy(), cache.v.cpu().numpy()
+    del cache
+    torch.cuda.empty_cache()
+    jobs = [("decode128k", 0, b, g, T,
+             [(n, q[b, g * G:(g + 1) * G], n, w.softmax_scale) for n in (T96, T)])
+            for b in range(B) for g in range(H)]
+    refs = {}
+    for (_, _, b, g, _, _), (kc, vc, r) in zip(jobs, pool_map(decode_row, jobs)):
+        assert np.array_equal(kg[b, g], kc), f"K bytes b={b} g={g}"
+        assert np.array_equal(vg[b, g], vc), f"V bytes b={b} g={g}"
         for n in (T96, T):
-            ref = o.attn_decode_rows_ref(q[b, g * G:(g + 1) * G], Kh[:n], Vh[:n], w.softmax_scale)
-            for P in (0, 16, 32, 64, 128, 256):
-                check_attn(outs[(n, P)][b, g * G:(g + 1) * G], ref, True, f"n={n} b={b} g={g} P={P}")
+            refs.setdefault(n, np.empty((B, w.n_q_heads, 128)))[b, g * G:(g + 1) * G] = r[n]
+    for (n, P, od), out in outs.items():
+        check_attn(out, refs[n], od == torch.float16, f"n={n} P={P} {od}")
 
 
 def test_two_phase_equals_one_call():
