@@ -37,6 +37,9 @@
  *   - Every pointer argument named as device memory is caller-owned device
  *     memory; the library never allocates, frees or caches device memory and
  *     keeps no mutable global state (calls are re-entrant and thread-safe).
+ *     The one exception is tbq4_attn_decode_noalloc, for callers that cannot
+ *     allocate: it uses a static device array that the library holds per
+ *     device (see its declaration).
  *   - All work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
  *     stream).  No call synchronises.  Order appends before attention on the
  *     same stream.
@@ -142,6 +145,29 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
                              int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
                              void *out, tbq4_dtype out_dtype, int32_t n_splits,
                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Decode attention that allocates nothing and takes no workspace: for
+ * callers that cannot allocate device memory or pass a scratch buffer (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, checks, kernels and results as
+ * tbq4_attn_decode minus the workspace: the split-K partial states go to a
+ * static device array of TBQ4_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends.
+ *   - Calls whose partial states exceed the array (batch * n_q_heads *
+ *     n_splits * 520 bytes, rounded up to 256, with n_splits the automatic
+ *     count when 0 is given) return TBQ4_ERR_WORKSPACE before any HIP call.
+ *   - The array's device address is looked up (hipGetSymbolAddress) on the
+ *     first call on each device; make that first call outside graph capture.
+ *   - All calls on one device share that device's array: calls that overlap
+ *     on one device (different streams, or different threads) race.  Calls
+ *     ordered on one stream do not.  Nothing in the array needs to start at
+ *     zero; the previous call's contents are simply overwritten.
+ * Calls no hipMalloc, hipFree or allocating library routine. */
+#define TBQ4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+tbq4_status tbq4_attn_decode_noalloc(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                     int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
+                                     void *out, tbq4_dtype out_dtype, int32_t n_splits,
+                                     void *hip_stream);
 
 /* The two phases of tbq4_attn_decode, for callers that produce or combine
  * split-K partial states themselves (for example partials computed over

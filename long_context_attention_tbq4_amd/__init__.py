@@ -17,11 +17,12 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS
+from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS, NOALLOC_SCRATCH_BYTES
 
 __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
-    "attn_decode_partial", "attn_decode_merge", "quantize_append_at", "attn_decode_varlen",
+    "attn_decode_partial", "attn_decode_merge", "attn_decode_noalloc", "quantize_append_at",
+    "attn_decode_varlen", "NOALLOC_SCRATCH_BYTES",
     "attn_verify", "verify_workspace_bytes", "MixedKVCache", "mixed_append",
     "mixed_attn_decode", "mixed_attn_prefill_chunk", "mixed_attn_verify", "FMT_TBQ4", "FMT_F16", "FMT_TBQ3", "FMT_Q8_0",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
@@ -320,6 +321,26 @@ def attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None, out_dtype=
                                        float(softmax_scale), _ptr(out), _dtype(out), n_splits,
                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(q.device)), "tbq4_attn_decode")
+    return out
+
+
+def attn_decode_noalloc(cache, q, n_ctx, softmax_scale, n_splits=0, out=None,
+                        out_dtype=torch.float16):
+    """attn_decode without a workspace: the library's static per-device
+    scratch array holds the split-K partial states (nothing is allocated by
+    the call itself; pass ``out`` to allocate nothing at all).  Calls that
+    overlap on one device race; partial states larger than
+    NOALLOC_SCRATCH_BYTES raise TBQ4Error (workspace)."""
+    _require(q, "q")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, Hq, D))
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_attn_decode_noalloc(ctypes.byref(d), _ptr(q), _dtype(q), Hq, n_ctx,
+                                               float(softmax_scale), _ptr(out), _dtype(out),
+                                               n_splits, _stream(q.device)),
+           "tbq4_attn_decode_noalloc")
     return out
 
 

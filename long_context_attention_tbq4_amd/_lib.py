@@ -24,9 +24,10 @@ EXPORTS = (
     "tbq4_attn_prefill_chunk", "tbq4_quantize_append_at", "tbq4_attn_decode_varlen",
     "tbq4_verify_workspace_bytes", "tbq4_attn_verify", "tbq4_format_row_bytes",
     "tbq4_mixed_append", "tbq4_mixed_attn_decode", "tbq4_mixed_attn_prefill_chunk",
-    "tbq4_mixed_attn_verify",
+    "tbq4_mixed_attn_verify", "tbq4_attn_decode_noalloc",
     "tbq4_status_str", "tbq4_version",
 )
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Cache(ctypes.Structure):
@@ -85,6 +86,8 @@ def lib():
     L.tbq4_quantize_blocks.restype = i32
     L.tbq4_attn_decode.argtypes = [pc, vp, i32, i32, i32, f32, vp, i32, i32, vp, sz, vp]
     L.tbq4_attn_decode.restype = i32
+    L.tbq4_attn_decode_noalloc.argtypes = [pc, vp, i32, i32, i32, f32, vp, i32, i32, vp]
+    L.tbq4_attn_decode_noalloc.restype = i32
     L.tbq4_attn_decode_partial.argtypes = [pc, vp, i32, i32, i32, f32, i32,
                                            ctypes.POINTER(i32), vp, sz, vp]
     L.tbq4_attn_decode_partial.restype = i32

@@ -205,6 +205,36 @@ tbq4_status tbq4_attn_decode(const tbq4_cache *cache, const void *q, tbq4_dtype 
   return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
 }
 
+static_assert(TBQ4_NOALLOC_SCRATCH_BYTES == tbq4::kDecodeScratchBytes,
+              "the header states the scratch size the library holds");
+
+tbq4_status tbq4_attn_decode_noalloc(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
+                                     int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
+                                     void *out, tbq4_dtype out_dtype, int32_t n_splits,
+                                     void *hip_stream) {
+  if (!out) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  // The checks of tbq4_attn_decode, with the scratch array standing for the
+  // workspace (a non-null, aligned stand-in address of its size: it is never
+  // dereferenced; the device address replaces it below).  Partial states that
+  // would not fit are TBQ4_ERR_WORKSPACE, before any HIP call.
+  tbq4::DecodeArgs a;
+  tbq4_status s = prepare_decode(cache, q, q_dtype, n_q_heads, n_ctx, softmax_scale, n_splits,
+                                 reinterpret_cast<void *>((uintptr_t)256),
+                                 tbq4::kDecodeScratchBytes, a);
+  if (s != TBQ4_OK) return s;
+  if (!aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)hip_stream;
+  void *ws = nullptr;
+  s = from_hip(tbq4::decode_scratch(st, &ws));
+  if (s != TBQ4_OK) return s;
+  a.ws = (float *)ws;
+  a.out = out;
+  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
+  if (s != TBQ4_OK) return s;
+  return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
+}
+
 tbq4_status tbq4_attn_decode_partial(const tbq4_cache *cache, const void *q, tbq4_dtype q_dtype,
                                      int32_t n_q_heads, int32_t n_ctx, float softmax_scale,
                                      int32_t n_splits, int32_t *n_splits_used, void *workspace,

@@ -31,6 +31,7 @@
 #include "tbq4_launch.h"
 
 #include <hip/hip_ext.h>
+#include <mutex>
 #include <type_traits>
 
 namespace tbq4 {
@@ -752,6 +753,44 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(DecodeArgs a) {
   o1 = n1 ? -o1 * r : o1 * r;
   dst[lane] = (OT)o0;
   dst[lane + 64] = (OT)o1;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation decode entry point (for callers that cannot
+// allocate device memory): the split-K partial states of a call live in this
+// file-scope device array, one copy per device, held until the process ends.
+// In host code `scratch` is only a host-side stand-in for the symbol: its
+// device address is looked up per device with hipGetSymbolAddress (with that
+// device current) and that address is what the kernels receive.  Every call on
+// a device shares the device's copy, so calls that overlap on one device race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(hipStream_t stream, void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,

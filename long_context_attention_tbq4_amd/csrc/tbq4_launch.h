@@ -87,6 +87,12 @@ hipError_t launch_store_q8(const StoreQ8Args &a, int dtype, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream);
+// Size of the static device array that holds the split-K partial states of
+// the no-allocation decode entry point, and its device address on the device
+// `stream` runs on (looked up once per device; never the array's host-side
+// name).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(hipStream_t stream, void **ptr);
 hipError_t launch_verify_partial(const VerifyArgs &a, int batch, int q_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_dtype,
                           hipStream_t stream);

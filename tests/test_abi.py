@@ -115,6 +115,27 @@ def test_decode_argument_errors(L):
     assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
 
 
+def test_decode_noalloc_argument_errors(L):
+    """The no-allocation decode call makes the checks of tbq4_attn_decode, with
+    the library's static scratch array standing for the workspace: partial
+    states larger than the array are a workspace error before any HIP call."""
+    c = _cache(batch=4, heads=8, cap=40000)
+
+    def dec(cache=c, q=FAKE, hq=64, n_ctx=40000, out=FAKE, odt=1, p=0):
+        return L.tbq4_attn_decode_noalloc(ctypes.byref(cache) if cache is not None else None, q,
+                                          0, hq, n_ctx, 1.0, out, odt, p, None)
+    assert dec(cache=None) == _lib.ERR_INVALID_ARG
+    assert dec(out=None) == _lib.ERR_INVALID_ARG
+    assert dec(odt=2) == _lib.ERR_INVALID_ARG
+    assert dec(hq=72) == _lib.ERR_UNSUPPORTED
+    assert dec(n_ctx=40001) == _lib.ERR_CAPACITY
+    assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
+    # 4 x 64 query rows x 1024 splits x 520 bytes = 130 MiB > 16 MiB
+    assert dec(p=1024) == _lib.ERR_WORKSPACE
+    per_split = 4 * 64 * 520
+    assert dec(p=_lib.NOALLOC_SCRATCH_BYTES // per_split + 1) == _lib.ERR_WORKSPACE
+
+
 def test_append_at_argument_errors(L):
     """Device positions cannot be checked on the host; everything else is."""
     c = _cache(heads=2, cap=64)
