@@ -113,6 +113,11 @@ size_t tbq4_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_
 tbq4_status tbq4_sign_vector(uint64_t seed, uint8_t out_bits[16]);
 
 /* Quantise and append new K and V rows (the write side of the cache).
+ * Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+ * section "Od czego zacząłem": each head vector becomes one 66-byte TBQ4
+ * block (2-byte scale, 64 bytes of 4-bit indices) in the rotated Hadamard
+ * domain; section "Konfiguracja" fixes the cache size up front (-c), which is
+ * why writes past the capacity are an error, not a reallocation.
  *   k_new, v_new  device, [batch][n_new][n_kv_heads][128] in src_dtype,
  *                 16-byte aligned.
  *   Writes the blocks of token slots [pos, pos + n_new) of every sequence of
@@ -132,6 +137,11 @@ tbq4_status tbq4_quantize_blocks(const void *x, tbq4_dtype src_dtype, int64_t n_
 
 /* Decode attention: one query per (sequence, query head) against cached
  * slots [0, n_ctx) of its KV head (kv head = h / (n_q_heads / n_kv_heads)).
+ * Page "Kontekst 262K na jednej RTX 4090: co dodałem do llama.cpp-turboq",
+ * section "Od czego zacząłem": flash attention reads the raw TBQ4 blocks and
+ * dequantises them in its inner loop, in the rotated domain, with no
+ * dequantisation pass and no F16 buffer; the result is softmax attention
+ * over the dequantised cache.
  *   q            device, [batch][n_q_heads][128], q_dtype (F32, F16 or BF16)
  *   out          device, [batch][n_q_heads][128], out_dtype (F16 or F32)
  *   softmax_scale multiplies q.k before the softmax
@@ -337,7 +347,11 @@ tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4
 
 /* Prefill-chunk attention: n_q new queries per sequence; query i sits at
  * absolute position n_past + i and attends slots [0, n_past + i] (causal
- * inside the chunk, full over the cached prefix).  Slots [n_past, n_past +
+ * inside the chunk, full over the cached prefix).  Same attention as
+ * tbq4_attn_decode (page "Kontekst 262K na jednej RTX 4090: co dodałem do
+ * llama.cpp-turboq", section "Od czego zacząłem"), for a long prompt taken
+ * in pieces (section "1. Checkpointy blokowały prefill": a 262K prefill with
+ * the prompt state saved at 32 points along the way).  Slots [n_past, n_past +
  * n_q) must already hold the chunk's own K/V (tbq4_quantize_append first).
  *   q, out   device, [batch][n_q][n_q_heads][128]; q_dtype F32, F16 or BF16,
  *            out_dtype F16 or F32.
