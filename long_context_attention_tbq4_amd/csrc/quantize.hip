@@ -63,6 +63,48 @@ __device__ __forceinline__ int half_round_sqrt(double ms) {
   return h;
 }
 
+// x of lane (lane ^ H), H in {1, 2, 4, 8, 16, 32}, without a round trip
+// through LDS: DPP quad permutations (1, 2), row shifts restricted to banks
+// (4: banks 0 and 2 read four lanes up, banks 1 and 3 four lanes down), a
+// row rotation (8), and gfx950's swaps of adjacent 16-lane rows and of the
+// two 32-lane halves (16, 32), whose two results hold the partner's value
+// for odd and even rows (halves) respectively.
+template <int H> __device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (H == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (H == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (H == 4) {
+    const int t = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x104, 0xF, 0x5, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x114, 0xF, 0xA, false);
+  } else if constexpr (H == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false);
+  } else if constexpr (H == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(H == 32, "lane_xor: H is a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+template <int H> __device__ __forceinline__ double lane_xor_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = lane_xor<H>((uint32_t)b, lane), hi = lane_xor<H>((uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+// One butterfly stage across lanes: (v_i, v_{i+H}) <- (v_i + v_{i+H}, v_i - v_{i+H})
+// for the element pair held by lanes i and i + H.
+template <int H> __device__ __forceinline__ void butterfly_lanes(double &v, int lane) {
+  const double p = lane_xor_f64<H>(v, lane);
+  v = (lane & H) ? (p - v) : (v + p);
+}
+// p_i <- p_i + p_{i+H} for lanes i < H (other lanes compute values nobody reads)
+template <int H> __device__ __forceinline__ void fold_lanes(double &p, int lane) {
+  p = p + lane_xor_f64<H>(p, lane);
+}
+
 template <typename T> __device__ __forceinline__ double load_exact(const T *p);
 template <> __device__ __forceinline__ double load_exact<float>(const float *p) { return (double)*p; }
 template <> __device__ __forceinline__ double load_exact<_Float16>(const _Float16 *p) { return (double)*p; }
@@ -123,14 +165,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   if (neg1) v1 = -v1;
 
   // butterflies h = 1..32 across lanes, then h = 64 inside the lane
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const double p0 = __shfl_xor(v0, h, 64);
-    const double p1 = __shfl_xor(v1, h, 64);
-    const bool upper = (lane & h) != 0;
-    v0 = upper ? (p0 - v0) : (v0 + p0);
-    v1 = upper ? (p1 - v1) : (v1 + p1);
-  }
+  butterfly_lanes<1>(v0, lane);  butterfly_lanes<1>(v1, lane);
+  butterfly_lanes<2>(v0, lane);  butterfly_lanes<2>(v1, lane);
+  butterfly_lanes<4>(v0, lane);  butterfly_lanes<4>(v1, lane);
+  butterfly_lanes<8>(v0, lane);  butterfly_lanes<8>(v1, lane);
+  butterfly_lanes<16>(v0, lane); butterfly_lanes<16>(v1, lane);
+  butterfly_lanes<32>(v0, lane); butterfly_lanes<32>(v1, lane);
   {
     const double a0 = v0, b0 = v1;
     v0 = a0 + b0;
@@ -144,12 +184,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const double q0 = u0 * u0;
   const double q1 = u1 * u1;
   double p = q0 + q1;
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) {
-    const double o = __shfl_down(p, h, 64);
-    p = p + o;
-  }
-  const double S = __shfl(p, 0, 64);
+  fold_lanes<32>(p, lane);
+  fold_lanes<16>(p, lane);
+  fold_lanes<8>(p, lane);
+  fold_lanes<4>(p, lane);
+  fold_lanes<2>(p, lane);
+  fold_lanes<1>(p, lane);
+  const uint64_t sb = __builtin_bit_cast(uint64_t, p);
+  const double S = __builtin_bit_cast(
+      double, (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb) |
+                  ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sb >> 32)) << 32));
   const double ms = S * 0x1p-7;
   const int dbits = half_round_sqrt(ms);
   const double d = half_value(dbits);
@@ -199,17 +243,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     i1 += dt < a1 ? 1 : 0;
   }
 
-  // byte m = code[2m] | code[2m+1] << 4; elements 2m, 2m+1 live in lanes
-  // (2m)&63 and (2m+1)&63, first element for m < 32, second for m >= 32
-  const int both = i0 | (i1 << 8);
-  const int srcl = (2 * lane) & 63;
-  const int e_a = __shfl(both, srcl, 64);
-  const int e_b = __shfl(both, srcl + 1, 64);
-  const int sh = lane < 32 ? 0 : 8;
-  const uint32_t byte = (uint32_t)(((e_a >> sh) & 15) | (((e_b >> sh) & 15) << 4));
-  const uint32_t next = (uint32_t)__shfl_down((int)byte, 1, 64);
-  if ((lane & 1) == 0) {
-    *(uint16_t *)(dst + 2 + lane) = (uint16_t)(byte | (next << 8));
+  // byte m = code[2m] | code[2m+1] << 4.  Elements 2m and 2m+1 sit in the
+  // adjacent lanes 2m and 2m+1 (m < 32, first element) or 2m-64 and 2m-63
+  // (m >= 32, second element): an even lane e forms bytes e/2 and 32 + e/2
+  // with its odd neighbour's codes, and a lane e = 4k joins them with lane
+  // e + 2's into two 16-bit words, bytes 2k, 2k+1 and 32+2k, 33+2k.
+  const uint32_t both = (uint32_t)(i0 | (i1 << 16));                 // codes < 16
+  const uint32_t pair = both | (lane_xor<1>(both, lane) << 4);      // even lanes
+  const uint32_t quad = pair | (lane_xor<2>(pair, lane) << 8);      // lanes 4k
+  if ((lane & 3) == 0) {
+    *(uint16_t *)(dst + 2 + (lane >> 1)) = (uint16_t)(quad & 0xFFFFu);
+    *(uint16_t *)(dst + 34 + (lane >> 1)) = (uint16_t)(quad >> 16);
   }
   if (lane == 0) *(uint16_t *)dst = (uint16_t)dbits;
 }
