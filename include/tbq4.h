@@ -366,10 +366,10 @@ tbq4_status tbq4_attn_prefill_chunk(const tbq4_cache *cache, const void *q, tbq4
 /* Prefill-chunk attention on a mixed-format cache (section "6. Ten sam cache
  * na Apple silicon" runs the same attention over a TBQ3 cache; section
  * "Konfiguracja" chooses the K and V types separately): as
- * tbq4_attn_prefill_chunk, with K and V each stored as TBQ4, TBQ3 or fp16
- * rows (tbq4_mixed_cache).  q is rotated only when K is stored rotated (TBQ4
- * or TBQ3), the output rotated back only when V is.  A q8_0 tensor is
- * TBQ4_ERR_UNSUPPORTED here (the decode calls read it); other errors as
+ * tbq4_attn_prefill_chunk, with K and V each stored as TBQ4, TBQ3, q8_0 or
+ * fp16 rows (tbq4_mixed_cache; the q8_0 cache of the tgstat.ru channel
+ * @tech_di page's server configuration).  q is rotated only when K is stored
+ * rotated (TBQ4 or TBQ3), the output rotated back only when V is.  Errors as
  * tbq4_attn_prefill_chunk. */
 tbq4_status tbq4_mixed_attn_prefill_chunk(const tbq4_mixed_cache *cache, const void *q,
                                           tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_past,
@@ -380,11 +380,10 @@ tbq4_status tbq4_mixed_attn_prefill_chunk(const tbq4_mixed_cache *cache, const v
  * verify of page "Kontekst 262K na jednej RTX 4090: co dodałem do
  * llama.cpp-turboq" over the per-tensor types of its section "Konfiguracja"
  * and the TBQ3 cache of section "6. Ten sam cache na Apple silicon"): as
- * tbq4_attn_verify, with K and V each stored as TBQ4, TBQ3 or fp16 rows
- * (tbq4_mixed_cache).  q is rotated only when K is stored rotated, the output
- * rotated back only when V is.  The workspace size is
- * tbq4_verify_workspace_bytes as for TBQ4.  A q8_0 tensor is
- * TBQ4_ERR_UNSUPPORTED here; other errors as tbq4_attn_verify. */
+ * tbq4_attn_verify, with K and V each stored as TBQ4, TBQ3, q8_0 or fp16
+ * rows (tbq4_mixed_cache).  q is rotated only when K is stored rotated, the
+ * output rotated back only when V is.  The workspace size is
+ * tbq4_verify_workspace_bytes as for TBQ4.  Errors as tbq4_attn_verify. */
 tbq4_status tbq4_mixed_attn_verify(const tbq4_mixed_cache *cache, const void *q,
                                    tbq4_dtype q_dtype, int32_t n_q_heads, int32_t n_past,
                                    int32_t n_q, float softmax_scale, void *out,

@@ -159,8 +159,7 @@ def mixed_attn_decode(cache, q, n_ctx, softmax_scale, n_splits=0, out=None,
 
 def mixed_attn_prefill_chunk(cache, q, n_past, softmax_scale, out=None, out_dtype=torch.float16):
     """Causal prefill-chunk attention over a MixedKVCache whose K and V are
-    TBQ4, TBQ3 or fp16 (q8_0 is decode-only); same shapes as
-    attn_prefill_chunk."""
+    TBQ4, TBQ3, q8_0 or fp16; same shapes as attn_prefill_chunk."""
     _require(q, "q")
     B, n_q, Hq, D = q.shape
     if out is None:
@@ -176,7 +175,7 @@ def mixed_attn_prefill_chunk(cache, q, n_past, softmax_scale, out=None, out_dtyp
 def mixed_attn_verify(cache, q, n_past, softmax_scale, n_splits=0, out=None,
                       out_dtype=torch.float16, workspace=None):
     """Multi-query verify attention over a MixedKVCache whose K and V are
-    TBQ4, TBQ3 or fp16 (q8_0 is decode-only); same shapes as attn_verify."""
+    TBQ4, TBQ3, q8_0 or fp16; same shapes as attn_verify."""
     _require(q, "q")
     B, n_q, Hq, D = q.shape
     if out is None:

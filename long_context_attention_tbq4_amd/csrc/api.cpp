@@ -427,7 +427,7 @@ size_t tbq4_verify_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_
 }
 
 // Verify over a cache view whose K and V tensors are stored in k_fmt / v_fmt
-// (TBQ4, fp16 or TBQ3); the caller has checked the view.
+// (TBQ4, fp16, TBQ3 or q8_0); the caller has checked the view.
 static tbq4_status verify_formats(const tbq4_cache *cache, int32_t k_fmt, int32_t v_fmt,
                                   const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
                                   int32_t n_past, int32_t n_q, float softmax_scale, void *out,
@@ -505,8 +505,6 @@ tbq4_status tbq4_mixed_attn_verify(const tbq4_mixed_cache *cache, const void *q,
   tbq4_cache view;
   tbq4_status s = mixed_view(cache, view);
   if (s != TBQ4_OK) return s;
-  if (cache->k_format == TBQ4_FMT_Q8_0 || cache->v_format == TBQ4_FMT_Q8_0)
-    return TBQ4_ERR_UNSUPPORTED;
   return verify_formats(&view, cache->k_format, cache->v_format, q, q_dtype, n_q_heads, n_past,
                         n_q, softmax_scale, out, out_dtype, n_splits, workspace, workspace_bytes,
                         hip_stream);
@@ -559,8 +557,8 @@ tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4
   return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
 }
 
-// Prefill on K / V tensors in the given formats (TBQ4, fp16 or TBQ3); the
-// cache view has been checked.
+// Prefill on K / V tensors in the given formats (TBQ4, fp16, TBQ3 or q8_0);
+// the cache view has been checked.
 static tbq4_status prefill_formats(const tbq4_cache *cache, int32_t k_fmt, int32_t v_fmt,
                                    const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
                                    int32_t n_past, int32_t n_q, float softmax_scale, void *out,
@@ -612,8 +610,6 @@ tbq4_status tbq4_mixed_attn_prefill_chunk(const tbq4_mixed_cache *cache, const v
   tbq4_cache view;
   tbq4_status s = mixed_view(cache, view);
   if (s != TBQ4_OK) return s;
-  if (cache->k_format == TBQ4_FMT_Q8_0 || cache->v_format == TBQ4_FMT_Q8_0)
-    return TBQ4_ERR_UNSUPPORTED;
   return prefill_formats(&view, cache->k_format, cache->v_format, q, q_dtype, n_q_heads, n_past,
                          n_q, softmax_scale, out, out_dtype, hip_stream);
 }

@@ -53,11 +53,14 @@ constexpr int kVTileB = kKT * kVRowB;
 // byte offset within V row r of the 16-byte chunk holding byte `byte`
 __device__ __forceinline__ int v_swizzle(int r, int byte) { return byte ^ (((r >> 2) & 1) << 4); }
 
-struct __attribute__((aligned(16))) PrefillLds {
+template <int KF, int VF> struct __attribute__((aligned(16))) PrefillLds {
   uint8_t k[2][kTileB];
   uint8_t v[2][kVTileB];
   float sk[2][kKT];
   float sv[2][kKT];
+  // q8_0 tensors: one scale per (key, 32-dim block)
+  float skq[KF == kFmtQ8 ? 2 : 1][4][KF == kFmtQ8 ? kKT : 4];
+  float svq[VF == kFmtQ8 ? 2 : 1][4][VF == kFmtQ8 ? kKT : 4];
 };
 
 // dimension held at row position p (8-dimension groups in nibble order)
@@ -74,26 +77,33 @@ template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p) {  
 }
 
 // Cache formats (K and V independently): TBQ4 blocks (the path described
-// above), TBQ3 blocks (50 bytes: scale + 3-bit codes) or fp16 rows (256
-// bytes, not rotated).  Every format is staged into the same LDS tiles of
-// fp16 values and per-key scales; TBQ4 rows keep the nibble order, TBQ3 and
-// fp16 rows the natural dimension order, and q' and the epilogue follow the
-// order of the tensor they meet.
+// above), TBQ3 blocks (50 bytes: scale + 3-bit codes), q8_0 rows (136 bytes:
+// four blocks of an fp16 scale and 32 int8 codes, not rotated) or fp16 rows
+// (256 bytes, not rotated).  Every format is staged into the same LDS tiles
+// of fp16 values and per-key scales (q8_0: exact integer codes and one scale
+// per key and 32-dim block, applied in fp32 after each block's K product and
+// folded into the P~ of each 32-dim block of V); TBQ4 rows keep the nibble
+// order, the others the natural dimension order, and q' and the epilogue
+// follow the order of the tensor they meet.
 template <int F> __device__ __forceinline__ int pos_to_dim_f(int p) {
   return F == kFmtTbq4 ? pos_to_dim(p) : p;
 }
 template <int F> constexpr uint32_t row_bytes_of() {
-  return F == kFmtTbq4 ? kBlockBytes : F == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+  return F == kFmtTbq4 ? kBlockBytes : F == kFmtTbq3 ? kBlockBytes3
+       : F == kFmtQ8 ? kQ8RowBytes : 2 * kHeadDim;
 }
 
 // One thread's share of a tile fetch for one tensor: the 16 values at
 // positions 16 fq .. 16 fq + 15 of key fkey -- TBQ4: 8 index bytes in 3 raw
 // words (realigned by 0 or 2 bytes); TBQ3: 6 code bytes in 2 words; fp16: 32
-// bytes -- and the key's scale (threads with fq = 0).
+// bytes; q8_0: 16 int8 codes of block fq / 2 in 5 words (realigned by 0 or
+// 2 bytes) -- and the key's scale (threads with fq = 0; q8_0: the block's
+// scale, threads with fq even).
 template <int F> struct RawPart;
 template <> struct RawPart<kFmtTbq4> { u32x3 w; uint16_t s; };
 template <> struct RawPart<kFmtTbq3> { u32x2 w; uint16_t s; };
 template <> struct RawPart<kFmtF16> { u32x4 w[2]; };
+template <> struct RawPart<kFmtQ8> { u32x4 w; uint32_t w1; uint16_t s; };
 template <int KF, int VF> struct TileRaw {
   RawPart<KF> k;
   RawPart<VF> v;
@@ -106,9 +116,9 @@ constexpr float kShareInv = 32.0f;
 
 template <typename QT, typename OT, int KF, int VF>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
-  __shared__ PrefillLds L;
-  constexpr bool kKRot = KF != kFmtF16;   // stored rotated: q is rotated to meet it
-  constexpr bool kVRot = VF != kFmtF16;   // stored rotated: the output is rotated back
+  __shared__ PrefillLds<KF, VF> L;
+  constexpr bool kKRot = KF == kFmtTbq4 || KF == kFmtTbq3;   // stored rotated: q is rotated to meet it
+  constexpr bool kVRot = VF == kFmtTbq4 || VF == kFmtTbq3;   // stored rotated: the output is rotated back
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -219,6 +229,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       part.w = buf_load_x2(rs, (base + (uint32_t)fkey * kBlockBytes3 + 2 + 6 * fq) & ~3u);
       part.s = 0;
       if (fq == 0 && live) part.s = buf_load_u16(rs, base + (uint32_t)fkey * kBlockBytes3);
+    } else if constexpr (F == kFmtQ8) {
+      // codes 16 (fq & 1) .. + 15 of block fq / 2: byte 34 (fq / 2) + 2 +
+      // 16 (fq & 1) of the key's 8-byte-aligned row
+      const uint32_t kb = (uint32_t)(t * kKT + fkey) * kQ8RowBytes + 34u * (uint32_t)(fq >> 1);
+      const uint32_t a4 = (kb + 2u + 16u * (uint32_t)(fq & 1)) & ~3u;
+      part.w = buf_load_x4(rs, a4);
+      part.w1 = buf_load_x1(rs, a4 + 16);
+      part.s = 0;
+      if ((fq & 1) == 0 && live) part.s = buf_load_u16(rs, kb);
     } else {
       // fp16 rows: an unwritten slot may hold NaN values, so it reads as zeros
       const uint32_t f = live ? (uint32_t)(t * kKT + fkey) * (2 * kHeadDim) + 32 * fq : 0xFFFF0000u;
@@ -251,6 +270,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       const uint32_t hi = part.w[1] >> (8 * sh);
       c0 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(lo & 0xFFFFFFu));
       c1 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(((lo >> 24) | (hi << 8)) & 0xFFFFFFu));
+    } else if constexpr (F == kFmtQ8) {
+      // int8 codes as exact fp16 values, natural order; the block scale is
+      // applied per key after the products
+      const uint32_t sh = ((uint32_t)fkey * kQ8RowBytes + 34u * (uint32_t)(fq >> 1) + 2u) & 3u;
+      const u32x4 w = part.w;
+      const uint32_t x0 = alignbyte(w[1], w[0], sh), x1 = alignbyte(w[2], w[1], sh);
+      const uint32_t x2 = alignbyte(w[3], w[2], sh), x3 = alignbyte(part.w1, w[3], sh);
+      c0 = __builtin_bit_cast(u32x4, i8x8_to_half8(x0, x1));
+      c1 = __builtin_bit_cast(u32x4, i8x8_to_half8(x2, x3));
     } else {
       c0 = part.w[0];
       c1 = part.w[1];
@@ -258,7 +286,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   };
   auto scale_of = [&](const auto &part, auto fmt_tag) -> float {
     constexpr int F = decltype(fmt_tag)::value;
-    if constexpr (F == kFmtF16) return 1.0f;
+    if constexpr (F == kFmtF16 || F == kFmtQ8) return 1.0f;
     else return half_bits_to_float(part.s);
   };
   // dequantise a fetched share into LDS buffer `buf`: 16 fp16 values of K
@@ -276,6 +304,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     if (fq == 0) {
       L.sk[buf][fkey] = scale_of(r.k, std::integral_constant<int, KF>{});
       L.sv[buf][fkey] = scale_of(r.v, std::integral_constant<int, VF>{});
+    }
+    // q8_0: the block scales (a slot at or past n_keys reads as scale 0, so
+    // its finite codes contribute nothing)
+    if constexpr (KF == kFmtQ8) {
+      if ((fq & 1) == 0) L.skq[buf][fq >> 1][fkey] = half_bits_to_float(r.k.s);
+    }
+    if constexpr (VF == kFmtQ8) {
+      if ((fq & 1) == 0) L.svq[buf][fq >> 1][fkey] = half_bits_to_float(r.v.s);
     }
   };
 
@@ -317,11 +353,35 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       float16v sacc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+      if constexpr (KF == kFmtQ8) {
+        // MFMA steps 2b and 2b + 1 span q8_0 block b, whose scale differs per
+        // key: each block's product is taken alone and scaled in fp32
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq) {
+          float16v t;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) t[e] = 0.0f;
+#pragma unroll
+          for (int c = 2 * bq; c < 2 * bq + 2; ++c) {
+            const half8 ka = *(const half8 *)(kb + (kb0 + row) * kRowB + 32 * c + 16 * half);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[c], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[c], t, 0, 0, 0);
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float4v d4 = *(const float4v *)(&L.skq[buf][bq][kb0 + 8 * m + 4 * half]);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2)
+              sacc[4 * m + e2] = fmaf(d4[e2], t[4 * m + e2], sacc[4 * m + e2]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const half8 ka = *(const half8 *)(kb + (kb0 + row) * kRowB + 32 * c + 16 * half);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[c], sacc, 0, 0, 0);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[c], sacc, 0, 0, 0);
+      }
       }
       // the softmax issues at raised priority: the SIMD's other wavefront,
       // when it is in its MFMA phase, keeps the matrix core busy meanwhile
@@ -381,11 +441,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       const bool fine = __any(p_top * kShareInv > l_run);
 
       uint32_t pw[8], rw[8];
+      if constexpr (VF != kFmtQ8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
-      if (fine) {
+        for (int j = 0; j < 8; ++j) pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
+        if (fine) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+          for (int j = 0; j < 8; ++j) rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+        }
       }
 
       __builtin_amdgcn_s_setprio(0);
@@ -409,8 +471,48 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
           }
         }
       };
-      pv(pw);
-      if (fine) pv(rw);
+      if constexpr (VF == kFmtQ8) {
+        // q8_0 V: dims 32 db .. 32 db + 31 form block db, whose P~ is p times
+        // the key's block-db scale (the staged key scales are 1)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          float q[16];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float4v d4 = *(const float4v *)(&L.svq[buf][db][kb0 + 8 * m + 4 * half]);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) q[4 * m + e2] = pt[4 * m + e2] * d4[e2];
+          }
+          uint32_t w[8], x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = pk_f16(q[2 * j], q[2 * j + 1]);
+          if (fine) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = pk_f16_residual(w[j], q[2 * j], q[2 * j + 1]);
+          }
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int r0 = kb0 + 16 * ks + tr_row;
+            const uint8_t *vbase = vb + r0 * kVRowB;
+            typedef __attribute__((address_space(3))) short4v lds_s4;
+            const int col = v_swizzle(r0, tr_col + 64 * db);
+            const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
+            const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
+            const half8 vs = __builtin_bit_cast(
+                half8, short8v{ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]});
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                vs, __builtin_bit_cast(half8, u32x4{w[4 * ks], w[4 * ks + 1], w[4 * ks + 2], w[4 * ks + 3]}),
+                o[db], 0, 0, 0);
+            if (fine)
+              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  vs, __builtin_bit_cast(half8, u32x4{x[4 * ks], x[4 * ks + 1], x[4 * ks + 2], x[4 * ks + 3]}),
+                  o[db], 0, 0, 0);
+          }
+        }
+      } else {
+        pv(pw);
+        if (fine) pv(rw);
+      }
     }
 
     if (more) stage(nxt, buf ^ 1);
@@ -465,18 +567,21 @@ hipError_t launch_prefill(const PrefillArgs &a, int batch, int q_dtype, int out_
   if (gx > 0x7FFFFFFF || batch > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)gx, batch);
   // (q dtype, output dtype, K format, V format) -> kernel instance; formats
-  // TBQ4 (0), fp16 (1), TBQ3 (2)
+  // TBQ4 (0), fp16 (1), TBQ3 (2), q8_0 (3)
 #define TBQ4_PF(QT, OT, KF, VF) reinterpret_cast<const void *>(&prefill_kernel<QT, OT, KF, VF>)
-#define TBQ4_PF_K(QT, OT, KF) {TBQ4_PF(QT, OT, KF, 0), TBQ4_PF(QT, OT, KF, 1), TBQ4_PF(QT, OT, KF, 2)}
-#define TBQ4_PF_Q(QT, OT) {TBQ4_PF_K(QT, OT, 0), TBQ4_PF_K(QT, OT, 1), TBQ4_PF_K(QT, OT, 2)}
-  static const void *const kernels[3][2][3][3] = {
+#define TBQ4_PF_K(QT, OT, KF) \
+  {TBQ4_PF(QT, OT, KF, 0), TBQ4_PF(QT, OT, KF, 1), TBQ4_PF(QT, OT, KF, 2), TBQ4_PF(QT, OT, KF, 3)}
+#define TBQ4_PF_Q(QT, OT) {TBQ4_PF_K(QT, OT, 0), TBQ4_PF_K(QT, OT, 1), TBQ4_PF_K(QT, OT, 2), \
+                           TBQ4_PF_K(QT, OT, 3)}
+  static const void *const kernels[3][2][kNumFormats][kNumFormats] = {
       {TBQ4_PF_Q(float, float), TBQ4_PF_Q(float, _Float16)},
       {TBQ4_PF_Q(_Float16, float), TBQ4_PF_Q(_Float16, _Float16)},
       {TBQ4_PF_Q(uint16_t, float), TBQ4_PF_Q(uint16_t, _Float16)}};
 #undef TBQ4_PF_Q
 #undef TBQ4_PF_K
 #undef TBQ4_PF
-  if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
+  if (a.k_fmt < 0 || a.k_fmt >= kNumFormats || a.v_fmt < 0 || a.v_fmt >= kNumFormats)
+    return hipErrorInvalidValue;
   if (q_dtype < 0 || q_dtype > 2) return hipErrorInvalidValue;
   const void *fn = kernels[q_dtype][out_dtype == 1 ? 1 : 0][a.k_fmt][a.v_fmt];
   PrefillArgs arg = a;

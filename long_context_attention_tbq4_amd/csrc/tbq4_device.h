@@ -214,20 +214,18 @@ __device__ __forceinline__ void load16_unaligned(rsrc_t r, uint32_t start, uint3
 // the same for all 128 values of a V row) moves the output by up to 2^-11 of
 // the V rows that carry the weight, which matters when few keys dominate.  The
 // residual x - fp16(x) (exact in fp32) rounded to fp16 restores ~22 bits when
-// it is accumulated by a second operand.  Both are written out as
-// instructions -- v_cvt_pk_f16_f32, then v_fma_mix with the fp16 halves as
-// sources -- so that the compiler cannot round the exact product straight to
-// fp16 for the residual while the operand holds the rounding of the fp32
-// product: the operand's value and the one the residual is taken from must be
-// the same number.
+// it is accumulated by a second operand.  The residual is written out as
+// instructions (v_fma_mix with the fp16 halves of the operand word as
+// sources) so that it is taken from exactly the operand's bits: left to
+// itself the compiler may round the exact product p d^V straight to fp16 for
+// the residual while the operand holds the rounding of the fp32 product, two
+// different numbers in the rare double-rounding cases.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pk_f16(float x0, float x1) {
-  uint32_t hw;
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hw) : "v"(x0), "v"(x1));
-  return hw;
+  return __builtin_bit_cast(uint32_t, fp16x2{(_Float16)x0, (_Float16)x1});
 }
-// fp16 pair of (x0 - h0, x1 - h1), h = the fp16 halves of hw, each difference
-// rounded once
+// fp16 pair of (x0 - h0, x1 - h1), h = the fp16 halves of the operand word hw
+// (whichever way it was rounded), each difference rounded once
 __device__ __forceinline__ uint32_t pk_f16_residual(uint32_t hw, float x0, float x1) {
   uint32_t rw;
   asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(rw) : "v"(hw), "v"(x0));

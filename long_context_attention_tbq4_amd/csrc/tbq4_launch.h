@@ -55,7 +55,7 @@ struct VerifyArgs {
   int32_t n_kv_heads, n_q_heads, group, capacity, n_past, n_q, n_splits;
   float qscale;          // softmax_scale * log2(e)
   uint32_t sign[4];
-  int32_t k_fmt, v_fmt;  // cache formats (TBQ4, fp16 or TBQ3; zero = TBQ4)
+  int32_t k_fmt, v_fmt;  // cache formats (TBQ4, fp16, TBQ3 or q8_0; zero = TBQ4)
 };
 
 struct PrefillArgs {

@@ -20,15 +20,15 @@
 //     q' operands wait in LDS (one 16-byte slot per lane) instead of
 //     registers, which keeps two wavefronts per SIMD for four queries,
 //   * every column is a distinct (query, head), so each lane finishes its
-//     own scores and P~ rows; P~ = p d^V is one fp16, rounded to nearest,
-//     plus its fp16 residual as a second PV product in tiles where one key
-//     carries more than 1/32 of a column's running weight.
+//     own scores and P~ rows; P~ = p d^V is an fp16 value, rounded to
+//     nearest, plus its fp16 residual, which a second MFMA multiplies by the
+//     same V operand.
 // Partial states use the decode workspace layout with (sequence, query) as
 // the row index, so the decode merge kernel finishes them.
 //
-// K and V may each be stored as TBQ4 blocks, TBQ3 blocks or fp16 rows
-// (template arguments KF, VF); the fetch, operand and staging steps of each
-// format are the decode kernel's.  q is rotated only when K is stored
+// K and V may each be stored as TBQ4 blocks, TBQ3 blocks, q8_0 rows or fp16
+// rows (template arguments KF, VF); the fetch, operand and staging steps of
+// each format are the decode kernel's.  q is rotated only when K is stored
 // rotated, and the merge rotates the output back only when V is.
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
@@ -43,20 +43,22 @@ constexpr int kBlk = kTile / 16;
 constexpr int kVRow = 80;           // staged TBQ4 V row: 64 index bytes + pad
 constexpr int kE4Row = 144;         // staged TBQ3 V row: 128 e4m3 bytes + pad
 constexpr int kF16Row = 288;        // staged fp16 V row: 256 bytes + pad
-// A tile takes the fp16 residual of P~ as a second PV product when one of its
-// keys carries more than 1/kShareInv of a column's running weight sum.
-constexpr float kShareInv = 32.0f;
 }  // namespace
 
 template <typename QT, int CG, int KF, int VF>
 __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
-  constexpr bool kKRot = KF != kFmtF16;
-  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
-  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : VF == kFmtTbq3 ? kBlockBytes3 : 2 * kHeadDim;
+  constexpr bool kKRot = KF == kFmtTbq4 || KF == kFmtTbq3;   // stored rotated
+  constexpr uint32_t kKBytes = KF == kFmtTbq4 ? kBlockBytes : KF == kFmtTbq3 ? kBlockBytes3
+                             : KF == kFmtQ8 ? kQ8RowBytes : 2 * kHeadDim;
+  constexpr uint32_t kVBytes = VF == kFmtTbq4 ? kBlockBytes : VF == kFmtTbq3 ? kBlockBytes3
+                             : VF == kFmtQ8 ? kQ8RowBytes : 2 * kHeadDim;
   __shared__ __attribute__((aligned(16))) uint8_t
-      vlds[kTile * (VF == kFmtTbq4 ? kVRow : VF == kFmtTbq3 ? kE4Row : kF16Row)];
+      vlds[kTile * (VF == kFmtTbq4 ? kVRow : VF == kFmtF16 ? kF16Row : kE4Row)];
   __shared__ __attribute__((aligned(16))) float sk[kTile];
   __shared__ __attribute__((aligned(16))) float sv[kTile];
+  // q8_0: one scale per (32-dim block, token), K scales times 2^-ex
+  __shared__ __attribute__((aligned(16))) float skq[KF == kFmtQ8 ? 4 * kTile : 4];
+  __shared__ __attribute__((aligned(16))) float svq[VF == kFmtQ8 ? 4 * kTile : 4];
   __shared__ __attribute__((aligned(16))) half8 qlds[CG][4][2][64];   // q' high / residual
 
   const int lane = threadIdx.x;
@@ -73,13 +75,16 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
   for (int c = 0; c < CG; ++c) {
     const int qi = 2 * c + qsub;
     const bool live = qi < a.n_q && head < G;
+    // lane quarter q holds dims 32 q + i; for a q8_0 K cache dims
+    // 32 (i/8) + 8 q + i%8 instead, so that MFMA step k spans q8_0 block k
     const QT *qp = (const QT *)a.q +
                    (((size_t)b * a.n_q + (live ? qi : 0)) * a.n_q_heads + (size_t)g * G +
-                    (live ? head : 0)) * kHeadDim + quarter * 32;
+                    (live ? head : 0)) * kHeadDim;
     const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float x = live ? load_q<QT>(qp + i) : 0.0f;
+      const int d = KF == kFmtQ8 ? 32 * (i >> 3) + 8 * quarter + (i & 7) : 32 * quarter + i;
+      const float x = live ? load_q<QT>(qp + d) : 0.0f;
       qv[c][i] = ((sw >> i) & 1u) ? -x : x;
     }
     if constexpr (kKRot) {
@@ -126,7 +131,8 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 #pragma unroll
       for (int el = 0; el < 8; ++el) {
         // TBQ4 K operands hold the 4 even then the 4 odd dims of a code
-        // word; TBQ3 and fp16 K operands hold 8 consecutive dims
+        // word; TBQ3, fp16 and q8_0 K operands hold 8 consecutive elements
+        // of the lane's order above
         const int i = KF == kFmtTbq4 ? 8 * k + (el < 4 ? 2 * el : 2 * el - 7) : 8 * k + el;
         const float x = ldexpf(qv[c][i], ex);
         const _Float16 hi = (_Float16)x;
@@ -182,11 +188,17 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
   // (TBQ4: 5 words realigned by 0 or 2 bytes; TBQ3: 12 code bytes in one
   // 16-byte load) or its token's 32 fp16 dims (4 aligned 16-byte loads), and
   // the scales of token `lane`; a tile past the split reads as zeros
-  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : 1;
+  // (q8_0 K: the lane's 8 codes of each of the token's 4 blocks in 10 words
+  // and two of the token's block scales per lane; q8_0 V: the lane's block,
+  // scale and 32 codes, in 9 words -- the decode kernel's fetches)
+  constexpr int kKW = KF == kFmtF16 ? 4 : 1, kVW = VF == kFmtF16 ? 4 : VF == kFmtQ8 ? 2 : 1;
   struct Raw {
     u32x4 k4[kBlk * kKW], v4[kBlk * kVW];
     uint32_t k1[kBlk], v1[kBlk];
+    u32x3 kq3[KF == kFmtQ8 ? 2 * kBlk : 1];
+    u32x2 kq2[KF == kFmtQ8 ? 2 * kBlk : 1];
     uint16_t sk, sv;
+    uint16_t skq[2];
   };
   const uint32_t lane_off = (uint32_t)col * kBlockBytes + 2 + 16 * quarter;
   const uint32_t shift = lane_off & 3u;   // (2 col + 2) mod 4: the same for TBQ3
@@ -203,6 +215,14 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         r.k1[blk] = buf_load_x1(rk, ad + 16);
       } else if constexpr (KF == kFmtTbq3) {
         r.k4[blk] = buf_load_x4(rk, a3);
+      } else if constexpr (KF == kFmtQ8) {
+        // codes 8 q .. 8 q + 7 of block c start at byte 34 c + 2 + 8 q of the
+        // token (token rows are 8-byte aligned)
+        const uint32_t tb = live ? tok * kQ8RowBytes + 8u * quarter : 0xFFFF0000u;
+        r.kq3[2 * blk] = buf_load_x3(rk, tb);
+        r.kq2[2 * blk] = buf_load_x2(rk, tb + 36);
+        r.kq3[2 * blk + 1] = buf_load_x3(rk, tb + 68);
+        r.kq2[2 * blk + 1] = buf_load_x2(rk, tb + 104);
       } else {
         const uint32_t fo = live ? tok * kKBytes + 64u * quarter : 0xFFFF0000u;
 #pragma unroll
@@ -213,11 +233,22 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         r.v1[blk] = buf_load_x1(rv, ad + 16);
       } else if constexpr (VF == kFmtTbq3) {
         r.v4[blk] = buf_load_x4(rv, a3);
+      } else if constexpr (VF == kFmtQ8) {
+        const uint32_t vb = live ? (tok * kQ8RowBytes + 34u * quarter) & ~3u : 0xFFFF0000u;
+        r.v4[2 * blk] = buf_load_x4(rv, vb);
+        r.v4[2 * blk + 1] = buf_load_x4(rv, vb + 16);
+        r.v1[blk] = buf_load_x1(rv, vb + 32);
       } else {
         const uint32_t fo = live ? tok * kVBytes + 64u * quarter : 0xFFFF0000u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) r.v4[4 * blk + c] = buf_load_x4(rv, fo + 16u * c);
       }
+    }
+    if constexpr (KF == kFmtQ8) {   // lane: token lane % 32, blocks 2 (lane / 32) + 0, 1
+      const uint32_t so = live ? (uint32_t)(t * kTile + (lane & 31)) * kQ8RowBytes + 68u * (lane >> 5)
+                               : 0xFFFF0000u;
+      r.skq[0] = buf_load_u16(rk, so);
+      r.skq[1] = buf_load_u16(rk, so + 34);
     }
     const uint32_t soff = lane < kTile ? base + (uint32_t)lane * kBlockBytes : 0xFFFF0000u;
     const uint32_t soff3 = lane < kTile && live ? (uint32_t)(t * kTile + lane) * kBlockBytes3 : 0xFFFF0000u;
@@ -234,10 +265,22 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     const int tok0 = t * kTile;
     uint32_t kw[kBlk][4];
     u32x4 kf[KF == kFmtF16 ? kBlk * 4 : 1];
+    uint32_t kq[KF == kFmtQ8 ? kBlk : 1][8];
 #pragma unroll
     for (int blk = 0; blk < kBlk; ++blk) {
       const u32x4 w = r.k4[blk];
-      if constexpr (KF == kFmtTbq4) {
+      if constexpr (KF == kFmtQ8) {
+        const u32x3 a0 = r.kq3[2 * blk], a2 = r.kq3[2 * blk + 1];
+        const u32x2 a1 = r.kq2[2 * blk], a3 = r.kq2[2 * blk + 1];
+        kq[blk][0] = alignbyte(a0[1], a0[0], 2u);
+        kq[blk][1] = alignbyte(a0[2], a0[1], 2u);
+        kq[blk][2] = a1[0];
+        kq[blk][3] = a1[1];
+        kq[blk][4] = alignbyte(a2[1], a2[0], 2u);
+        kq[blk][5] = alignbyte(a2[2], a2[1], 2u);
+        kq[blk][6] = a3[0];
+        kq[blk][7] = a3[1];
+      } else if constexpr (KF == kFmtTbq4) {
         kw[blk][0] = alignbyte(w[1], w[0], shift);
         kw[blk][1] = alignbyte(w[2], w[1], shift);
         kw[blk][2] = alignbyte(w[3], w[2], shift);
@@ -272,6 +315,21 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         uint8_t *rowp = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
         *(u32x4 *)rowp = u32x4{e[0], e[1], e[2], e[3]};
         *(u32x4 *)(rowp + 16) = u32x4{e[4], e[5], e[6], e[7]};
+      } else if constexpr (VF == kFmtQ8) {
+        // block `quarter` of the token: scale then 32 codes, from byte 0 (even
+        // quarter: codes 2 bytes into the words) or byte 2 (odd quarter)
+        const u32x4 w0 = r.v4[2 * blk], w1 = r.v4[2 * blk + 1];
+        const uint32_t d[9] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], r.v1[blk]};
+        const bool odd = (quarter & 1) != 0;
+        uint32_t cw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cw[j] = odd ? d[j + 1] : alignbyte(d[j + 1], d[j], 2u);
+        uint8_t *rowp = vlds + (16 * blk + col) * kE4Row + 32 * quarter;
+        *(u32x4 *)rowp = u32x4{cw[0], cw[1], cw[2], cw[3]};
+        *(u32x4 *)(rowp + 16) = u32x4{cw[4], cw[5], cw[6], cw[7]};
+        const uint16_t sbits = (uint16_t)(odd ? d[0] >> 16 : d[0] & 0xFFFFu);
+        const bool dead = kPartial && tok0 + 16 * blk + col >= n_kv;   // (NaN guard)
+        svq[quarter * kTile + 16 * blk + col] = dead ? 0.0f : half_bits_to_float(sbits);
       } else {
         const bool dead = kPartial && tok0 + 16 * blk + col >= n_kv;   // (as for K)
 #pragma unroll
@@ -280,10 +338,17 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
               dead ? u32x4{0u, 0u, 0u, 0u} : r.v4[4 * blk + c];
       }
     }
+    if constexpr (KF == kFmtQ8) {
+      const int tk = lane & 31, c0 = 2 * (lane >> 5);
+      const bool dead = kPartial && tok0 + tk >= n_kv;
+      skq[c0 * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[0]) * qs_inv;
+      skq[(c0 + 1) * kTile + tk] = dead ? 0.0f : half_bits_to_float(r.skq[1]) * qs_inv;
+    }
     if (lane < kTile) {
-      float dk = qs_inv, dv = 1.0f;
-      if constexpr (KF != kFmtF16) dk = half_bits_to_float(r.sk) * qs_inv;
-      if constexpr (VF != kFmtF16) dv = half_bits_to_float(r.sv);
+      float dk = qs_inv, dv = 1.0f;   // (q8_0: per-block scales above)
+      if constexpr (KF == kFmtTbq4 || KF == kFmtTbq3) dk = half_bits_to_float(r.sk) * qs_inv;
+      if constexpr (KF == kFmtQ8) dk = 1.0f;
+      if constexpr (VF == kFmtTbq4 || VF == kFmtTbq3) dv = half_bits_to_float(r.sv);
       if constexpr (kPartial) {
         // slots past the drafted tokens may hold anything (NaN survives p = 0)
         if (tok0 + lane >= n_kv) dk = dv = 0.0f;
@@ -295,8 +360,8 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
     // group only when a score exceeds the reference by more than 8 (log2), so
     // p <= 256 and P~ = p d^V <= 65504 while every V scale is below 256; a
     // tile with a larger scale (or an unused slot's bits) uses lag 0
-    bool vbig = false;
-    if constexpr (VF != kFmtF16) vbig = __any(r.sv > 0x5BFFu);
+    bool vbig = VF == kFmtQ8;
+    if constexpr (VF == kFmtTbq4 || VF == kFmtTbq3) vbig = __any(r.sv > 0x5BFFu);
     fetch(r, t + 1);
 
     // ---- scores: S^T[token][(query, head)] = K . (q'_hi + q'_lo)
@@ -310,6 +375,7 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
           if constexpr (KF == kFmtTbq4) kh[blk][k] = word_to_half8(kw[blk][k]);
           else if constexpr (KF == kFmtTbq3)
             kh[blk][k] = tbq3_chunk_to_half8(tbq3_chunk(kw[blk][0], kw[blk][1], kw[blk][2], k));
+          else if constexpr (KF == kFmtQ8) kh[blk][k] = i8x8_to_half8(kq[blk][2 * k], kq[blk][2 * k + 1]);
           else kh[blk][k] = __builtin_bit_cast(half8, kf[4 * blk + k]);
         }
       // consecutive MFMAs rotate through the CG x 2 accumulators, so none
@@ -319,6 +385,33 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
       for (int c = 0; c < CG; ++c)
 #pragma unroll
         for (int blk = 0; blk < kBlk; ++blk) acc[c][blk] = float4v{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KF == kFmtQ8) {
+        // step k spans q8_0 block k, whose scale differs per token: each
+        // step's product is taken alone and scaled in fp32
+        __syncthreads();   // the block scales are staged
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float4v st[CG][kBlk];
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              const half8 qo = qlds[c][k][hl][lane];
+#pragma unroll
+              for (int blk = 0; blk < kBlk; ++blk)
+                st[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    kh[blk][k], qo, hl ? st[c][blk] : float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+          for (int blk = 0; blk < kBlk; ++blk) {
+            const float4v kd4 = *(const float4v *)(skq + k * kTile + 16 * blk + 4 * quarter);
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[c][blk][e] = fmaf(kd4[e], st[c][blk][e], acc[c][blk][e]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -330,11 +423,12 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
             for (int blk = 0; blk < kBlk; ++blk)
               acc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh[blk][k], qo, acc[c][blk], 0, 0, 0);
           }
+      }
     }
     __syncthreads();
 
     half8 pa[CG], pr[CG];
-    bool fine = false;
+    float pq[VF == kFmtQ8 ? CG : 1][8];   // q8_0 V: the weights p, scaled per block below
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
       const int qi = 2 * c + qsub;
@@ -374,7 +468,7 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) t4[blk][e] += shift_t;
       }
-      float psum = 0.0f, p_top = 0.0f;
+      float psum = 0.0f;
       float pt[8];
 #pragma unroll
       for (int blk = 0; blk < kBlk; ++blk) {
@@ -383,32 +477,28 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(t4[blk][e]);
           psum += p;
-          p_top = fmaxf(p_top, p);
           pt[4 * blk + e] = p * vd[e];
         }
       }
       l_run[c] += psum;
-      uint32_t pw[4];
+      if constexpr (VF == kFmtQ8) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
-      pa[c] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      // a key with more than 1/kShareInv of its column's running weight sum
-      // (this lane's quarter of it: a lower bound) sends the residual of P~
-      // through a second PV product
-      pr[c] = half8{};
-      if (__any(p_top * kShareInv > l_run[c])) {
-        fine = true;
-        uint32_t rw[4];
+        for (int e = 0; e < 8; ++e) pq[c][e] = pt[e];   // (the staged token scales are 1)
+      } else {
+        uint32_t pw[4], rw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) {
+          pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
+          rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+        }
+        pa[c] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
         pr[c] = __builtin_bit_cast(half8, u32x4{rw[0], rw[1], rw[2], rw[3]});
       }
     }
 
-    // ---- O'^T += P~ V for every column group (V dequantised once); in a
-    // tile where the residual of P~ is carried, a second pass over the
-    // staged V takes it
-    auto pv_tbq4 = [&](const half8 *w) {
+    // ---- O'^T += P~ V for every column group, then the residual of P~
+    // times the same V operand (V dequantised once)
+    if constexpr (VF == kFmtTbq4) {
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
         typedef __attribute__((address_space(3))) int2v lds_i2;
@@ -418,14 +508,54 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
         const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
-          o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[c], ve, o[c][2 * cg], 0, 0, 0);
-          o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[c], vo, o[c][2 * cg + 1], 0, 0, 0);
+          o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], ve, o[c][2 * cg], 0, 0, 0);
+          o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vo, o[c][2 * cg + 1], 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+          o[c][2 * cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr[c], ve, o[c][2 * cg], 0, 0, 0);
+          o[c][2 * cg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr[c], vo, o[c][2 * cg + 1], 0, 0, 0);
         }
       }
-    };
-    if constexpr (VF == kFmtTbq4) {
-      pv_tbq4(pa);
-      if (fine) pv_tbq4(pr);
+    } else if constexpr (VF == kFmtQ8) {
+      // q8_0 V: codes staged as int8, one byte-transposed read per 16 dims;
+      // dims 32 cc .. 32 cc + 31 lie in block cc, whose P~ is p times the
+      // token's block-cc scale (value and residual)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        half8 pb[CG], rb[CG];
+        const float4v d0 = *(const float4v *)(svq + cc * kTile + 4 * quarter);
+        const float4v d1 = *(const float4v *)(svq + cc * kTile + 16 + 4 * quarter);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+          float pt[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pt[e] = pq[c][e] * d0[e];
+            pt[4 + e] = pq[c][4 + e] * d1[e];
+          }
+          uint32_t pw[4], rw[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pw[j] = pk_f16(pt[2 * j], pt[2 * j + 1]);
+            rw[j] = pk_f16_residual(pw[j], pt[2 * j], pt[2 * j + 1]);
+          }
+          pb[c] = __builtin_bit_cast(half8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+          rb[c] = __builtin_bit_cast(half8, u32x4{rw[0], rw[1], rw[2], rw[3]});
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int db = 2 * cc + h;
+          typedef __attribute__((address_space(3))) int2v lds_i2;
+          const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
+          const half8 vv = i8x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]);
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb[c], vv, o[c][db], 0, 0, 0);
+            o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rb[c], vv, o[c][db], 0, 0, 0);
+          }
+        }
+      }
     } else {
       // TBQ3: e4m3 bytes, one byte-transposed read per 16 dims; fp16: two
       // 16-bit transposed reads per 16 dims (dim 16 db + col)
@@ -447,28 +577,9 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 #pragma unroll
         for (int c = 0; c < CG; ++c)
           o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[c], vv, o[c][db], 0, 0, 0);
-      }
-      if (fine) {
-        // the residual of P~ through a second pass over the staged V
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          half8 vv;
-          if constexpr (VF == kFmtTbq3) {
-            typedef __attribute__((address_space(3))) int2v lds_i2;
-            const int2v rr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr8_3_off + 16 * db));
-            vv = e4m3x8_to_half8((uint32_t)rr[0], (uint32_t)rr[1]);
-          } else {
-            typedef __attribute__((address_space(3))) short4v lds_s4;
-            const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vlds + tr16_off + 32 * db));
-            const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s4 *)(vlds + tr16_off + 16 * kF16Row + 32 * db));
-            const short8v s8 = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-            vv = __builtin_bit_cast(half8, s8);
-          }
-#pragma unroll
-          for (int c = 0; c < CG; ++c)
-            o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr[c], vv, o[c][db], 0, 0, 0);
-        }
+        for (int c = 0; c < CG; ++c)
+          o[c][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr[c], vv, o[c][db], 0, 0, 0);
       }
     }
   };
@@ -519,17 +630,21 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 hipError_t launch_verify_partial(const VerifyArgs &a, int batch, int q_dtype, hipStream_t stream) {
   dim3 grid(a.n_splits, a.n_kv_heads, batch);
   // (q dtype, column groups, K format, V format) -> kernel instance;
-  // formats TBQ4 (0), fp16 (1), TBQ3 (2)
+  // formats TBQ4 (0), fp16 (1), TBQ3 (2), q8_0 (3)
 #define TBQ4_VF(QT, CG, KF, VF) reinterpret_cast<const void *>(&verify_split_kernel<QT, CG, KF, VF>)
-#define TBQ4_VF_K(QT, CG, KF) {TBQ4_VF(QT, CG, KF, 0), TBQ4_VF(QT, CG, KF, 1), TBQ4_VF(QT, CG, KF, 2)}
-#define TBQ4_VF_C(QT, CG) {TBQ4_VF_K(QT, CG, 0), TBQ4_VF_K(QT, CG, 1), TBQ4_VF_K(QT, CG, 2)}
-  static const void *const kernels[3][2][3][3] = {{TBQ4_VF_C(float, 1), TBQ4_VF_C(float, 2)},
+#define TBQ4_VF_K(QT, CG, KF) \
+  {TBQ4_VF(QT, CG, KF, 0), TBQ4_VF(QT, CG, KF, 1), TBQ4_VF(QT, CG, KF, 2), TBQ4_VF(QT, CG, KF, 3)}
+#define TBQ4_VF_C(QT, CG) \
+  {TBQ4_VF_K(QT, CG, 0), TBQ4_VF_K(QT, CG, 1), TBQ4_VF_K(QT, CG, 2), TBQ4_VF_K(QT, CG, 3)}
+  static const void *const kernels[3][2][kNumFormats][kNumFormats] = {
+                                                  {TBQ4_VF_C(float, 1), TBQ4_VF_C(float, 2)},
                                                   {TBQ4_VF_C(_Float16, 1), TBQ4_VF_C(_Float16, 2)},
                                                   {TBQ4_VF_C(uint16_t, 1), TBQ4_VF_C(uint16_t, 2)}};
 #undef TBQ4_VF_C
 #undef TBQ4_VF_K
 #undef TBQ4_VF
-  if (a.k_fmt < 0 || a.k_fmt > 2 || a.v_fmt < 0 || a.v_fmt > 2) return hipErrorInvalidValue;
+  if (a.k_fmt < 0 || a.k_fmt >= kNumFormats || a.v_fmt < 0 || a.v_fmt >= kNumFormats)
+    return hipErrorInvalidValue;
   if (q_dtype < 0 || q_dtype > 2) return hipErrorInvalidValue;
   const void *fn = kernels[q_dtype][a.n_q > 2 ? 1 : 0][a.k_fmt][a.v_fmt];
   VerifyArgs arg = a;

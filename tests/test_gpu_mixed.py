@@ -134,15 +134,12 @@ def test_append_block_counts_not_multiple_of_four(kf, vf, B, H, n_new):
     assert not cache.k[:, :, :5].any() and not cache.k[:, :, 5 + n_new:].any()
 
 
-PREFILL_FORMATS = list(itertools.product([tb.FMT_TBQ4, tb.FMT_F16, tb.FMT_TBQ3], repeat=2))
-
-
-@pytest.mark.parametrize("kf,vf", PREFILL_FORMATS)
+@pytest.mark.parametrize("kf,vf", ALL)
 def test_prefill_formats(kf, vf):
     """Prefill chunk (query i at n_past + i sees slots 0 .. n_past + i) on K
-    and V stored as TBQ4, TBQ3 or fp16, against the fp64 definition on the
-    dequantised tensors; unused slots hold 0xFF bytes (NaN fp16 values, NaN
-    scales) that must not leak."""
+    and V stored as TBQ4, TBQ3, q8_0 or fp16, against the fp64 definition on
+    the dequantised tensors; unused slots hold 0xFF bytes (NaN fp16 values,
+    NaN scales) that must not leak."""
     rng = np.random.default_rng(40 + kf + 4 * vf)
     B, H, G, n_past, n_q, cap, seed, scale = 2, 2, 4, 301, 97, 424, 5, 0.09
     T = n_past + n_q
@@ -183,16 +180,17 @@ VERIFY_SHAPES = [   # B, H, G, n_past, n_q, cap, P
     (2, 2, 4, 301, 3, 320, 0),
     (1, 1, 8, 5, 4, 16, 1),
     (3, 2, 1, 70, 1, 80, 3),
+    (1, 2, 8, 1000, 2, 1008, 4),
 ]
 
 
-@pytest.mark.parametrize("kf,vf", PREFILL_FORMATS)
+@pytest.mark.parametrize("kf,vf", ALL)
 @pytest.mark.parametrize("shape", range(len(VERIFY_SHAPES)))
 def test_verify_formats(kf, vf, shape):
     """Multi-query verify (query i at n_past + i sees slots 0 .. n_past + i)
-    on K and V stored as TBQ4, TBQ3 or fp16, against the fp64 definition on
-    the dequantised tensors; unused slots hold 0xFF bytes that must not
-    leak."""
+    on K and V stored as TBQ4, TBQ3, q8_0 or fp16, against the fp64
+    definition on the dequantised tensors; unused slots hold 0xFF bytes that
+    must not leak."""
     B, H, G, n_past, n_q, cap, P = VERIFY_SHAPES[shape]
     rng = np.random.default_rng(70 + kf + 4 * vf + 16 * shape)
     seed, scale = 9 + shape, 0.1
