@@ -139,6 +139,139 @@ class HipEvents:
         self.ev = []
 
 
+def dist(ms):
+    """median, p10 and p90 of a list of per-call times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
+class Flush:
+    """Reads a 1 GiB buffer (untimed, on the same stream, before the first
+    event of a timed call) with the library's streaming-read helper, which
+    evicts the 256 MB Infinity Cache and the L2s with clean lines: the call
+    that follows reads its inputs from HBM.  (Writing the buffer instead
+    leaves ~256 MB of dirty lines whose write-back then competes with the
+    timed call's reads.)"""
+
+    def __init__(self, torch):
+        import ctypes
+        import long_context_attention_tbq4_amd as tb
+        self.ct = ctypes
+        self.L = tb._lib.lib()
+        self.torch = torch
+        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        self.sink = torch.empty(512, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        st = self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        rc = self.L.tbq4_bench_stream_read(self.ct.c_void_p(self.buf.data_ptr()), self.buf.numel(),
+                                           self.ct.c_void_p(self.sink.data_ptr()), 512, st)
+        assert rc == 0, rc
+
+
+def time_each(torch, fn, n, flush=None):
+    """Per-call times (ms) of n calls of fn, each between two events on the
+    current stream; with `flush`, the flush runs before each call's first
+    event (outside the timed interval)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def manifest_clocks():
+    """Current clock levels as rocm-smi reports them (None if it cannot)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        return [" ".join(l.split()) for l in r.stdout.splitlines()
+                if "sclk" in l or "mclk" in l or "fclk" in l][:6]
+    except Exception:
+        return None
+
+
+def manifest(torch):
+    """What the numbers were measured on: ROCm, device, clocks, sources."""
+    import hashlib
+    import subprocess
+    root = os.path.dirname(os.path.abspath(__file__))
+    m = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            m["rocm"] = f.read().strip()
+    except OSError:
+        m["rocm"] = None
+    props = torch.cuda.get_device_properties(0)
+    m["device"] = props.name
+    m["gfx_arch"] = getattr(props, "gcnArchName", None)
+    m["compute_units"] = props.multi_processor_count
+    m["hbm_bytes"] = props.total_memory
+    m["clocks_idle"] = manifest_clocks()
+    h = hashlib.sha256()
+    for sub in ("long_context_attention_tbq4_amd/csrc", "include"):
+        d = os.path.join(root, sub)
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    m["sources_sha256"] = h.hexdigest()
+    try:
+        r = subprocess.run(["git", "-C", root, "rev-parse", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        m["git_head"] = r.stdout.strip() or None
+    except Exception:
+        m["git_head"] = None
+    m["host_cpus"] = len(os.sched_getaffinity(0))
+    return m
+
+
+def bench_denominators(tb, torch):
+    """Measured-achievable peaks: a read-only streaming kernel over 1 GiB
+    (best of four grid sizes) and an MFMA-only loop of independent fp16
+    32x32x16 products (best of three grid sizes)."""
+    import ctypes
+    L = tb._lib.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n = 1 << 30
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1 << 18, dtype=torch.float32, device="cuda")
+    read = []
+    for nb in (256, 512, 1024, 2048):
+        def rd():
+            assert L.tbq4_bench_stream_read(ctypes.c_void_p(buf.data_ptr()), n,
+                                            ctypes.c_void_p(sink.data_ptr()), nb, st) == 0
+        for _ in range(3):
+            rd()
+        ms = float(np.median(time_each(torch, rd, 10)))
+        read.append({"workgroups": nb, "ms": round(ms, 5), "gbs": round(n / (ms * 1e-3) / 1e9, 1)})
+    mf = []
+    iters = 2000
+    for nb in (256, 512, 1024):
+        def mm():
+            assert L.tbq4_bench_mfma_f16(iters, ctypes.c_void_p(sink.data_ptr()), nb, st) == 0
+        for _ in range(2):
+            mm()
+        ms = float(np.median(time_each(torch, mm, 5)))
+        flops = nb * 4 * iters * 8 * 32768
+        mf.append({"workgroups": nb, "ms": round(ms, 5),
+                   "tflops": round(flops / (ms * 1e-3) / 1e12, 1)})
+    del buf, sink
+    best_r = max(read, key=lambda r: r["gbs"])
+    best_m = max(mf, key=lambda r: r["tflops"])
+    log(f"achievable: stream read {best_r['gbs']:.0f} GB/s, fp16 MFMA {best_m['tflops']:.0f} TFLOP/s")
+    return {"stream_read_gbs": best_r["gbs"], "mfma_f16_tflops": best_m["tflops"],
+            "stream_read": read, "mfma_f16": mf,
+            "note": "stream: 1 GiB read once, 16-byte non-temporal loads, 4 in flight per lane; "
+                    "mfma: 8 independent v_mfma_f32_32x32x16_f16 chains per wavefront, "
+                    "register operands; medians of back-to-back calls"}
+
+
 def fill_cache(tb, torch, cache, w, t0, t1, chunk=32768, keep=None):
     """Append tokens t0 .. t1 of the workload to the TBQ4 cache; with `keep`
     (a list) the fp32 K/V chunks stay resident on the GPU for later caches."""
@@ -208,6 +341,19 @@ def bench_decode(tb, torch, args):
     e1.record()
     torch.cuda.synchronize()
     kern_b2b = e0.elapsed_time(e1) / args.steps
+    # per-step and per-kernel distributions: warm (back to back, the cache
+    # partly resident in the Infinity Cache) and cold (1 GiB written before
+    # every timed call)
+    flush = Flush(torch)
+    split = lambda: tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
+    n_d = max(args.steps, 30)
+    dists = {"step_warm": dist(time_each(torch, step, n_d)),
+             "step_cold": dist(time_each(torch, step, n_d, flush)),
+             "split_kernel_warm": dist(time_each(torch, split, n_d)),
+             "split_kernel_cold": dist(time_each(torch, split, n_d, flush))}
+    del flush
+    log("decode128k per-call ms: " + ", ".join(f"{k} {v['median']:.4f}" for k, v in dists.items()))
+    share = bench_share(tb, torch, args, cache, q, w)
     sweep = bench_split_sweep(tb, torch, args, cache, q, w)
     graph = bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w)
     verify = bench_verify(tb, torch, args, cache, w)
@@ -236,6 +382,8 @@ def bench_decode(tb, torch, args):
         "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
         "tokens_per_s": B * T / (ms * 1e-3),
         "graph": graph,
+        "dists": dists,
+        "share": share,
         "sweep": sweep,
         "verify": verify,
         "formats": formats,
@@ -280,6 +428,54 @@ def bench_format(tb, torch, args, cache, q, out, ws, P, w):
             "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(B * T / (ms * 1e-3), 1)}
+
+
+def bench_share(tb, torch, args, cache, q, w):
+    """One GPU's share when the decode128k heads are sharded over 8 GPUs:
+    batch 4, 1 KV head / 8 query heads, 131072 slots (KV head 0 of the
+    resident cache, copied untimed), split kernel + merge at 128 and 256
+    splits and the automatic count; calls back to back."""
+    B, T = cache.batch, cache.capacity
+    c1 = tb.KVCache(B, 1, T)
+    c1.k.copy_(cache.k[:, 0:1])
+    c1.v.copy_(cache.v[:, 0:1])
+    q1 = q[:, 0:8].contiguous()
+    out = torch.empty((B, 8, 128), dtype=torch.float16, device="cuda")
+    kv = B * T * 2 * 66
+    res = []
+    for P in (128, 256, 0):
+        Pu = P or tb.decode_auto_splits(B, 1, T)
+        ws = torch.empty(tb.decode_workspace_bytes(B, 1, 8, T, Pu), dtype=torch.uint8, device="cuda")
+        call = lambda: tb.attn_decode(c1, q1, T, w.softmax_scale, n_splits=Pu, out=out, workspace=ws)
+        part = lambda: tb.attn_decode_partial(c1, q1, T, w.softmax_scale, n_splits=Pu, workspace=ws)
+        for _ in range(args.warmup + args.settle // 10):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        e0.record()
+        for _ in range(args.steps):
+            part()
+        e1.record()
+        torch.cuda.synchronize()
+        kms = e0.elapsed_time(e1) / args.steps
+        res.append({"n_splits": Pu, "ms_per_call": round(ms, 5), "kernel_ms": round(kms, 5),
+                    "gbs": round(kv / (ms * 1e-3) / 1e9, 1),
+                    "kernel_gbs": round((kv + B * 8 * 512) / (kms * 1e-3) / 1e9, 1),
+                    "kernel_frac_of_hbm_peak": round((kv + B * 8 * 512) / (kms * 1e-3) / 1e9
+                                                     / HBM_PEAK_GBS, 4)})
+    assert torch.isfinite(out.float()).all()
+    del c1, q1
+    log("share (1 KV head / 8 q heads): " + ", ".join(f"P={r['n_splits']}: {r['gbs']:.0f}" for r in res))
+    return {"workload": "one GPU's share of decode128k sharded by KV head over 8 GPUs: batch 4, "
+                        "1 KV / 8 query heads, 131072 slots; decode call (split kernel + merge) "
+                        "back to back, and the split kernel alone",
+            "kv_bytes": kv, "results": res}
 
 
 def bench_split_sweep(tb, torch, args, cache, q, w):
@@ -414,8 +610,18 @@ def bench_contexts(tb, torch, args):
     ms = e0.elapsed_time(e1) / n
     assert torch.isfinite(out.float()).all()
     byt = kv_step_bytes(T, H, Hq)
+    # the 17 MB cache fits in the 256 MB Infinity Cache: cold steps read
+    # 1 GiB before each timed step
+    flush = Flush(torch)
+    d16 = {"step_warm": dist(time_each(torch, step16, 100)),
+           "step_cold": dist(time_each(torch, step16, 100, flush))}
+    del flush
+    log(f"decode16k per-step ms: warm {d16['step_warm']['median']:.4f}, "
+        f"cold {d16['step_cold']['median']:.4f}")
     res.append({"workload": "decode16k: batch 1, 8 KV / 64 query heads, 16384 slots, one layer; "
                             "step = append one token + decode",
+                "per_step_ms": d16,
+                "cold_gbs": round(byt / (d16["step_cold"]["median"] * 1e-3) / 1e9, 1),
                 "n_splits": tb.decode_auto_splits(1, H, T), "steps": n, "ms_per_step": round(ms, 5),
                 "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
                 "frac_of_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -508,10 +714,23 @@ def bench_prefill(tb, torch, args):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    att_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    att_list = [a.elapsed_time(b) for a, b in evs]
+    att_ms = float(np.mean(att_list))
     pairs = sum(n_past + i + 1 for i in range(n_q))
     flops = 4 * 128 * Hq * pairs
     assert torch.isfinite(out.float()).all()
+    # cold attention calls (1 GiB read before each; the 141 MB cache would
+    # otherwise sit in the Infinity Cache) and the chunk's quantise-append
+    flush = Flush(torch)
+    att_cold = time_each(torch, lambda: tb.attn_prefill_chunk(cache, q, n_past, w.softmax_scale,
+                                                              out=out), steps, flush)
+    app = lambda: tb.quantize_append(cache, k_new, v_new, n_past)
+    app_warm = time_each(torch, app, 20)
+    app_cold = time_each(torch, app, 20, flush)
+    del flush
+    app_bytes = 2 * n_q * Hkv * 128 * 4 + 2 * n_q * Hkv * 66     # fp32 rows in, blocks out
+    app_blocks = 2 * n_q * Hkv
+    log(f"prefill attention cold {np.median(att_cold):.3f} ms; append {np.median(app_warm):.4f} ms")
     # the same chunk on caches whose K and V are TBQ3 or fp16 rows
     formats = []
     for kf, vf in (PREFILL_FORMATS if args.formats else ()):
@@ -540,6 +759,15 @@ def bench_prefill(tb, torch, args):
         "workload": "prefill: 2048 new queries on 131072 cached tokens, batch 1, 8 KV / 64 Q "
                     "heads, head_dim 128; step = append of the chunk's K/V + causal attention",
         "steps": steps, "ms_per_step": wall * 1e3 / steps, "attention_ms": att_ms,
+        "attention_ms_warm": dist(att_list), "attention_ms_cold": dist(att_cold),
+        "tflops_cold": flops / (float(np.median(att_cold)) * 1e-3) / 1e12,
+        "append": {"workload": "quantise-append of the chunk: 2048 tokens x 8 KV heads, K and V "
+                               "(fp32 rows in, 66-byte blocks out)",
+                   "blocks": app_blocks, "bytes": app_bytes,
+                   "ms_warm": dist(app_warm), "ms_cold": dist(app_cold),
+                   "gbs_warm": round(app_bytes / (float(np.median(app_warm)) * 1e-3) / 1e9, 1),
+                   "gbs_cold": round(app_bytes / (float(np.median(app_cold)) * 1e-3) / 1e9, 1),
+                   "blocks_per_s": round(app_blocks / (float(np.median(app_warm)) * 1e-3), 1)},
         "tflops": flops / (att_ms * 1e-3) / 1e12,
         "frac_of_mfma_peak": flops / (att_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
         "algorithmic_tflop": flops / 1e12, "query_tokens_per_s": n_q / (att_ms * 1e-3),
@@ -547,38 +775,175 @@ def bench_prefill(tb, torch, args):
     }
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle, untuned, on whole (sequence, KV head) rows of the decode128k
-    workload: fp64 dequantise of the 131072 K and V blocks + attention of the
-    8 query heads.  Rate in GB/s of packed K+V consumed."""
-    from oracle import tbq4_oracle as o
-    from workloads import WORKLOADS, K, V, kv_rows, q_decode
-    w = WORKLOADS["decode128k"]
-    T, G = w.n_ctx, w.n_q_heads // w.n_kv_heads
-    q = q_decode(w)
-    done, spent, rows = 0, 0.0, []
-    for (b, g) in [(0, 0), (1, 3), (2, 5), (3, 7), (0, 4), (1, 1)]:
-        kc = o.quantize_blocks(kv_rows(w, 0, K, b, g, 0, T))[0]
-        vc = o.quantize_blocks(kv_rows(w, 0, V, b, g, 0, T))[0]
-        t0 = time.perf_counter()
-        o.attn_decode_rows_ref(q[b, g * G:(g + 1) * G], o.dequantize_blocks(kc),
-                               o.dequantize_blocks(vc), w.softmax_scale)
-        spent += time.perf_counter() - t0
-        done += 1
-        log(f"cpu baseline: row {done} done, {spent:.1f} s")
-        rows.append((b, g))
-        if spent >= budget_s:
-            break
-    threads = 1
+# --------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, on the host's cores.  Each leg
+# times one oracle call (dequantise the packed rows + softmax attention) on
+# inputs prepared beforehand (generated and quantised, untimed); rows are
+# spread over worker processes (one BLAS thread each), so `cores` is the
+# number of workers.
+# --------------------------------------------------------------------------
+def _cpu_workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _one_blas_thread():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
         pass
-    gbs = done * T * 132 / spent / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of 32 (sequence, KV head) rows of decode128k (131072 tokens x "
-                      f"8 query heads each), fp64 dequantise + attention; {spent:.1f} s"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+    except Exception:
+        return None
+
+
+def _cpu_quantize_job(n_blocks):
+    """fp64 quantiser on n seeded N(0,1) blocks: (blocks, seconds).  (numpy
+    element-wise work: one thread per process.)"""
+    from oracle import tbq4_oracle as o
+    x = np.random.default_rng([0, 77, n_blocks]).standard_normal((n_blocks, 128)).astype(np.float32)
+    t0 = time.perf_counter()
+    o.quantize_blocks(x)
+    return n_blocks, time.perf_counter() - t0
+
+
+def _cpu_row_prep(args):
+    """Generate and quantise one (layer, sequence, KV head) row of a decode
+    workload (untimed preparation): returns the packed K, V rows."""
+    _one_blas_thread()
+    from oracle import tbq4_oracle as o
+    from workloads import WORKLOADS, K, V, kv_rows
+    wname, layer, b, g, t_end = args
+    w = WORKLOADS[wname]
+    return (o.quantize_blocks(kv_rows(w, layer, K, b, g, 0, t_end))[0],
+            o.quantize_blocks(kv_rows(w, layer, V, b, g, 0, t_end))[0])
+
+
+def _cpu_row_call(args):
+    """The timed oracle work of one row: dequantise the packed rows and run
+    softmax attention for each (q_rows, n) asked for.  Returns seconds."""
+    _one_blas_thread()
+    from oracle import tbq4_oracle as o
+    kc, vc, jobs, scale = args
+    t0 = time.perf_counter()
+    Kd, Vd = o.dequantize_blocks(kc), o.dequantize_blocks(vc)
+    for qr, n in jobs:
+        o.attn_decode_rows_ref(qr, Kd[:n], Vd[:n], scale)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(quick=False):
+    """The oracle's legs; `quick` (for the host-side test) shrinks every
+    sample to a row or a few blocks."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from oracle import tbq4_oracle as o
+    from workloads import WORKLOADS, K, V, kv_rows, kv_tensor, q_decode, q_prefill, tiny_inputs
+    nw = _cpu_workers()
+    legs = {}
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(nw, mp_context=ctx) as ex:
+        # quantise: one process, then all workers at once
+        nq = 512 if quick else 32768
+        n1, s1 = _cpu_quantize_job(nq)
+        t0 = time.perf_counter()
+        done = sum(n for n, _ in ex.map(_cpu_quantize_job, [nq] * nw))
+        wall = time.perf_counter() - t0
+        legs["quantize"] = {"blocks_per_s_1_thread": round(n1 / s1, 1),
+                            "blocks_per_s_all": round(done / wall, 1), "workers": nw,
+                            "sample": f"{nq} seeded N(0,1) blocks per process"}
+        log(f"cpu baseline: quantize {n1 / s1:.0f} blocks/s (1 thread), {done / wall:.0f} ({nw})")
+
+        def prepare(wname, layer_heads, t_end):
+            return list(ex.map(_cpu_row_prep, [(wname, l, b, g, t_end) for l, b, g in layer_heads]))
+
+        def decode_call(wname, layer_heads, n, qfn, prep):
+            """the (layer, b, g) rows of one call, prepared beforehand: time
+            the call with the rows spread over the workers"""
+            w = WORKLOADS[wname]
+            G = w.n_q_heads // w.n_kv_heads
+            jobs = [(kc, vc, [(qfn(l)[b, g * G:(g + 1) * G], n)], w.softmax_scale)
+                    for (l, b, g), (kc, vc) in zip(layer_heads, prep)]
+            t0 = time.perf_counter()
+            cpu_s = sum(ex.map(_cpu_row_call, jobs))
+            return time.perf_counter() - t0, cpu_s
+
+        # C1: the tiny workload, whole (one process)
+        k, v, q, _ = tiny_inputs()
+        kc = o.quantize_blocks(k.transpose(0, 2, 1, 3))[0]
+        vc = o.quantize_blocks(v.transpose(0, 2, 1, 3))[0]
+        t0 = time.perf_counter()
+        o.attn_decode_ref(q, kc, vc, 1024, WORKLOADS["tiny"].softmax_scale)
+        legs["tiny"] = {"ms_per_call": round((time.perf_counter() - t0) * 1e3, 3), "workers": 1}
+        # C2: decode16k, one whole call (8 KV heads)
+        w = WORKLOADS["decode16k"]
+        rows = [(0, 0, g) for g in range(1 if quick else 8)]
+        wall, cs = decode_call("decode16k", rows, w.n_ctx, lambda l: q_decode(w),
+                               prepare("decode16k", rows, w.n_ctx))
+        legs["decode16k"] = {"s_per_call": round(wall, 3), "cpu_s": round(cs, 3), "workers": nw,
+                             "rows": len(rows), "gbs": round(w.n_ctx * len(rows) * 132 / wall / 1e9, 4)}
+        log(f"cpu baseline: decode16k {wall:.2f} s per call")
+        # C3: one call at 98304 and at 131072 slots (all 32 rows)
+        w = WORKLOADS["decode128k"]
+        rows = [(0, b, g) for b in range(1 if quick else 4) for g in range(1 if quick else 8)]
+        prep = prepare("decode128k", rows, 131072)    # the 98304-slot call reads a prefix
+        for n in (98304, 131072):
+            wall, cs = decode_call("decode128k", rows, n, lambda l: q_decode(w), prep)
+            legs[f"decode_{n}"] = {"s_per_call": round(wall, 3), "cpu_s": round(cs, 3),
+                                   "workers": nw, "rows": len(rows),
+                                   "gbs": round(len(rows) * n * 132 / wall / 1e9, 4)}
+            log(f"cpu baseline: decode {n} {wall:.2f} s per call")
+        del prep
+        # C5: one long-decode step at its first position: layer 0 measured
+        # (8 KV heads), the 4-layer step is that x 4
+        w = WORKLOADS["longdecode"]
+        n5 = w.n_ctx + 1
+        rows = [(0, 0, g) for g in range(1 if quick else 8)]
+        wall, cs = decode_call("longdecode", rows, n5, lambda l: q_decode(w, l, 0),
+                               prepare("longdecode", rows, n5))
+        legs["longdecode_step"] = {"s_one_layer": round(wall, 3), "s_per_step_x4": round(4 * wall, 3),
+                                   "cpu_s": round(cs, 3), "workers": nw,
+                                   "rows": len(rows), "gbs": round(n5 * len(rows) * 132 / wall / 1e9, 4),
+                                   "note": "layer 0 of step 0 (8 KV heads at 262081 slots) measured; "
+                                           "the 4-layer step is that x 4 (extrapolated)"}
+        log(f"cpu baseline: long-decode layer {wall:.2f} s")
+    # C4: one KV-head group of the prefill chunk (all 2048 queries), x 8;
+    # numpy's BLAS on nw threads in this process
+    w = WORKLOADS["prefill"]
+    T = w.n_ctx + w.n_q
+    kc = o.quantize_blocks(kv_rows(w, 0, K, 0, 0, 0, T))[0]
+    vc = o.quantize_blocks(kv_rows(w, 0, V, 0, 0, 0, T))[0]
+    stride = 512 if quick else 16
+    rows = np.arange(0, w.n_q, stride)              # 128 of the 2048 chunk rows
+    qg = q_prefill(w)[0][rows, 0:8]
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(nw):
+        t0 = time.perf_counter()
+        Kd, Vd = o.dequantize_blocks(kc), o.dequantize_blocks(vc)
+        o.attn_prefill_rows_ref(qg, Kd, Vd, w.n_ctx, rows, w.softmax_scale)
+        grp = time.perf_counter() - t0
+    flops = 4 * 128 * 64 * sum(w.n_ctx + i + 1 for i in range(w.n_q))
+    est = grp * stride * 8
+    legs["prefill"] = {"s_sample": round(grp, 3), "s_per_chunk_extrapolated": round(est, 1),
+                       "tflops": round(flops / est / 1e12, 6), "blas_threads": nw,
+                       "note": "KV-head group 0, every 16th of the 2048 chunk queries (128 rows x 8 "
+                               "heads, dequantise + causal attention) measured; the chunk is that "
+                               "x 16 x 8 (extrapolated)"}
+    log(f"cpu baseline: prefill sample {grp:.2f} s (chunk ~{est:.0f} s)")
+    del Kd, Vd
+    head = legs["decode_131072"]
+    return {"value": head["gbs"], "unit": "GB/s", "cores": nw, "kind": "oracle",
+            "sample": f"{head['rows']} of the 32 (sequence, KV head) rows of one decode128k call "
+                      "at 131072 slots (packed K+V, 8 query heads each): fp64 dequantise + softmax "
+                      f"attention, rows spread over {nw} worker processes with one BLAS thread "
+                      f"each; {head['s_per_call']} s",
+            "host_cpus": len(os.sched_getaffinity(0)), "blas_threads_default": _blas_threads(),
+            "legs": legs}
 
 
 def main():
@@ -602,13 +967,18 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "copies": 5}))
         return
+    man = manifest(torch)
+    den = bench_denominators(tb, torch)
     dec = bench_decode(tb, torch, args)
+    man["clocks_after_decode"] = manifest_clocks()
     log(f"decode: {dec['ms']:.4f} ms/step, kernel {dec['kernel_ms']:.4f} ms, "
         f"{dec['achieved']:.0f} GB/s")
     ctx = None if args.no_contexts else bench_contexts(tb, torch, args)
     pre = None if args.no_prefill else bench_prefill(tb, torch, args)
     if pre:
         log(f"prefill: {pre['attention_ms']:.3f} ms, {pre['tflops']:.1f} TFLOP/s")
+        pre["frac_of_achievable_mfma"] = pre["tflops"] / den["mfma_f16_tflops"]
+        pre["achievable_mfma_tflops"] = den["mfma_f16_tflops"]
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": METRIC,
@@ -645,6 +1015,20 @@ def main():
                         "kernel + merge) over 131072 slots, calls back to back",
             "results": dec["formats"],
         },
+        "per_call_ms": {
+            "workload": "decode128k; step = append + split kernel + merge; warm: back to back "
+                        "(part of the cache stays in the 256 MB Infinity Cache), cold: 1 GiB "
+                        "read before each timed call; each call between two HIP events",
+            **dec["dists"],
+            "step_cold_gbs": round(dec["step_bytes"] / (dec["dists"]["step_cold"]["median"] * 1e-3)
+                                   / 1e9, 1),
+            "split_kernel_cold_gbs": round((dec["kv_bytes"] + 4 * 64 * 512)
+                                           / (dec["dists"]["split_kernel_cold"]["median"] * 1e-3)
+                                           / 1e9, 1),
+        },
+        "share_1_of_8_gpus": dec["share"],
+        "achievable": den,
+        "manifest": man,
         "split_sweep": {
             "workload": "decode128k cache; split kernel alone at 98304 and 131072 attended "
                         "slots, batch 4, 8 / 64 heads",
@@ -663,6 +1047,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+            "frac_of_achievable": round(dec["achieved"] / den["stream_read_gbs"], 4),
+            "achievable_peak": den["stream_read_gbs"],
             "traffic": measured_traffic(dec["P"]),
             "kernel_ms": round(dec["kernel_ms"], 5),
             "kernel_ms_in_step": round(dec["kernel_ms_in_step"], 5),

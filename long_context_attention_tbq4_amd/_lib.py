@@ -28,6 +28,8 @@ EXPORTS = (
     "tbq4_status_str", "tbq4_version",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
+# measurement helpers (include/tbq4_bench.h)
+BENCH_EXPORTS = ("tbq4_bench_stream_read", "tbq4_bench_mfma_f16")
 
 
 class Cache(ctypes.Structure):
@@ -117,6 +119,10 @@ def lib():
     L.tbq4_mixed_attn_verify.restype = i32
     L.tbq4_attn_prefill_chunk.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, vp]
     L.tbq4_attn_prefill_chunk.restype = i32
+    L.tbq4_bench_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    L.tbq4_bench_stream_read.restype = i32
+    L.tbq4_bench_mfma_f16.argtypes = [i32, vp, i32, vp]
+    L.tbq4_bench_mfma_f16.restype = i32
     L.tbq4_status_str.argtypes = [i32]
     L.tbq4_status_str.restype = ctypes.c_char_p
     L.tbq4_version.argtypes = []

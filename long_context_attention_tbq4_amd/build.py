@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtbq4.so")
-SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "verify.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "verify.hip", "prefill.hip",
+           "bench_kernels.hip"]
 # per-source options: the decode loop keeps its MFMA accumulators in
 # ordinary VGPRs (its conditional rescale then needs no register copies)
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

@@ -33,6 +33,21 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_library_exports_the_measurement_helpers(L):
+    with open(os.path.join(ROOT, "include", "tbq4_bench.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(tbq4_[a-z_0-9]+)\s*\(", header))
+    assert declared == set(_lib.BENCH_EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    # argument checks run before any launch
+    assert L.tbq4_bench_stream_read(None, 1 << 20, FAKE, 64, None) == -1
+    assert L.tbq4_bench_stream_read(FAKE, 24, FAKE, 64, None) == -1
+    assert L.tbq4_bench_stream_read(FAKE, 1 << 20, FAKE, 0, None) == -1
+    assert L.tbq4_bench_mfma_f16(0, FAKE, 64, None) == -1
+    assert L.tbq4_bench_mfma_f16(10, None, 64, None) == -1
+
+
 def test_version_and_status_strings(L):
     assert L.tbq4_version().decode().count(".") == 2
     for s in (0, -1, -2, -3, -4, -5, -6):
