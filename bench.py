@@ -55,8 +55,8 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # -> x1.0).  Reported only while the kernel's sources hash to the version the
 # counters were taken on; otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "f996f0500e8e79e3335e2961a082db29febccdb54fa0693c84bd2e5db80ad016",
-           "n_splits": 64, "fetch_kib": 271200.9, "fetch_factor": 2.0,
+TRAFFIC = {"sources_sha256": "f39677f0a0e3bcc3418ba7ea40fad49e70eb80f33f03a4a7ac94c2b77827d2eb",
+           "n_splits": 64, "fetch_kib": 271201.3, "fetch_factor": 2.0,
            "write_kib": 8704.1, "write_factor": 1.0}
 
 
@@ -187,20 +187,49 @@ def time_each(torch, fn, n, flush=None):
 
 
 def manifest_clocks():
-    """Current clock levels as rocm-smi reports them (None if it cannot)."""
-    import subprocess
+    """Current core, memory and fabric clock levels from the driver's sysfs
+    tables (the level marked '*'), per GPU card; None where unreadable."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        card = {}
+        for clk in ("sclk", "mclk", "fclk", "socclk"):
+            try:
+                with open(os.path.join(dev, "pp_dpm_" + clk)) as f:
+                    cur = [l.split(":", 1)[1].strip(" *\n") for l in f if l.rstrip().endswith("*")]
+                card[clk] = cur[0] if cur else None
+            except (OSError, IndexError):
+                pass
+        if card:
+            out[os.path.basename(os.path.dirname(dev))] = card
+    return out or None
+
+
+def git_head(root):
+    """Commit of the working tree, read from .git without running git."""
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        return [" ".join(l.split()) for l in r.stdout.splitlines()
-                if "sclk" in l or "mclk" in l or "fclk" in l][:6]
-    except Exception:
-        return None
+        with open(os.path.join(root, ".git", "HEAD")) as f:
+            ref = f.read().strip()
+        if not ref.startswith("ref: "):
+            return ref or None
+        name = ref[5:]
+        path = os.path.join(root, ".git", name)
+        if os.path.exists(path):
+            with open(path) as f:
+                return f.read().strip() or None
+        with open(os.path.join(root, ".git", "packed-refs")) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 2 and parts[1] == name:
+                    return parts[0]
+    except OSError:
+        pass
+    return None
 
 
 def manifest(torch):
     """What the numbers were measured on: ROCm, device, clocks, sources."""
     import hashlib
-    import subprocess
     root = os.path.dirname(os.path.abspath(__file__))
     m = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
     try:
@@ -221,12 +250,7 @@ def manifest(torch):
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(f.encode() + fh.read())
     m["sources_sha256"] = h.hexdigest()
-    try:
-        r = subprocess.run(["git", "-C", root, "rev-parse", "HEAD"], capture_output=True, text=True,
-                           timeout=10)
-        m["git_head"] = r.stdout.strip() or None
-    except Exception:
-        m["git_head"] = None
+    m["git_head"] = git_head(root)   # None where the tree was copied without .git
     m["host_cpus"] = len(os.sched_getaffinity(0))
     return m
 
@@ -342,7 +366,7 @@ def bench_decode(tb, torch, args):
     torch.cuda.synchronize()
     kern_b2b = e0.elapsed_time(e1) / args.steps
     # per-step and per-kernel distributions: warm (back to back, the cache
-    # partly resident in the Infinity Cache) and cold (1 GiB written before
+    # partly resident in the Infinity Cache) and cold (1 GiB read before
     # every timed call)
     flush = Flush(torch)
     split = lambda: tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
