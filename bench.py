@@ -325,11 +325,20 @@ def bench_decode(tb, torch, args):
     q = torch.from_numpy(q_decode(w)).cuda()
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
     P = args.splits or tb.decode_auto_splits(B, Hkv, T)
-    ws = torch.empty(tb.decode_workspace_bytes(B, Hkv, Hq, T, P), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tb.decode_step_workspace_bytes(B, Hkv, Hq, T, P), dtype=torch.uint8,
+                     device="cuda")
 
     hip = HipEvents(args.steps)
 
-    def step(i=None):
+    def step():
+        """the decode step: the new token appended and attended in the split
+        kernel's launch (one extra wavefront per (sequence, KV head)), then
+        the merge"""
+        tb.decode_step(cache, k_new, v_new, q, T - 1, w.softmax_scale, n_splits=P, out=out,
+                       workspace=ws)
+
+    def step_unfused(i=None):
+        """the same step as three launches: append, split kernel, merge"""
         tb.quantize_append(cache, k_new, v_new, T - 1)
         tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws,
                                events=None if i is None else hip.pair(i))
@@ -348,11 +357,20 @@ def bench_decode(tb, torch, args):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the split kernel's duration: the same steps again, with HIP events
-    # recorded by every split dispatch (their markers add idle gaps around
-    # the kernel, so the step time above is taken without them)
+    # the same steps as three launches (append, split kernel, merge)
+    for _ in range(args.warmup):
+        step_unfused()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step_unfused()
+    torch.cuda.synchronize()
+    wall_unfused = time.perf_counter() - t0
+    # the split kernel's duration inside those steps: HIP events recorded by
+    # every split dispatch (their markers add idle gaps around the kernel, so
+    # the step times above are taken without them)
+    for i in range(args.steps):
+        step_unfused(i)
     torch.cuda.synchronize()
     kern_ms = hip.elapsed_ms()
     hip.destroy()
@@ -395,11 +413,12 @@ def bench_decode(tb, torch, args):
     append_bytes = 2 * B * Hkv * 128 * 4 + 2 * B * Hkv * 66
     step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
     ms = wall * 1e3 / args.steps
+    ms_unfused = wall_unfused * 1e3 / args.steps
     kern_avg = float(np.mean(kern_ms))
     achieved = (kv_bytes + q_bytes) / (kern_b2b * 1e-3) / 1e9
     assert torch.isfinite(out.float()).all()
     return {
-        "P": P, "ms": ms, "value": step_bytes / (ms * 1e-3) / 1e9,
+        "P": P, "ms": ms, "value": step_bytes / (ms * 1e-3) / 1e9, "ms_unfused": ms_unfused,
         "kernel_ms": kern_b2b, "kernel_ms_in_step": kern_avg,
         "kernel_ms_in_step_min": float(np.min(kern_ms)),
         "kernel_ms_in_step_p90": float(np.percentile(kern_ms, 90)),
@@ -530,16 +549,14 @@ def bench_split_sweep(tb, torch, args, cache, q, w):
 
 
 def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
-    """The same step as one captured HIP graph: append at device positions,
-    then varlen decode over device lengths; replayed back to back."""
+    """The same step as one captured HIP graph, the new token's slot read
+    from device memory; replayed back to back."""
     B, T = cache.batch, cache.capacity
     pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
-    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
 
     def step():
-        tb.quantize_append_at(cache, k_new, v_new, pos)
-        tb.attn_decode_varlen(cache, q, lens, T, w.softmax_scale, n_splits=P, out=out,
-                              workspace=ws)
+        tb.decode_step(cache, k_new, v_new, q, T - 1, w.softmax_scale, positions=pos,
+                       n_splits=P, out=out, workspace=ws)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -561,7 +578,8 @@ def bench_graph_step(tb, torch, args, cache, k_new, v_new, q, out, ws, P, w):
     ms = e0.elapsed_time(e1) / args.steps
     assert torch.isfinite(out.float()).all()
     return {"ms_per_step": ms, "replays": args.steps,
-            "note": "one captured graph per step (append_at + decode_varlen), replayed back to back"}
+            "note": "one captured graph per step (the decode step at device positions: split "
+                    "kernel with the new-token wavefronts + merge), replayed back to back"}
 
 
 def bench_verify(tb, torch, args, cache, w, n_q=4):
@@ -596,8 +614,9 @@ def bench_contexts(tb, torch, args):
     slots (batch 1, one layer; step = append one token + decode, 200 steps)
     and the long decode (batch 1, 4 layers, prefix 262080 slots, then 64
     steps that each append one token per layer and decode it over pos + 1
-    slots, layers back to back).  Automatic split counts; every call goes
-    through the library's decode entry point (split kernel + merge)."""
+    slots, layers back to back).  Automatic split counts; every step goes
+    through the library's decode-step entry point (the split kernel with the
+    new-token wavefronts, then the merge)."""
     from workloads import WORKLOADS, K, V, kv_tensor, q_decode
     res = []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -616,12 +635,12 @@ def bench_contexts(tb, torch, args):
     k_new, v_new = k[:, T - 1:].contiguous(), v[:, T - 1:].contiguous()
     q = torch.from_numpy(q_decode(w)).cuda()
     out = torch.empty((1, Hq, 128), dtype=torch.float16, device="cuda")
-    ws = torch.empty(tb.decode_workspace_bytes(1, H, Hq, T, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tb.decode_step_workspace_bytes(1, H, Hq, T, 0), dtype=torch.uint8,
+                     device="cuda")
     n = 200
 
     def step16():
-        tb.quantize_append(cache, k_new, v_new, T - 1)
-        tb.attn_decode(cache, q, T, w.softmax_scale, out=out, workspace=ws)
+        tb.decode_step(cache, k_new, v_new, q, T - 1, w.softmax_scale, out=out, workspace=ws)
 
     for _ in range(max(args.warmup, 20)):
         step16()
@@ -675,7 +694,8 @@ def bench_contexts(tb, torch, args):
     qs = [[torch.from_numpy(q_decode(w, layer, st)).cuda() for st in range(w.steps)]
           for layer in range(w.layers)]
     out = torch.empty((1, Hq, 128), dtype=torch.float16, device="cuda")
-    ws = torch.empty(tb.decode_workspace_bytes(1, H, Hq, T, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(tb.decode_step_workspace_bytes(1, H, Hq, T, 0), dtype=torch.uint8,
+                     device="cuda")
     for _ in range(max(args.warmup, 5)):          # warm-up on the prefix (no append)
         for layer in range(w.layers):
             tb.attn_decode(caches[layer], qs[layer][0], T0, w.softmax_scale, out=out, workspace=ws)
@@ -684,10 +704,8 @@ def bench_contexts(tb, torch, args):
     for st in range(w.steps):
         pos = T0 + st
         for layer in range(w.layers):
-            tb.quantize_append(caches[layer], new_k[layer][:, st:st + 1], new_v[layer][:, st:st + 1],
-                               pos)
-            tb.attn_decode(caches[layer], qs[layer][st], pos + 1, w.softmax_scale, out=out,
-                           workspace=ws)
+            tb.decode_step(caches[layer], new_k[layer][:, st:st + 1], new_v[layer][:, st:st + 1],
+                           qs[layer][st], pos, w.softmax_scale, out=out, workspace=ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / w.steps
@@ -1012,6 +1030,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms"], 5),
+        "ms_per_step_three_launches": round(dec["ms_unfused"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1020,7 +1039,9 @@ def main():
         "config": {
             "workload": "decode128k: batch 4 sequences, 8 KV / 64 query heads, head_dim 128, "
                         "131072 cached tokens in TBQ4 K and V (Student-t nu=5 x per-channel "
-                        "scales); step = append one token per sequence + split-K decode",
+                        "scales); step = append one token per sequence + split-K decode, as "
+                        "one decode-step call (split kernel whose extra wavefronts quantise, store "
+                        "and score the new token, then the merge)",
             "batch": 4, "n_ctx": 131072, "n_kv_heads": 8, "n_q_heads": 64, "n_splits": dec["P"],
             "hbm_frac_of_step": round(dec["value"] / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(dec["tokens_per_s"], 1),
@@ -1040,7 +1061,8 @@ def main():
             "results": dec["formats"],
         },
         "per_call_ms": {
-            "workload": "decode128k; step = append + split kernel + merge; warm: back to back "
+            "workload": "decode128k; step = one decode-step call (split kernel with the new-token "
+                        "wavefronts + merge); warm: back to back "
                         "(part of the cache stays in the 256 MB Infinity Cache), cold: 1 GiB "
                         "read before each timed call; each call between two HIP events",
             **dec["dists"],

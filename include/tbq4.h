@@ -345,6 +345,47 @@ tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4
                                     int32_t n_splits, void *workspace, size_t workspace_bytes,
                                     void *hip_stream);
 
+/* Decode step: append one token per sequence and attend over the cache that
+ * now holds it, in two launches instead of three.  The one-token step of a
+ * generation loop (page "Kontekst 262K na jednej RTX 4090: co dodałem do
+ * llama.cpp-turboq", section "Od czego zacząłem": quantise the new K/V into
+ * the cache, then flash attention over the raw blocks).  Same results as
+ * tbq4_quantize_append(k_new, v_new, pos, n_new = 1) followed by
+ * tbq4_attn_decode(n_ctx = pos + 1): the stored bytes are identical; the
+ * output differs only in rounding (the new token's score and value are
+ * taken in fp64 from its codes instead of through the fp16 MFMA operands).
+ * In the decode launch one extra wavefront per (sequence, KV head)
+ * quantises and stores the token and writes its own partial softmax state,
+ * while the other wavefronts stream the slots before it.
+ *   k_new, v_new  device, [batch][1][n_kv_heads][128] in src_dtype (F32, F16
+ *                 or BF16), 16-byte aligned.
+ *   pos, positions  positions == NULL: every sequence writes slot pos and
+ *                 attends slots [0, pos]; 0 <= pos < capacity, else
+ *                 TBQ4_ERR_CAPACITY.  positions = device int32 [batch], read
+ *                 when the kernel runs: sequence b writes slot positions[b] and
+ *                 attends [0, positions[b]], and pos is the largest position the
+ *                 call may meet (it sets the launch shape, the automatic split
+ *                 count and the workspace size, so a captured HIP graph replays
+ *                 unchanged while positions advance); a position outside
+ *                 [0, pos] writes nothing and gives that sequence a zero output.
+ *   q, out, softmax_scale, out_dtype  as tbq4_attn_decode.
+ *   n_splits     splits over the slots before the new token, in [1, 1023],
+ *                or 0 for the automatic count of tbq4_attn_decode at n_ctx =
+ *                pos + 1.
+ *   workspace    device, >= tbq4_decode_step_workspace_bytes(batch,
+ *                n_kv_heads, n_q_heads, pos + 1, n_splits) bytes, 16-byte
+ *                aligned: the decode layout with n_splits + 1 partial states
+ *                per (sequence, head), the new token's last.
+ * Errors as tbq4_quantize_append and tbq4_attn_decode. */
+size_t tbq4_decode_step_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                        int32_t n_ctx, int32_t n_splits);
+tbq4_status tbq4_decode_step(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                             tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
+                             const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                             float softmax_scale, void *out, tbq4_dtype out_dtype,
+                             int32_t n_splits, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
 /* Prefill-chunk attention: n_q new queries per sequence; query i sits at
  * absolute position n_past + i and attends slots [0, n_past + i] (causal
  * inside the chunk, full over the cached prefix).  Same attention as

@@ -22,7 +22,7 @@ from ._lib import BLOCK_BYTES, HEAD_DIM, MAX_SPLITS, NOALLOC_SCRATCH_BYTES
 __all__ = [
     "TBQ4Error", "KVCache", "quantize_append", "quantize_blocks", "attn_decode",
     "attn_decode_partial", "attn_decode_merge", "attn_decode_noalloc", "quantize_append_at",
-    "attn_decode_varlen", "NOALLOC_SCRATCH_BYTES",
+    "attn_decode_varlen", "NOALLOC_SCRATCH_BYTES", "decode_step", "decode_step_workspace_bytes",
     "attn_verify", "verify_workspace_bytes", "MixedKVCache", "mixed_append",
     "mixed_attn_decode", "mixed_attn_prefill_chunk", "mixed_attn_verify", "FMT_TBQ4", "FMT_F16", "FMT_TBQ3", "FMT_Q8_0",
     "attn_prefill_chunk", "sign_vector", "cache_bytes", "decode_auto_splits",
@@ -252,6 +252,47 @@ def attn_decode_varlen(cache, q, ctx_lens, max_ctx, softmax_scale, n_splits=0, o
         _ptr(out), _dtype(out), n_splits, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q.device)),
         "tbq4_attn_decode_varlen")
+    return out
+
+
+def decode_step_workspace_bytes(batch, n_kv_heads, n_q_heads, n_ctx, n_splits=0):
+    return _lib.lib().tbq4_decode_step_workspace_bytes(batch, n_kv_heads, n_q_heads, n_ctx,
+                                                       n_splits)
+
+
+def decode_step(cache, k_new, v_new, q, pos, softmax_scale, positions=None, n_splits=0, out=None,
+                out_dtype=torch.float16, workspace=None):
+    """Append one token per sequence (k_new, v_new: [batch][1][n_kv_heads][128])
+    and attend over the cache that holds it, in one decode launch and the
+    merge.  positions=None: every sequence writes slot pos and attends
+    [0, pos]; else positions is a device int32 tensor [batch] read when the
+    kernel runs (sequence b writes slot positions[b] and attends
+    [0, positions[b]]) and pos bounds them.  Returns out [batch][n_q_heads][128]."""
+    _require(q, "q")
+    _require(k_new, "k_new")
+    _require(v_new, "v_new", k_new.shape)
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must share a dtype")
+    if tuple(k_new.shape) != (cache.batch, 1, cache.n_kv_heads, HEAD_DIM):
+        raise ValueError("k_new must be [batch][1][n_kv_heads][128]")
+    if positions is not None:
+        _require(positions, "positions", (cache.batch,))
+        if positions.dtype != torch.int32:
+            raise TypeError("positions must be int32")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", (B, Hq, D))
+    if workspace is None:
+        need = decode_step_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, pos + 1, n_splits)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    d = cache.descriptor()
+    _check(_lib.lib().tbq4_decode_step(
+        ctypes.byref(d), _ptr(k_new), _ptr(v_new), _dtype(k_new), pos,
+        _ptr(positions) if positions is not None else None, _ptr(q), _dtype(q), Hq,
+        float(softmax_scale), _ptr(out), _dtype(out), n_splits, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device)),
+        "tbq4_decode_step")
     return out
 
 

@@ -557,6 +557,54 @@ tbq4_status tbq4_attn_decode_varlen(const tbq4_cache *cache, const void *q, tbq4
   return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
 }
 
+size_t tbq4_decode_step_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                        int32_t n_ctx, int32_t n_splits) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_ctx <= 0) return 0;
+  if (n_splits < 0 || n_splits > TBQ4_MAX_SPLITS) return 0;
+  const int32_t p = n_splits == 0 ? auto_splits(batch, n_kv_heads, n_ctx) : n_splits;
+  return round256((size_t)batch * n_q_heads * (p + 1) * 130 * sizeof(float));
+}
+
+tbq4_status tbq4_decode_step(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                             tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
+                             const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                             float softmax_scale, void *out, tbq4_dtype out_dtype,
+                             int32_t n_splits, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  if (!out || !k_new || !v_new) return TBQ4_ERR_INVALID_ARG;
+  if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
+  if (!valid_dtype(src_dtype)) return TBQ4_ERR_INVALID_ARG;
+  if (pos < 0) return TBQ4_ERR_CAPACITY;
+  if (pos == INT32_MAX) return TBQ4_ERR_CAPACITY;
+  // the checks of a decode over pos + 1 slots (capacity, heads, split count)
+  // with a stand-in workspace; the step's own size is checked below
+  tbq4::DecodeArgs a;
+  tbq4_status s = prepare_decode(cache, q, q_dtype, n_q_heads, pos + 1, softmax_scale, n_splits,
+                                 reinterpret_cast<void *>((uintptr_t)256), (size_t)-1, a);
+  if (s != TBQ4_OK) return s;
+  if (a.n_splits + 1 > TBQ4_MAX_SPLITS) return TBQ4_ERR_INVALID_ARG;
+  const size_t need = tbq4_decode_step_workspace_bytes(cache->batch, cache->n_kv_heads, n_q_heads,
+                                                       pos + 1, a.n_splits);
+  if (!workspace || workspace_bytes < need) return TBQ4_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(out)) return TBQ4_ERR_ALIGNMENT;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TBQ4_ERR_ALIGNMENT;
+  a.ws = (float *)workspace;
+  a.out = out;
+  a.n_ctx = pos;                // the streaming splits stop before the new token
+  a.ctx_lens = positions;       // (device mode: the token's slot per sequence)
+  a.n_splits += 1;              // the new token's partial state comes last
+  if ((int64_t)(a.n_splits + 1) * cache->n_kv_heads * cache->batch > 0x7FFFFFFF)
+    return TBQ4_ERR_UNSUPPORTED;  // one 1-D grid holds every wavefront
+  a.step = 1;
+  a.new_dtype = (int32_t)src_dtype;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  hipStream_t st = (hipStream_t)hip_stream;
+  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
+  if (s != TBQ4_OK) return s;
+  return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
+}
+
 // Prefill on K / V tensors in the given formats (TBQ4, fp16, TBQ3 or q8_0);
 // the cache view has been checked.
 static tbq4_status prefill_formats(const tbq4_cache *cache, int32_t k_fmt, int32_t v_fmt,

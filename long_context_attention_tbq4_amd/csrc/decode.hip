@@ -29,6 +29,7 @@
 //   * keeps the online-softmax state in the log2 domain.
 #include "tbq4_device.h"
 #include "tbq4_launch.h"
+#include "tbq4_quant.h"
 
 #include <hip/hip_ext.h>
 #include <mutex>
@@ -61,6 +62,153 @@ __device__ __forceinline__ uint32_t split_f16x2(float x0, float x1) {
   return hw | (uint32_t)__builtin_amdgcn_update_dpp(0, rw, 0x128, 0xF, 0xF, true);
 }
 
+// Level magnitude of a TBQ4 (bits 0-2) or TBQ3 (bits 0-1) code, signed by
+// its top bit: exact dyadic values.
+template <int FMT> __device__ __forceinline__ double code_level(int c) {
+  if constexpr (FMT == kFmtTbq3) {
+    const double mag = (c & 3) == 0 ? 0.25 : (c & 3) == 1 ? 0.75 : (c & 3) == 2 ? 1.375 : 2.25;
+    return (c & 4) ? -mag : mag;
+  } else {
+    constexpr double kMag[8] = {0.125, 0.375, 0.625, 0.9375, 1.25, 1.625, 2.0, 2.75};
+    const double mag = kMag[c & 7];
+    return (c & 8) ? -mag : mag;
+  }
+}
+
+// element i of a head vector of dtype 0 (fp32), 1 (fp16) or 2 (bf16), exact in fp64
+__device__ __forceinline__ double load_any(const void *row, int dtype, int i) {
+  if (dtype == 0) return load_exact<float>((const float *)row + i);
+  if (dtype == 1) return load_exact<_Float16>((const _Float16 *)row + i);
+  return load_exact<uint16_t>((const uint16_t *)row + i);
+}
+template <int FMT>
+__device__ __forceinline__ LaneCodes quantize_any(const void *row, int dtype, uint32_t w_a,
+                                                  uint32_t w_b, int lane) {
+  return quantize_values<FMT>(load_any(row, dtype, lane), load_any(row, dtype, lane + 64), w_a,
+                              w_b, lane);
+}
+
+// x of lane (lane ^ H) for an fp32 value (the quantiser's DPP / permlane
+// exchanges)
+template <int H> __device__ __forceinline__ float lane_xor_f32(float x, int lane) {
+  return __uint_as_float(lane_xor<H>(__float_as_uint(x), lane));
+}
+
+// The new token of a decode step, two wavefronts per (sequence b, KV head g),
+// which each quantise one of its head vectors with the append kernel's
+// arithmetic (identical bytes) and store it at the token's slot, and between
+// them write the token's own partial state for the G query heads of g as
+// split n_splits - 1:
+//   K wavefront: m = qscale * (q . k~), l = 1, with k~ = R^T (d^K level(code^K))
+//                (the dequantised key, rotated back in fp32);
+//   V wavefront: o' = d^V level(code^V) (rotated domain, as the splits keep it).
+// The streaming splits never read the token (they stop at its slot), so the
+// stores and the partial state need no ordering against them; the merge, a
+// later launch, sees them.  Splitting the work halves what each wavefront
+// takes from the vector unit of the SIMD it shares with two streaming
+// wavefronts.
+template <typename QT, int KF, int VF>
+__device__ void step_new_token(const DecodeArgs &a, int b, int g, int is_v, int lane) {
+  constexpr uint32_t kKB = KF == kFmtTbq3 ? kBlockBytes3 : kBlockBytes;
+  constexpr uint32_t kVB = VF == kFmtTbq3 ? kBlockBytes3 : kBlockBytes;
+  const int G = a.group, P = a.n_splits;
+  float *wsb = a.ws + ((size_t)b * a.n_q_heads + (size_t)g * G) * P * 130 + (size_t)(P - 1) * 130;
+  const int slot = a.ctx_lens ? a.ctx_lens[b] : a.n_ctx;
+  const bool none = slot < 0 || slot > a.n_ctx;   // no token for this sequence: an empty state
+  const size_t vec = (size_t)b * a.n_kv_heads + g;   // source row and cache row
+  const size_t at = vec * (size_t)a.capacity + (size_t)(none ? 0 : slot);
+  const uint32_t w_a = lane < 32 ? a.sign[0] : a.sign[1];
+  const uint32_t w_b = lane < 32 ? a.sign[2] : a.sign[3];
+  const size_t src = vec * kHeadDim * (a.new_dtype == 0 ? 4 : 2);
+  if (is_v) {
+    float o0 = 0.0f, o1 = 0.0f;
+    if (!none) {
+      const LaneCodes vc = quantize_any<VF>((const uint8_t *)a.v_new + src, a.new_dtype, w_a, w_b,
+                                            lane);
+      // the caches are the caller's writable buffers (held const for the streaming splits)
+      store_lanes<VF>(const_cast<uint8_t *>(a.v) + at * kVB, vc, lane);
+      const double dv = half_value(vc.dbits);
+      o0 = (float)(dv * code_level<VF>(vc.c0));   // exact: <= 15 significant bits
+      o1 = (float)(dv * code_level<VF>(vc.c1));
+    }
+    for (int h = 0; h < G; ++h) {
+      float *w = wsb + (size_t)h * P * 130;
+      w[2 + lane] = o0;
+      w[66 + lane] = o1;
+    }
+    return;
+  }
+  if (none) {
+    for (int h = 0; h < G; ++h) {
+      if (lane == 0) {
+        float *w = wsb + (size_t)h * P * 130;
+        w[0] = -INFINITY;
+        w[1] = 0.0f;
+      }
+    }
+    return;
+  }
+  // the queries' two values per lane, loaded before the quantiser runs
+  const QT *qb = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * kHeadDim;
+  float qa[8], qc[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    qa[h] = h < G ? load_q<QT>(qb + (size_t)h * kHeadDim + lane) : 0.0f;
+    qc[h] = h < G ? load_q<QT>(qb + (size_t)h * kHeadDim + lane + 64) : 0.0f;
+  }
+  const LaneCodes kc = quantize_any<KF>((const uint8_t *)a.k_new + src, a.new_dtype, w_a, w_b,
+                                        lane);
+  store_lanes<KF>(const_cast<uint8_t *>(a.k) + at * kKB, kc, lane);
+  // k~ = s * (H k') / sqrt(128), elements lane and lane + 64, in fp32
+  const float dk = (float)half_value(kc.dbits);
+  float k0 = dk * (float)code_level<KF>(kc.c0), k1 = dk * (float)code_level<KF>(kc.c1);
+#pragma unroll
+  for (int hh = 1; hh < 64; hh <<= 1) {
+    float p0, p1;
+    switch (hh) {
+      case 1: p0 = lane_xor_f32<1>(k0, lane); p1 = lane_xor_f32<1>(k1, lane); break;
+      case 2: p0 = lane_xor_f32<2>(k0, lane); p1 = lane_xor_f32<2>(k1, lane); break;
+      case 4: p0 = lane_xor_f32<4>(k0, lane); p1 = lane_xor_f32<4>(k1, lane); break;
+      case 8: p0 = lane_xor_f32<8>(k0, lane); p1 = lane_xor_f32<8>(k1, lane); break;
+      case 16: p0 = lane_xor_f32<16>(k0, lane); p1 = lane_xor_f32<16>(k1, lane); break;
+      default: p0 = lane_xor_f32<32>(k0, lane); p1 = lane_xor_f32<32>(k1, lane); break;
+    }
+    const bool upper = (lane & hh) != 0;
+    k0 = upper ? (p0 - k0) : (k0 + p0);
+    k1 = upper ? (p1 - k1) : (k1 + p1);
+  }
+  {
+    const float x = k0, y = k1;
+    k0 = x + y;
+    k1 = x - y;
+  }
+  const float r = 0.08838834764831845f;
+  k0 = ((w_a >> (lane & 31)) & 1u) ? -(k0 * r) : k0 * r;
+  k1 = ((w_b >> (lane & 31)) & 1u) ? -(k1 * r) : k1 * r;
+  float sc[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) sc[h] = fmaf(qa[h], k0, qc[h] * k1);
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    sc[h] += lane_xor_f32<32>(sc[h], lane);
+    sc[h] += lane_xor_f32<16>(sc[h], lane);
+    sc[h] += lane_xor_f32<8>(sc[h], lane);
+    sc[h] += lane_xor_f32<4>(sc[h], lane);
+    sc[h] += lane_xor_f32<2>(sc[h], lane);
+    sc[h] += lane_xor_f32<1>(sc[h], lane);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      if (h < G) {
+        float *w = wsb + (size_t)h * P * 130;
+        w[0] = sc[h] * a.qscale;
+        w[1] = 1.0f;
+      }
+    }
+  }
+}
+
 template <typename QT, int KF, int VF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // bytes per head vector of each tensor
@@ -79,7 +227,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float sv[kTile + 32];   // d^V per token, then zeros
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if constexpr ((KF == kFmtTbq4 || KF == kFmtTbq3) && (VF == kFmtTbq4 || VF == kFmtTbq3)) {
+    if (a.step) {
+      // decode step: a 1-D grid of the streaming splits in (split, head,
+      // sequence) order -- the order and XCD placement of the plain 3-D grid
+      // -- followed by two new-token wavefronts per (head, sequence).  The
+      // new-token wavefronts come last so that the dispatcher has already
+      // given every SIMD its share of streaming wavefronts when they arrive.
+      const int n_stream = a.n_splits - 1;
+      const int L = blockIdx.x;
+      const int rows = (int)gridDim.x / (n_stream + 2);   // n_kv_heads * batch
+      if (L >= n_stream * rows) {   // the new token: K then V wavefront of each row
+        const int e = L - n_stream * rows, r = e >> 1;
+        step_new_token<QT, KF, VF>(a, r / a.n_kv_heads, r % a.n_kv_heads, e & 1, lane);
+        return;
+      }
+      split = L % n_stream;
+      g = (L / n_stream) % a.n_kv_heads;
+      b = L / (n_stream * a.n_kv_heads);
+    }
+  }
   const int G = a.group;
   const int quarter = lane >> 4;       // 32-dimension quarter / token sub-group
   const int col = lane & 15;           // MFMA column: query head (col & 7), part col >> 3
@@ -164,10 +332,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   // ---------------- token range of this split: this sequence's length (from
   // device memory when given) in 32-token tiles, spread evenly over the splits
+  // (a decode step: the slots before the new token's, none when its slot is
+  // outside [0, n_ctx]; the last split index is the new token's)
   int n_ctx = a.n_ctx;
-  if (a.ctx_lens) n_ctx = min(max(a.ctx_lens[b], 0), a.n_ctx);
+  if (a.ctx_lens) {
+    const int len = a.ctx_lens[b];
+    n_ctx = a.step && (len < 0 || len > a.n_ctx) ? 0 : min(max(len, 0), a.n_ctx);
+  }
+  const int n_stream = a.n_splits - a.step;
   const int n_tiles = (n_ctx + kTile - 1) / kTile;
-  const int tiles_per_split = (n_tiles + a.n_splits - 1) / a.n_splits;
+  const int tiles_per_split = (n_tiles + n_stream - 1) / n_stream;
   const int t_begin = split * tiles_per_split;
   const int t_end = min(t_begin + tiles_per_split, n_tiles);
 
@@ -795,7 +969,12 @@ hipError_t decode_scratch(hipStream_t stream, void **ptr) {
 
 hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hipStream_t stream,
                                  hipEvent_t start, hipEvent_t stop) {
-  dim3 grid(a.n_splits, a.n_kv_heads, batch);
+  // (the decode step: a 1-D grid, streaming splits first, new-token
+  // wavefronts last)
+  // (n_splits - 1 streaming splits + 2 new-token wavefronts per row)
+  const int64_t n_wg = (int64_t)(a.n_splits + 1) * a.n_kv_heads * batch;
+  if (a.step && n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid = a.step ? dim3((unsigned)n_wg, 1, 1) : dim3(a.n_splits, a.n_kv_heads, batch);
   // (q dtype, K format, V format) -> kernel instance
 #define TBQ4_DEC(QT, KF, VF) reinterpret_cast<const void *>(&decode_split_kernel<QT, KF, VF>)
 #define TBQ4_DEC_K(QT, KF) {TBQ4_DEC(QT, KF, 0), TBQ4_DEC(QT, KF, 1), TBQ4_DEC(QT, KF, 2), TBQ4_DEC(QT, KF, 3)}

@@ -45,6 +45,16 @@ struct DecodeArgs {
   int32_t rotate_out;    // merge applies R^T (the V cache holds rotated values)
   float qscale;          // softmax_scale * log2(e)
   uint32_t sign[4];      // sign bits 0..31, 32..63, 64..95, 96..127
+  // Decode step (append + attend in one launch; TBQ K and V): the last of
+  // the n_splits partial states of each head is the new token's, written by
+  // two extra wavefronts per (sequence, KV head) that also store its blocks.
+  // The new token sits at slot ctx_lens[b] (device) or n_ctx (host) and the
+  // other splits stream the slots before it; a device slot outside
+  // [0, n_ctx] gives that sequence no token and no context.
+  int32_t step;          // 0: plain decode; 1: decode step
+  int32_t new_dtype;     // dtype of k_new / v_new (0 fp32, 1 fp16, 2 bf16)
+  const void *k_new;     // [B][H_kv][128]
+  const void *v_new;
 };
 
 struct VerifyArgs {

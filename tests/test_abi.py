@@ -182,6 +182,40 @@ def test_decode_varlen_argument_errors(L):
     assert dec(out=FAKE + 8) == _lib.ERR_ALIGNMENT
 
 
+def test_decode_step_argument_errors(L):
+    """The fused step makes the append's and the decode's checks on the host
+    (pos + 1 slots attended; one more partial state per head in the
+    workspace)."""
+    c = _cache(heads=2, cap=64)
+    need = L.tbq4_decode_step_workspace_bytes(1, 2, 8, 64, 4)
+    assert need == ((1 * 8 * 5 * 130 * 4 + 255) // 256) * 256
+    assert L.tbq4_decode_step_workspace_bytes(1, 2, 8, 64, 1025) == 0
+    assert L.tbq4_decode_step_workspace_bytes(1, 2, 8, 0, 4) == 0
+
+    def step(cache=c, kn=FAKE, vn=FAKE, sdt=0, pos=10, positions=None, q=FAKE, qdt=0, hq=8,
+             out=FAKE, odt=1, p=4, w=FAKE, wb=need):
+        return L.tbq4_decode_step(ctypes.byref(cache) if cache is not None else None, kn, vn, sdt,
+                                  pos, positions, q, qdt, hq, 1.0, out, odt, p, w, wb, None)
+    assert step(cache=None) == _lib.ERR_INVALID_ARG
+    assert step(kn=None) == _lib.ERR_INVALID_ARG
+    assert step(out=None) == _lib.ERR_INVALID_ARG
+    assert step(sdt=5) == _lib.ERR_INVALID_ARG
+    assert step(odt=2) == _lib.ERR_INVALID_ARG
+    assert step(qdt=4) == _lib.ERR_INVALID_ARG
+    assert step(pos=-1) == _lib.ERR_CAPACITY
+    assert step(pos=64) == _lib.ERR_CAPACITY          # slot past the capacity
+    assert step(pos=2 ** 31 - 1) == _lib.ERR_CAPACITY
+    assert step(hq=7) == _lib.ERR_UNSUPPORTED
+    assert step(hq=18) == _lib.ERR_UNSUPPORTED
+    assert step(p=1024) == _lib.ERR_INVALID_ARG       # 1024 splits + the new token's
+    assert step(p=-1) == _lib.ERR_INVALID_ARG
+    assert step(w=None) == _lib.ERR_WORKSPACE
+    assert step(wb=need - 256) == _lib.ERR_WORKSPACE  # the decode's size is one split short
+    assert step(kn=FAKE + 4) == _lib.ERR_ALIGNMENT
+    assert step(out=FAKE + 8) == _lib.ERR_ALIGNMENT
+    assert step(cache=_cache(cap=60)) == _lib.ERR_ALIGNMENT
+
+
 def test_verify_argument_errors(L):
     c = _cache(heads=2, cap=64)
     ws = 1 << 20
