@@ -276,6 +276,8 @@ def test_rising_scores_and_large_v_scales(vmag, P):
                          n_splits=P, out_dtype=torch.float32).cpu().numpy()
     ref = o.attn_decode_ref(q[:, 0], kc, vc, T, 1 / math.sqrt(128), 3)
     check_attn(out / vmag, ref / vmag, False, f"vmag={vmag} P={P}")
+    if vmag <= 300.0:   # and at the bare absolute bound while |V| stays in the hundreds
+        check_attn(out, ref, False, f"bare bound vmag={vmag} P={P}")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
