@@ -91,6 +91,9 @@ def parse():
     p.add_argument("--no-formats", dest="formats", action="store_false",
                    help="skip the decode timings of the TBQ3 / fp16 cache formats")
     p.add_argument("--prefill-steps", type=int, default=0)
+    p.add_argument("--prefill-only", action="store_true",
+                   help="only time the prefill chunk (for profiler passes over that kernel) and "
+                        "print its measurements as one JSON line")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB five times "
                         "(reference for the profiler's byte counters) and exit")
@@ -1008,6 +1011,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(tb, torch, args)}), flush=True)
         return
     man = manifest(torch)
     den = bench_denominators(tb, torch)
