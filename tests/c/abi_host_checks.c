@@ -69,6 +69,11 @@ int main(void) {
         TBQ4_ERR_CAPACITY);
   CHECK(tbq4_attn_verify(&c, fake, TBQ4_F32, 16, 10, 5, 1.0f, fake, TBQ4_F16, 0, fake, 1 << 20,
                          NULL) == TBQ4_ERR_UNSUPPORTED);
+  CHECK(tbq4_decode_step_workspace_bytes(1, 2, 8, 64, 4) == ((size_t)8 * 5 * 130 * 4 + 255) / 256 * 256);
+  CHECK(tbq4_decode_step(&c, fake, fake, TBQ4_F32, 64, NULL, fake, TBQ4_F32, 8, 1.0f, fake,
+                         TBQ4_F16, 4, fake, 1 << 20, NULL) == TBQ4_ERR_CAPACITY);
+  CHECK(tbq4_decode_step(&c, fake, fake, TBQ4_F32, 10, NULL, fake, TBQ4_F32, 8, 1.0f, fake,
+                         TBQ4_F16, 4, fake, 8 * 4 * 130 * 4, NULL) == TBQ4_ERR_WORKSPACE);
   tbq4_mixed_cache m = {fake, fake, TBQ4_FMT_TBQ4, TBQ4_FMT_Q8_0, 1, 2, 128, 64, 0};
   CHECK(tbq4_mixed_append(&m, fake, fake, TBQ4_F32, 60, 5, NULL) == TBQ4_ERR_CAPACITY);
   m.v_format = 7;

@@ -1,9 +1,9 @@
 """The C ABI end to end on the GPU: tests/c/abi_gpu_decode.c (plain C, gcc,
 the HIP runtime's C API for device memory) quantise-appends seeded K/V rows and
-runs decode attention through include/tbq4.h; its packed caches must be the
-oracle's bytes and its output must meet the attention bar against the fp64
-oracle (method: page "Kontekst 262K na jednej RTX 4090: co dodałem do
-llama.cpp-turboq", section "Od czego zacząłem")."""
+runs decode attention, and the one-call decode step, through include/tbq4.h;
+its packed caches must be the oracle's bytes and its outputs must meet the
+attention bar against the fp64 oracle (method: page "Kontekst 262K na jednej
+RTX 4090: co dodałem do llama.cpp-turboq", section "Od czego zacząłem")."""
 
 import os
 import shutil
@@ -53,3 +53,10 @@ def test_c_program_decodes_on_gpu(tmp_path, B, H, G, n_ctx, cap, P):
     assert not kc[:, :, n_ctx:].any() and not vc[:, :, n_ctx:].any()
     ref = o.attn_decode_ref(q, want_k, want_v, n_ctx, np.float32(scale), seed)
     check_attn(out, ref, False, f"C program decode B={B} H={H} G={G} n_ctx={n_ctx} P={P}")
+    # the decode step (prefix appended, then the last token appended and
+    # attended in one call): the same bytes and the same attention bar
+    kc2 = np.fromfile(tmp_path / "kc_step.bin", np.uint8).reshape(B, H, cap, 66)
+    vc2 = np.fromfile(tmp_path / "vc_step.bin", np.uint8).reshape(B, H, cap, 66)
+    out2 = np.fromfile(tmp_path / "out_step.bin", np.float32).reshape(B, H * G, 128)
+    assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)
+    check_attn(out2, ref, False, f"C program decode step B={B} H={H} G={G} n_ctx={n_ctx} P={P}")
