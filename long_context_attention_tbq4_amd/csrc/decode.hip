@@ -828,13 +828,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
 // Merge: o = R^T (sum_p 2^(m_p - M) o'_p / sum_p 2^(m_p - M) l_p), one
 // workgroup of NW wavefronts per (sequence, query head), in one pass over the
-// partials.  Wavefront w takes splits w, w + NW, ... in chunks of 16 (lane
-// holds dims lane and lane + 64), all loads of a chunk in flight together,
-// combined under a running maximum; the wavefronts' sums meet in LDS,
-// rescaled to the common maximum, and wavefront 0 normalises, applies the
-// inverse rotation and stores.  Empty splits carry m = -inf and weigh 0.
-// NW grows with the split count (16 NW splits per round) so that up to 256
-// splits are read in one round of loads.
+// partials.  Wavefront w takes splits w, w + NW, ... in chunks of
+// kMergeChunk (lane holds dims lane and lane + 64), all loads of a chunk in
+// flight together, combined under a running maximum; the wavefronts' sums
+// meet in LDS, rescaled to the common maximum, and wavefront 0 normalises,
+// applies the inverse rotation and stores.  Empty splits carry m = -inf and
+// weigh 0.  NW grows with the split count (kMergeChunk NW splits per round)
+// so that up to 272 splits are read in one round of loads; 17 per wavefront
+// let a decode step's extra partial state (the new token's, after 64, 128 or
+// 256 splits) in without a larger workgroup or a second round.
+constexpr int kMergeChunk = 17;   // partial states per wavefront and round of loads
+
 template <typename OT, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float red[NW][130];   // o'[128], l, m per wavefront
@@ -844,12 +848,12 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(DecodeArgs a) {
   const float *base = a.ws + ((size_t)b * a.n_q_heads + h) * P * 130;
 
   float M = -INFINITY, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int p0 = wave; p0 < P; p0 += 16 * NW) {
-    float mp[16], lp[16], x0[16], x1[16];
+  for (int p0 = wave; p0 < P; p0 += kMergeChunk * NW) {
+    float mp[kMergeChunk], lp[kMergeChunk], x0[kMergeChunk], x1[kMergeChunk];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kMergeChunk; ++u) {
       // splits past P reread split p0 (valid: p0 < P) and weigh 0, so that
-      // the 64 loads issue together without branches
+      // the chunk's loads issue together without branches
       const int p = p0 + NW * u;
       const float *bp = base + (size_t)(p < P ? p : p0) * 130;
       mp[u] = bp[0];
@@ -858,18 +862,18 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(DecodeArgs a) {
       x1[u] = bp[66 + lane];
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+    for (int u = 0; u < kMergeChunk; ++u)
       if (p0 + NW * u >= P) mp[u] = -INFINITY;
     float cm = M;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) cm = fmaxf(cm, mp[u]);
+    for (int u = 0; u < kMergeChunk; ++u) cm = fmaxf(cm, mp[u]);
     if (cm == -INFINITY) continue;   // only empty splits so far (wavefront-uniform)
     const float al = __builtin_amdgcn_exp2f(M - cm);   // 0 while M is -inf
     L *= al;
     o0 *= al;
     o1 *= al;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kMergeChunk; ++u) {
       const float wt = __builtin_amdgcn_exp2f(mp[u] - cm);
       L = fmaf(wt, lp[u], L);
       o0 = fmaf(wt, x0[u], o0);
@@ -1001,7 +1005,7 @@ hipError_t launch_decode_partial(const DecodeArgs &a, int batch, int q_dtype, hi
 hipError_t launch_decode_merge(const DecodeArgs &a, int batch, int out_dtype, hipStream_t stream) {
   dim3 grid(a.n_q_heads, batch);
   // wavefronts per workgroup: all splits in one round of 16 per wavefront
-  const int nw = a.n_splits <= 64 ? 4 : a.n_splits <= 128 ? 8 : 16;
+  const int nw = a.n_splits <= 4 * kMergeChunk ? 4 : a.n_splits <= 8 * kMergeChunk ? 8 : 16;
   static const void *const kernels[2][3] = {
       {reinterpret_cast<const void *>(&decode_merge_kernel<float, 4>),
        reinterpret_cast<const void *>(&decode_merge_kernel<float, 8>),
