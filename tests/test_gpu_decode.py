@@ -139,6 +139,18 @@ def test_decode16k_workload_full():
                                      out_dtype=od)
                 check_attn(out.float().cpu().numpy(), ref, od == torch.float16,
                            f"16k scale={scale} P={P} {od}")
+        # the decode step (bench.py's): the last token appended again (same
+        # bytes) and attended in one call
+        for P in (0, 64):
+            for od in (torch.float16, torch.float32):
+                out = tb.decode_step(cache, torch.from_numpy(k[:, T - 1:].copy()).cuda(),
+                                     torch.from_numpy(v[:, T - 1:].copy()).cuda(),
+                                     torch.from_numpy(q).cuda(), T - 1, scale, n_splits=P,
+                                     out_dtype=od)
+                check_attn(out.float().cpu().numpy(), ref, od == torch.float16,
+                           f"16k decode step scale={scale} P={P} {od}")
+    assert np.array_equal(cache.k.cpu().numpy(), kc)
+    assert np.array_equal(cache.v.cpu().numpy(), vc)
 
 
 @pytest.mark.slow
@@ -150,7 +162,8 @@ def test_decode128k_workload_full():
     re-quantised by the oracle in worker processes (all appended bytes
     compared) and every output of every query head is checked, for split
     counts 16 .. 256 and the automatic one, with fp16 output and with fp32
-    output at the bare bound."""
+    output at the bare bound; and the decode step (the last token appended
+    again and attended in one call, bench.py's step)."""
     from _rows import decode_row, pool_map
     w = WORKLOADS["decode128k"]
     T = w.n_ctx
@@ -168,6 +181,13 @@ def test_decode128k_workload_full():
     outs = {(n, P, od): tb.attn_decode(cache, qt, n, w.softmax_scale, n_splits=P,
                                        out_dtype=od).float().cpu().numpy()
             for n in (T96, T) for P in splits for od in (torch.float16, torch.float32)}
+    # the decode step as bench.py times it: the last token appended again
+    # (the same row, so the same bytes) and attended in one call
+    k_last = torch.from_numpy(kv_tensor(w, 0, 0, T - 1, T)).cuda()
+    v_last = torch.from_numpy(kv_tensor(w, 0, 1, T - 1, T)).cuda()
+    steps = {(P, od): tb.decode_step(cache, k_last, v_last, qt, T - 1, w.softmax_scale,
+                                     n_splits=P, out_dtype=od).float().cpu().numpy()
+             for P in (0, 64, 256) for od in (torch.float16, torch.float32)}
     kg, vg = cache.k.cpu().numpy(), cache.v.cpu().numpy()
     del cache
     torch.cuda.empty_cache()
@@ -182,6 +202,8 @@ def test_decode128k_workload_full():
             refs.setdefault(n, np.empty((B, w.n_q_heads, 128)))[b, g * G:(g + 1) * G] = r[n]
     for (n, P, od), out in outs.items():
         check_attn(out, refs[n], od == torch.float16, f"n={n} P={P} {od}")
+    for (P, od), out in steps.items():
+        check_attn(out, refs[T], od == torch.float16, f"decode step P={P} {od}")
 
 
 def test_two_phase_equals_one_call():

@@ -5,7 +5,9 @@ section "Konfiguracja" fixes the context at 262,144 tokens; section "4.
 Poprawność w długich sesjach" asks for correct long sessions.  Workload: batch
 1, 8 KV / 64 query heads, K/V Student-t (nu = 3) plus a per-(layer, tensor,
 head, channel) Gaussian random-walk mean, prefix 262,080 slots, then 64 steps
-that each append one token per layer and decode it.  Checked: for every KV
+that each append one token per layer and decode it (one decode-step call per
+layer, the path bench.py times; the plain decode call at the checked steps).
+Checked: for every KV
 head of every layer the whole packed cache row (prefix and the 64 appended
 tokens) is byte-identical to the oracle's, and the decode outputs of every
 query head at steps 0, 31 and 63 of every layer are within max-abs 2e-3 and
@@ -47,18 +49,19 @@ def test_longdecode_262k_four_layers():
         caches.append(cache)
     torch.cuda.synchronize()
 
-    # the 64 steps: per layer, append one token, then decode over pos + 1
-    # slots (at the checked steps once more with fp32 output)
+    # the 64 steps: per layer, one decode-step call (append the token at pos
+    # and attend over pos + 1 slots, as bench.py times it); at the checked
+    # steps the plain decode call once more, with fp32 output
     outs = {}
-    ws = torch.empty(tb.decode_workspace_bytes(1, H, w.n_q_heads, T, 0), dtype=torch.uint8,
+    ws = torch.empty(tb.decode_step_workspace_bytes(1, H, w.n_q_heads, T, 0), dtype=torch.uint8,
                      device="cuda")
     for step in range(w.steps):
         pos = w.n_ctx + step
         for layer in range(w.layers):
-            tb.quantize_append(caches[layer], new_k[layer][:, step:step + 1].contiguous(),
-                               new_v[layer][:, step:step + 1].contiguous(), pos)
             q = torch.from_numpy(q_decode(w, layer, step)).cuda()
-            out = tb.attn_decode(caches[layer], q, pos + 1, w.softmax_scale, workspace=ws)
+            out = tb.decode_step(caches[layer], new_k[layer][:, step:step + 1].contiguous(),
+                                 new_v[layer][:, step:step + 1].contiguous(), q, pos,
+                                 w.softmax_scale, workspace=ws)
             if step in CHECK_STEPS:
                 outs[(layer, step, torch.float16)] = out.float().cpu().numpy()
                 outs[(layer, step, torch.float32)] = tb.attn_decode(
