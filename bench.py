@@ -6,31 +6,31 @@
 One step = one pass of the whole decode hot path over the decode128k workload
 (batch 4 independent sequences, 8 KV / 64 query heads, head_dim 128, 131072
 cached tokens in TBQ4 K and V caches resident in HBM): quantise-append the new
-token's K and V for every sequence, then split-K decode attention over all
-131072 slots (partial kernel + merge kernel).  The headline value is the
-step's algorithmic HBM bytes (packed K+V read, q read, output written, appended
-rows) divided by the step time, in GB/s.  The prefill-chunk workload (2048
-queries on 131072 cached tokens, 8 KV / 64 query heads, append of the chunk's
-K/V then causal attention) is timed in the same run and reported under
-"prefill" in TFLOP/s (4 * 128 * 64 FLOPs per unmasked (query, key) pair).
-The same decode rows stored as TBQ3, q8_0 or fp16 K / V tensors (mixed
-formats) are timed under "formats" (one decode call per format pair, KV GB/s),
-and the prefill chunk over TBQ3 and fp16 caches under "prefill"."formats".
-Decode at 16384 slots (batch 1) and the 4-layer long decode at 262144 slots
-(batch 1, 64 append + decode steps per layer) are timed under "contexts".
+token's K and V for every sequence and split-K decode attention over all
+131072 slots, as one tbq4_decode_step call (the split kernel, whose extra
+wavefronts quantise, store and score the new token, then the merge kernel).
+The headline value is the step's algorithmic HBM bytes (packed K+V read, q
+read, output written, appended rows) divided by the step time, in GB/s; the
+same step as three launches (append, split kernel, merge) is timed beside it.
+The prefill-chunk workload (2048 queries on 131072 cached tokens, 8 KV / 64
+query heads, append of the chunk's K/V then causal attention) is timed in the
+same run and reported under "prefill" in TFLOP/s (4 * 128 * 64 FLOPs per
+unmasked (query, key) pair).  The same decode rows stored as TBQ3, q8_0 or
+fp16 K / V tensors (mixed formats) are timed under "formats" (one decode call
+per format pair, KV GB/s), and the prefill chunk over TBQ3 and fp16 caches
+under "prefill"."formats".  Decode at 16384 slots (batch 1) and the 4-layer
+long decode at 262144 slots (batch 1, 64 decode steps per layer) are timed
+under "contexts".
 
 Before the W warm-up steps, S untimed steps (default 1000, ~0.12 s) let the
 clocks settle: the first milliseconds of sustained load run faster, then the
 clocks dip and recover over tens of milliseconds.  The step value is timed
-over K steps without any event markers.  A second loop of the same K steps
-records HIP events from the dispatch of every decode-partial launch (start and
-end of that kernel's execution; each pair of markers leaves the GPU idle for
-several microseconds around the kernel, which is why the step time is taken
-without them): their mean is reported as kernel_ms_in_step.  Then the split
-kernel alone is launched K times back to back between two events on the
-stream it runs on: its mean duration there is the roofline's kernel_ms (the
-dispatch-recorded events read a few microseconds per call more than a kernel
-trace of the same calls).
+over K steps (default 200, ~23 ms) without any event markers.  A second loop
+of the same K steps records HIP events from the dispatch of every split
+kernel (start and end of that kernel's execution): their mean is the
+roofline's kernel_ms, and the kernel's algorithmic bytes over it the
+roofline's achieved rate.  The plain split kernel is also timed inside K
+three-launch steps and K times back to back with no gaps.
 The CPU oracle is timed on a bounded sample of the same workload (rows of the
 decode cache, fp64 dequantise + attention) on the host's cores.
 
@@ -48,16 +48,17 @@ import numpy as np
 
 METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 
-# HBM bytes per decode_split_kernel launch on this workload (64 splits), from
-# two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch)
-# scaled by what the same counters read for a plain 256 MiB device copy
-# (FETCH_SIZE reads half the copied bytes -> x2.0; WRITE_SIZE reads them all
-# -> x1.0).  Reported only while the kernel's sources hash to the version the
-# counters were taken on; otherwise the traffic is unknown (null).
+# HBM bytes per launch of the decode step's split kernel on this workload (64
+# streaming splits + the new-token wavefronts), from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same
+# counters read for a plain 256 MiB device copy (FETCH_SIZE reads half the
+# copied bytes -> x2.0; WRITE_SIZE reads them all -> x1.0).  Reported only while
+# the kernel's sources hash to the version the counters were taken on;
+# otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "c98dc5ae0828bd5ea5d6f0106caa0115c48e42d9d40033553b5a7d76ffa1752a",
-           "n_splits": 64, "fetch_kib": 271211.1, "fetch_factor": 2.0,
-           "write_kib": 8704.1, "write_factor": 1.0}
+TRAFFIC = {"sources_sha256": "f1716435a7e4568d629b6553ba2249aff96943bde9f344bb677aa3fb494af161",
+           "n_splits": 64, "fetch_kib": 271284.2, "fetch_factor": 2.0,
+           "write_kib": 8852.0, "write_factor": 1.0}
 
 
 def measured_traffic(n_splits):
@@ -79,8 +80,10 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # 200 timed steps (~23 ms): a window long enough that a clock transient of
+    # a few ms does not decide the step time
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--settle", type=int, default=SETTLE_STEPS,
                    help="untimed decode steps before the warm-up steps (clock settling)")
@@ -333,18 +336,20 @@ def bench_decode(tb, torch, args):
 
     hip = HipEvents(args.steps)
 
-    def step():
+    hip3 = HipEvents(args.steps)
+
+    def step(i=None):
         """the decode step: the new token appended and attended in the split
-        kernel's launch (one extra wavefront per (sequence, KV head)), then
-        the merge"""
+        kernel's launch (two extra wavefronts per (sequence, KV head)), then
+        the merge; with i, the split kernel's dispatch records HIP events"""
         tb.decode_step(cache, k_new, v_new, q, T - 1, w.softmax_scale, n_splits=P, out=out,
-                       workspace=ws)
+                       workspace=ws, events=None if i is None else hip.pair(i))
 
     def step_unfused(i=None):
         """the same step as three launches: append, split kernel, merge"""
         tb.quantize_append(cache, k_new, v_new, T - 1)
         tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws,
-                               events=None if i is None else hip.pair(i))
+                               events=None if i is None else hip3.pair(i))
         tb.attn_decode_merge(ws, B, Hq, P, cache.sign_seed, out=out)
 
     # Under sustained load the clocks dip within ~4 ms and recover over tens
@@ -360,7 +365,16 @@ def bench_decode(tb, torch, args):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the same steps as three launches (append, split kernel, merge)
+    # the step's split kernel inside the steps: the same K steps again, each
+    # split dispatch recording HIP events (their markers add small idle gaps
+    # around the kernel, so the step time above is taken without them)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern_ms = hip.elapsed_ms()
+    hip.destroy()
+    # the same steps as three launches (append, split kernel, merge), and the
+    # plain split kernel's duration inside them
     for _ in range(args.warmup):
         step_unfused()
     torch.cuda.synchronize()
@@ -369,16 +383,14 @@ def bench_decode(tb, torch, args):
         step_unfused()
     torch.cuda.synchronize()
     wall_unfused = time.perf_counter() - t0
-    # the split kernel's duration inside those steps: HIP events recorded by
-    # every split dispatch (their markers add idle gaps around the kernel, so
-    # the step times above are taken without them)
     for i in range(args.steps):
         step_unfused(i)
     torch.cuda.synchronize()
-    kern_ms = hip.elapsed_ms()
-    hip.destroy()
-    # and the split kernel alone: the same K launches back to back between
-    # two events on the stream they run on (no markers between launches)
+    kern3_ms = hip3.elapsed_ms()
+    hip3.destroy()
+    # and the plain split kernel alone: K launches back to back between two
+    # events on the stream they run on (no markers, no gaps: the hottest
+    # case for the clocks)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -418,13 +430,18 @@ def bench_decode(tb, torch, args):
     ms = wall * 1e3 / args.steps
     ms_unfused = wall_unfused * 1e3 / args.steps
     kern_avg = float(np.mean(kern_ms))
-    achieved = (kv_bytes + q_bytes) / (kern_b2b * 1e-3) / 1e9
+    # the step's split kernel: packed K+V of the T - 1 slots before the new
+    # token, the queries, the new token's fp32 K and V rows and its two blocks
+    kernel_bytes = (B * (T - 1) * Hkv * 2 * 66 + q_bytes + 2 * B * Hkv * 128 * 4
+                    + 2 * B * Hkv * 66)
+    achieved = kernel_bytes / (kern_avg * 1e-3) / 1e9
     assert torch.isfinite(out.float()).all()
     return {
         "P": P, "ms": ms, "value": step_bytes / (ms * 1e-3) / 1e9, "ms_unfused": ms_unfused,
-        "kernel_ms": kern_b2b, "kernel_ms_in_step": kern_avg,
-        "kernel_ms_in_step_min": float(np.min(kern_ms)),
-        "kernel_ms_in_step_p90": float(np.percentile(kern_ms, 90)),
+        "kernel_ms": kern_avg, "kernel_ms_min": float(np.min(kern_ms)),
+        "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
+        "kernel_ms_three_launch_step": float(np.mean(kern3_ms)),
+        "kernel_ms_b2b_plain": kern_b2b, "kernel_bytes": kernel_bytes,
         "achieved": achieved, "kv_bytes": kv_bytes, "step_bytes": step_bytes,
         "tokens_per_s": B * T / (ms * 1e-3),
         "graph": graph,
@@ -739,7 +756,7 @@ def bench_prefill(tb, torch, args):
     q = torch.from_numpy(q_prefill(w)).cuda()
     out = torch.empty((1, n_q, Hq, 128), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
-    steps = args.prefill_steps or max(3, args.steps // 4)
+    steps = args.prefill_steps or min(10, max(3, args.steps // 4))
 
     def step(ev=None):
         tb.quantize_append(cache, k_new, v_new, n_past)
@@ -1093,7 +1110,8 @@ def main():
             "note": dec["graph"]["note"],
         },
         "roofline": {
-            "kernel": "decode_split_kernel",
+            "kernel": "decode_split_kernel (the decode step's launch: 64 streaming splits and "
+                      "the new-token wavefronts)",
             "bound": "hbm",
             "achieved": round(dec["achieved"], 1),
             "peak": HBM_PEAK_GBS,
@@ -1102,15 +1120,18 @@ def main():
             "frac_of_achievable": round(dec["achieved"] / den["stream_read_gbs"], 4),
             "achievable_peak": den["stream_read_gbs"],
             "traffic": measured_traffic(dec["P"]),
+            "kernel_bytes": dec["kernel_bytes"],
             "kernel_ms": round(dec["kernel_ms"], 5),
-            "kernel_ms_in_step": round(dec["kernel_ms_in_step"], 5),
-            "kernel_ms_in_step_min": round(dec["kernel_ms_in_step_min"], 5),
-            "kernel_ms_in_step_p90": round(dec["kernel_ms_in_step_p90"], 5),
-            "timing": "kernel_ms: K launches of the split kernel back to back between two "
-                      "HIP events on the stream they run on, right after the timed steps; "
-                      "kernel_ms_in_step: HIP events recorded by the split kernel's own "
-                      "dispatch (hipExtLaunchKernel) on every step of a second loop of the "
-                      "same K steps (their markers add a few microseconds per call)",
+            "kernel_ms_min": round(dec["kernel_ms_min"], 5),
+            "kernel_ms_p90": round(dec["kernel_ms_p90"], 5),
+            "kernel_ms_three_launch_step": round(dec["kernel_ms_three_launch_step"], 5),
+            "kernel_ms_b2b_plain": round(dec["kernel_ms_b2b_plain"], 5),
+            "timing": "kernel_ms: mean of the HIP events that the split kernel's own dispatch "
+                      "(hipExtLaunchKernel) records in each of K decode steps run right after "
+                      "the timed ones; achieved = kernel_bytes / kernel_ms. "
+                      "kernel_ms_three_launch_step: the same for the plain split kernel inside "
+                      "K three-launch steps; kernel_ms_b2b_plain: K plain split kernels back to "
+                      "back between two events, no gaps (the hottest case for the clocks)",
         },
         "cpu_baseline": cpu,
         "contexts": ctx,

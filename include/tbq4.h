@@ -385,6 +385,17 @@ tbq4_status tbq4_decode_step(const tbq4_cache *cache, const void *k_new, const v
                              float softmax_scale, void *out, tbq4_dtype out_dtype,
                              int32_t n_splits, void *workspace, size_t workspace_bytes,
                              void *hip_stream);
+/* tbq4_decode_step_timed: tbq4_decode_step plus two optional HIP events
+ * (hipEvent_t, created by the caller with timing enabled; either may be
+ * NULL) that the split kernel's own dispatch records at its start and end,
+ * as tbq4_attn_decode_partial_timed does: the duration of the step's main
+ * kernel without a profiler. */
+tbq4_status tbq4_decode_step_timed(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                                   tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
+                                   const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                                   float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                   int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream, void *start_event, void *stop_event);
 
 /* Prefill-chunk attention: n_q new queries per sequence; query i sits at
  * absolute position n_past + i and attends slots [0, n_past + i] (causal

@@ -261,13 +261,15 @@ def decode_step_workspace_bytes(batch, n_kv_heads, n_q_heads, n_ctx, n_splits=0)
 
 
 def decode_step(cache, k_new, v_new, q, pos, softmax_scale, positions=None, n_splits=0, out=None,
-                out_dtype=torch.float16, workspace=None):
+                out_dtype=torch.float16, workspace=None, events=None):
     """Append one token per sequence (k_new, v_new: [batch][1][n_kv_heads][128])
     and attend over the cache that holds it, in one decode launch and the
     merge.  positions=None: every sequence writes slot pos and attends
     [0, pos]; else positions is a device int32 tensor [batch] read when the
     kernel runs (sequence b writes slot positions[b] and attends
-    [0, positions[b]]) and pos bounds them.  Returns out [batch][n_q_heads][128]."""
+    [0, positions[b]]) and pos bounds them.  events: optional (start, stop)
+    hipEvent_t handles that the split kernel's dispatch records.  Returns out
+    [batch][n_q_heads][128]."""
     _require(q, "q")
     _require(k_new, "k_new")
     _require(v_new, "v_new", k_new.shape)
@@ -287,12 +289,16 @@ def decode_step(cache, k_new, v_new, q, pos, softmax_scale, positions=None, n_sp
         need = decode_step_workspace_bytes(cache.batch, cache.n_kv_heads, Hq, pos + 1, n_splits)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     d = cache.descriptor()
-    _check(_lib.lib().tbq4_decode_step(
-        ctypes.byref(d), _ptr(k_new), _ptr(v_new), _dtype(k_new), pos,
-        _ptr(positions) if positions is not None else None, _ptr(q), _dtype(q), Hq,
-        float(softmax_scale), _ptr(out), _dtype(out), n_splits, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(q.device)),
-        "tbq4_decode_step")
+    args = (ctypes.byref(d), _ptr(k_new), _ptr(v_new), _dtype(k_new), pos,
+            _ptr(positions) if positions is not None else None, _ptr(q), _dtype(q), Hq,
+            float(softmax_scale), _ptr(out), _dtype(out), n_splits, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    if events is None:
+        _check(_lib.lib().tbq4_decode_step(*args), "tbq4_decode_step")
+    else:
+        _check(_lib.lib().tbq4_decode_step_timed(*args, ctypes.c_void_p(events[0]),
+                                                 ctypes.c_void_p(events[1])),
+               "tbq4_decode_step_timed")
     return out
 
 

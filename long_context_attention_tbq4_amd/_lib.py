@@ -25,7 +25,7 @@ EXPORTS = (
     "tbq4_verify_workspace_bytes", "tbq4_attn_verify", "tbq4_format_row_bytes",
     "tbq4_mixed_append", "tbq4_mixed_attn_decode", "tbq4_mixed_attn_prefill_chunk",
     "tbq4_mixed_attn_verify", "tbq4_attn_decode_noalloc",
-    "tbq4_decode_step_workspace_bytes", "tbq4_decode_step",
+    "tbq4_decode_step_workspace_bytes", "tbq4_decode_step", "tbq4_decode_step_timed",
     "tbq4_status_str", "tbq4_version",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -108,6 +108,9 @@ def lib():
     L.tbq4_decode_step.argtypes = [pc, vp, vp, i32, i32, vp, vp, i32, i32, f32, vp, i32, i32, vp,
                                    sz, vp]
     L.tbq4_decode_step.restype = i32
+    L.tbq4_decode_step_timed.argtypes = [pc, vp, vp, i32, i32, vp, vp, i32, i32, f32, vp, i32,
+                                         i32, vp, sz, vp, vp, vp]
+    L.tbq4_decode_step_timed.restype = i32
     L.tbq4_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.tbq4_verify_workspace_bytes.restype = sz
     L.tbq4_attn_verify.argtypes = [pc, vp, i32, i32, i32, i32, f32, vp, i32, i32, vp, sz, vp]

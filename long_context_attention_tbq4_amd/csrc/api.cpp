@@ -565,12 +565,12 @@ size_t tbq4_decode_step_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32
   return round256((size_t)batch * n_q_heads * (p + 1) * 130 * sizeof(float));
 }
 
-tbq4_status tbq4_decode_step(const tbq4_cache *cache, const void *k_new, const void *v_new,
-                             tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
-                             const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
-                             float softmax_scale, void *out, tbq4_dtype out_dtype,
-                             int32_t n_splits, void *workspace, size_t workspace_bytes,
-                             void *hip_stream) {
+static tbq4_status decode_step(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                               tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
+                               const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                               float softmax_scale, void *out, tbq4_dtype out_dtype,
+                               int32_t n_splits, void *workspace, size_t workspace_bytes,
+                               void *hip_stream, void *start_event, void *stop_event) {
   if (!out || !k_new || !v_new) return TBQ4_ERR_INVALID_ARG;
   if (out_dtype != TBQ4_F32 && out_dtype != TBQ4_F16) return TBQ4_ERR_INVALID_ARG;
   if (!valid_dtype(src_dtype)) return TBQ4_ERR_INVALID_ARG;
@@ -600,9 +600,32 @@ tbq4_status tbq4_decode_step(const tbq4_cache *cache, const void *k_new, const v
   a.k_new = k_new;
   a.v_new = v_new;
   hipStream_t st = (hipStream_t)hip_stream;
-  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st));
+  s = from_hip(tbq4::launch_decode_partial(a, cache->batch, (int)q_dtype, st,
+                                           (hipEvent_t)start_event, (hipEvent_t)stop_event));
   if (s != TBQ4_OK) return s;
   return from_hip(tbq4::launch_decode_merge(a, cache->batch, (int)out_dtype, st));
+}
+
+tbq4_status tbq4_decode_step(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                             tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
+                             const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                             float softmax_scale, void *out, tbq4_dtype out_dtype,
+                             int32_t n_splits, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  return decode_step(cache, k_new, v_new, src_dtype, pos, positions, q, q_dtype, n_q_heads,
+                     softmax_scale, out, out_dtype, n_splits, workspace, workspace_bytes,
+                     hip_stream, nullptr, nullptr);
+}
+
+tbq4_status tbq4_decode_step_timed(const tbq4_cache *cache, const void *k_new, const void *v_new,
+                                   tbq4_dtype src_dtype, int32_t pos, const int32_t *positions,
+                                   const void *q, tbq4_dtype q_dtype, int32_t n_q_heads,
+                                   float softmax_scale, void *out, tbq4_dtype out_dtype,
+                                   int32_t n_splits, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream, void *start_event, void *stop_event) {
+  return decode_step(cache, k_new, v_new, src_dtype, pos, positions, q, q_dtype, n_q_heads,
+                     softmax_scale, out, out_dtype, n_splits, workspace, workspace_bytes,
+                     hip_stream, start_event, stop_event);
 }
 
 // Prefill on K / V tensors in the given formats (TBQ4, fp16, TBQ3 or q8_0);

@@ -214,6 +214,13 @@ def test_decode_step_argument_errors(L):
     assert step(kn=FAKE + 4) == _lib.ERR_ALIGNMENT
     assert step(out=FAKE + 8) == _lib.ERR_ALIGNMENT
     assert step(cache=_cache(cap=60)) == _lib.ERR_ALIGNMENT
+    # the timed variant makes the same checks before anything is launched
+    assert L.tbq4_decode_step_timed(ctypes.byref(c), FAKE, FAKE, 0, 64, None, FAKE, 0, 8, 1.0,
+                                    FAKE, 1, 4, FAKE, need, None, None,
+                                    None) == _lib.ERR_CAPACITY
+    assert L.tbq4_decode_step_timed(ctypes.byref(c), FAKE, FAKE, 0, 10, None, FAKE, 0, 8, 1.0,
+                                    None, 1, 4, FAKE, need, None, None,
+                                    None) == _lib.ERR_INVALID_ARG
 
 
 def test_verify_argument_errors(L):

@@ -54,7 +54,7 @@ def test_defaults_settle_and_switches(monkeypatch):
     bench = _bench_module()
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = bench.parse()
-    assert (a.gpus, a.steps, a.warmup, a.splits) == (1, 20, 5, 0)
+    assert (a.gpus, a.steps, a.warmup, a.splits) == (1, 200, 20, 0)
     assert a.settle == bench.SETTLE_STEPS >= 600   # timed steps start after the clock dip
     monkeypatch.setattr(sys, "argv", ["bench.py", "--settle", "60", "--no-contexts", "--no-prefill"])
     a = bench.parse()

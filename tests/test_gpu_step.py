@@ -204,3 +204,33 @@ def test_step_graph_replays():
                 assert np.array_equal(kc[b, h, p], o.quantize_blocks(hist_k[b, p, h][None], seed)[0][0])
                 ref = _ref(qn[b, h * G:(h + 1) * G], kc[b, h], vc[b, h], p + 1, 0.1, seed)
                 check_attn(got[b, h * G:(h + 1) * G], ref, False, f"replay {t} b={b} h={h}")
+
+
+def test_step_timed_matches_and_records_events():
+    """tbq4_decode_step_timed: the same output as the untimed call, and the
+    two events its split-kernel dispatch records span a positive time."""
+    import ctypes
+    rt = ctypes.CDLL("libamdhip64.so.7")
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+    rng = np.random.default_rng(46)
+    B, H, G, cap, pos = 2, 2, 4, 4096, 3000
+    cache = _prefix_cache(rng, B, H, cap, pos, 1)
+    kn = torch.from_numpy(rng.standard_normal((B, 1, H, 128)).astype(np.float32)).cuda()
+    vn = torch.from_numpy(rng.standard_normal((B, 1, H, 128)).astype(np.float32)).cuda()
+    q = torch.from_numpy(rng.standard_normal((B, H * G, 128)).astype(np.float32)).cuda()
+    a = tb.decode_step(cache, kn, vn, q, pos, 0.1, out_dtype=torch.float32)
+    b = tb.decode_step(cache, kn, vn, q, pos, 0.1, out_dtype=torch.float32,
+                       events=(ev[0].value, ev[1].value))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ms = ctypes.c_float()
+    assert rt.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    assert 0.0 < ms.value < 1000.0
+    for e in ev:
+        rt.hipEventDestroy(e)
