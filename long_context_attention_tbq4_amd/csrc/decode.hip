@@ -94,6 +94,49 @@ template <int H> __device__ __forceinline__ float lane_xor_f32(float x, int lane
   return __uint_as_float(lane_xor<H>(__float_as_uint(x), lane));
 }
 
+// One butterfly level across lanes H apart (16: adjacent 16-lane rows, 32:
+// the two halves) for two registers at once: lanes with bit H clear take
+// x + x', the others x' - x (x' the partner lane's value).  The first swap
+// puts a and its partner side by side in the rows (halves) of a with bit H
+// clear and b and its partner in the others, so one add and one subtract
+// form every result, and the second swap puts them back in place.
+template <int H> __device__ __forceinline__ void butterfly_pair(float &a, float &b) {
+  static_assert(H == 16 || H == 32, "butterfly_pair: rows or halves");
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const auto r = H == 16 ? __builtin_amdgcn_permlane16_swap(ua, ub, false, false)
+                         : __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+  const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+  const float s = x + y, d = x - y;
+  const auto t = H == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(d), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(d), false, false);
+  a = __uint_as_float(t[0]);
+  b = __uint_as_float(t[1]);
+}
+
+// Eight consecutive query elements from a 16-byte aligned address, as fp32.
+template <typename QT> __device__ __forceinline__ void load_q8(const QT *p, float *x);
+template <> __device__ __forceinline__ void load_q8<float>(const float *p, float *x) {
+  const float4v a = *(const float4v *)p, b = *(const float4v *)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+template <> __device__ __forceinline__ void load_q8<_Float16>(const _Float16 *p, float *x) {
+  const half8 h = *(const half8 *)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+}
+template <> __device__ __forceinline__ void load_q8<uint16_t>(const uint16_t *p, float *x) {
+  const u32x4 w = *(const u32x4 *)p;   // bf16 pairs: the upper halves of fp32s
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 // The new token of a decode step, two wavefronts per (sequence b, KV head g),
 // which each quantise one of its head vectors with the append kernel's
 // arithmetic (identical bytes) and store it at the token's slot, and between
@@ -263,70 +306,104 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 
   // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
-  // fp16 K cache), split into fp16 hi + residual
-  float qv[32];
+  // fp16 or q8_0 K cache), split into an fp16 high part and residual.  Lane
+  // quarter q holds the quarter's 32 elements i of each head: dims 32 q + i,
+  // or for a q8_0 K cache 32 (i/8) + 8 q + i%8, so that MFMA step c spans
+  // q8_0 block c.  Lanes col and col + 8 carry the same head (the high part
+  // and the residual of its operand), so they share the work: lane part p =
+  // col / 8 rotates and splits elements 16 p .. 16 p + 15, and the two trade
+  // the fp16 words each needs from the other at the end.
+  half8 qop[4];
+  float qs_inv;
   {
-    // lane quarter q holds dims 32 q + i; for a q8_0 K cache dims
-    // 32 (i/8) + 8 q + i%8 instead, so that MFMA step c spans q8_0 block c
-    const QT *qp = (const QT *)a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + head) * kHeadDim;
-    const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int d = KF == kFmtQ8 ? 32 * (i >> 3) + 8 * quarter + (i & 7) : 32 * quarter + i;
-      float x = head < G ? load_q<QT>(qp + d) : 0.0f;
-      qv[i] = ((sw >> i) & 1u) ? -x : x;
+    const int part = lo_part ? 1 : 0;
+    const bool live = head < G;
+    // a lane past the group reads head 0's row (in bounds) and is zeroed below
+    const QT *qp = (const QT *)a.q +
+                   ((size_t)b * a.n_q_heads + (size_t)g * G + (live ? head : 0)) * kHeadDim;
+    float qv[16];
+    if constexpr (KF == kFmtQ8) {
+      load_q8<QT>(qp + 64 * part + 8 * quarter, qv);
+      load_q8<QT>(qp + 64 * part + 32 + 8 * quarter, qv + 8);
+    } else {
+      load_q8<QT>(qp + 32 * quarter + 16 * part, qv);
+      load_q8<QT>(qp + 32 * quarter + 16 * part + 8, qv + 8);
     }
     if constexpr (kKRot) {
+      // signs, then the 128-point butterflies: elements 1..8 apart in
+      // registers, 16 apart between the two parts (lanes 8 apart), 32 and 64
+      // apart across quarters (lanes 16 and 32 apart)
+      const uint32_t sw = a.sign[quarter] >> (16 * part);
 #pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
+      for (int j = 0; j < 16; ++j) qv[j] = ((sw >> j) & 1u) ? -qv[j] : qv[j];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if ((i & h) == 0) {
-          const float x = qv[i], y = qv[i + h];
-          qv[i] = x + y;
-          qv[i + h] = x - y;
+      for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if ((j & h) == 0) {
+            const float x = qv[j], y = qv[j + h];
+            qv[j] = x + y;
+            qv[j + h] = x - y;
+          }
         }
       }
+      const float sg = part ? -1.0f : 1.0f;   // part 0: v + v', part 1: v' - v
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qv[j] = fmaf(sg, qv[j], lane_xor_f32<8>(qv[j], lane));
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) butterfly_pair<16>(qv[j], qv[j + 1]);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) butterfly_pair<32>(qv[j], qv[j + 1]);
     }
+    // one power-of-two normalisation for the whole group: max |q'| in
+    // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
+    // range, and 2^-ex folds into the per-token key scale.  (The maximum of
+    // |v| f is the maximum of |v| times f, rounded: rounding is monotonic.)
+    const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
+    float mx = 0.0f;
 #pragma unroll
-    for (int h = 16; h <= 32; h <<= 1) {   // dims 32 and 64 apart: lanes 16 / 32 apart
-      const bool upper = (lane & h) != 0;
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(qv[j]));
+    mx = fmaxf(mx, lane_xor_f32<1>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<2>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<4>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<8>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<16>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<32>(mx, lane));
+    mx *= fabsf(f);
+    int ex = 0;
+    if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
+    ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+    qs_inv = ldexpf(1.0f, -ex);
+    const float fs = live ? ldexpf(f, ex) : 0.0f;   // f 2^ex: exact
+    // operand word k of block c holds elements (8c + e0, 8c + e0 + d): TBQ4 K
+    // operands hold the 4 even then the 4 odd dims of a code word (pairs 0 2,
+    // 4 6, 1 3, 5 7), the other formats 8 consecutive dims
+    uint32_t hw[2][4], lw[2][4];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float o = __shfl_xor(qv[i], h, 64);
-        qv[i] = upper ? (o - qv[i]) : (qv[i] + o);
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e0 = KF == kFmtTbq4 ? (k < 2 ? 4 * k : 4 * (k - 2) + 1) : 2 * k;
+        const int e1 = KF == kFmtTbq4 ? e0 + 2 : e0 + 1;
+        const float x0 = qv[8 * cc + e0] * fs, x1 = qv[8 * cc + e1] * fs;
+        hw[cc][k] = pk_f16(x0, x1);
+        lw[cc][k] = pk_f16_residual(hw[cc][k], x0, x1);
       }
     }
-    }
-  }
-  const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
-  float mx = 0.0f;
+    // part 0 (high part) takes its own high words for blocks 0-1 and the
+    // partner's for blocks 2-3; part 1 (residual) the partner's residual
+    // words for blocks 0-1 and its own for 2-3
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    qv[i] *= f;
-    mx = fmaxf(mx, fabsf(qv[i]));
-  }
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4 w0, w1;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  // one power-of-two normalisation for the whole group: max |q'| in
-  // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
-  // range, and 2^-ex folds into the per-token key scale
-  int ex = 0;
-  if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
-  ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
-  const float qs_inv = ldexpf(1.0f, -ex);
-  half8 qop[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int el = 0; el < 8; ++el) {
-      // TBQ4 K operands hold the 4 even then the 4 odd dims of a code word;
-      // fp16, TBQ3 and q8_0 K operands hold 8 consecutive dims
-      const int i = KF == kFmtTbq4 ? 8 * c + (el < 4 ? 2 * el : 2 * el - 7) : 8 * c + el;
-      const float x = ldexpf(qv[i], ex);
-      const _Float16 hi = (_Float16)x;
-      const _Float16 lo = (_Float16)(x - (float)hi);
-      qop[c][el] = lo_part ? lo : hi;
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t rh = lane_xor<8>(hw[cc][k], lane), rl = lane_xor<8>(lw[cc][k], lane);
+        w0[k] = part ? rl : hw[cc][k];
+        w1[k] = part ? lw[cc][k] : rh;
+      }
+      qop[cc] = __builtin_bit_cast(half8, w0);
+      qop[2 + cc] = __builtin_bit_cast(half8, w1);
     }
   }
 
@@ -791,13 +868,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   for (; t < t_end; ++t) process(r, t, std::true_type{});
 
   // ---------------- partial state of this split
-  l_run += __shfl_xor(l_run, 8, 64);
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[i][e] += __shfl_xor(o[i][e], 32, 64);
+  l_run += lane_xor_f32<8>(l_run, lane);
+  l_run += lane_xor_f32<16>(l_run, lane);
+  l_run += lane_xor_f32<32>(l_run, lane);
 
   const int P = a.n_splits;
   float *wsb = a.ws + ((size_t)b * a.n_q_heads + (size_t)g * G) * P * 130 + (size_t)split * 130;
@@ -805,22 +878,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     wsb[(size_t)lane * P * 130 + 0] = m_run;
     wsb[(size_t)lane * P * 130 + 1] = l_run;
   }
-  if (lane < 32) {
+  // O'^T rows h and h + 8 (lanes l and l + 32) add up to head h's output.
+  // Accumulators pair up (o[2k], o[2k+1]): one swap of the halves leaves
+  // each lane of the lower half a value of o[2k] and its partner, and each
+  // lane of the upper half a value of o[2k+1] and its partner, so one add
+  // forms both registers' sums and all 64 lanes store: lanes 0-31 the dims
+  // of o[2k], lanes 32-63 those of o[2k+1], for heads 4 (quarter % 2) + e.
+  const int hsel = quarter >> 1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * quarter + e;   // query head within the group
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[2 * k][e]),
+                                                       __float_as_uint(o[2 * k + 1][e]), false, false);
+      const float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int r = 4 * (quarter & 1) + e;   // query head within the group
       if (r < G) {
-        float *dst = wsb + (size_t)r * P * 130 + 2;
-        if constexpr (VF == kFmtTbq4) {
-#pragma unroll
-          for (int cg = 0; cg < 4; ++cg) {
-            dst[32 * cg + 2 * col] = o[2 * cg][e];
-            dst[32 * cg + 2 * col + 1] = o[2 * cg + 1][e];
-          }
-        } else {
-#pragma unroll
-          for (int db = 0; db < 8; ++db) dst[16 * db + col] = o[db][e];
-        }
+        // TBQ4 V: o[2k] holds dims 32 k + 2 col, o[2k+1] the odd dims after
+        // them; the other formats: o[db] holds dims 16 db + col
+        const int d = VF == kFmtTbq4 ? 32 * k + 2 * col + hsel : 16 * (2 * k + hsel) + col;
+        wsb[(size_t)r * P * 130 + 2 + d] = s;
       }
     }
   }
