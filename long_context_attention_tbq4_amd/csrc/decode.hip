@@ -88,55 +88,6 @@ __device__ __forceinline__ LaneCodes quantize_any(const void *row, int dtype, ui
                               w_b, lane);
 }
 
-// x of lane (lane ^ H) for an fp32 value (the quantiser's DPP / permlane
-// exchanges)
-template <int H> __device__ __forceinline__ float lane_xor_f32(float x, int lane) {
-  return __uint_as_float(lane_xor<H>(__float_as_uint(x), lane));
-}
-
-// One butterfly level across lanes H apart (16: adjacent 16-lane rows, 32:
-// the two halves) for two registers at once: lanes with bit H clear take
-// x + x', the others x' - x (x' the partner lane's value).  The first swap
-// puts a and its partner side by side in the rows (halves) of a with bit H
-// clear and b and its partner in the others, so one add and one subtract
-// form every result, and the second swap puts them back in place.
-template <int H> __device__ __forceinline__ void butterfly_pair(float &a, float &b) {
-  static_assert(H == 16 || H == 32, "butterfly_pair: rows or halves");
-  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-  const auto r = H == 16 ? __builtin_amdgcn_permlane16_swap(ua, ub, false, false)
-                         : __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
-  const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
-  const float s = x + y, d = x - y;
-  const auto t = H == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(d), false, false)
-                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(d), false, false);
-  a = __uint_as_float(t[0]);
-  b = __uint_as_float(t[1]);
-}
-
-// Eight consecutive query elements from a 16-byte aligned address, as fp32.
-template <typename QT> __device__ __forceinline__ void load_q8(const QT *p, float *x);
-template <> __device__ __forceinline__ void load_q8<float>(const float *p, float *x) {
-  const float4v a = *(const float4v *)p, b = *(const float4v *)(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
-}
-template <> __device__ __forceinline__ void load_q8<_Float16>(const _Float16 *p, float *x) {
-  const half8 h = *(const half8 *)p;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
-}
-template <> __device__ __forceinline__ void load_q8<uint16_t>(const uint16_t *p, float *x) {
-  const u32x4 w = *(const u32x4 *)p;   // bf16 pairs: the upper halves of fp32s
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-
 // The new token of a decode step, two wavefronts per (sequence b, KV head g),
 // which each quantise one of its head vectors with the append kernel's
 // arithmetic (identical bytes) and store it at the token's slot, and between
@@ -305,108 +256,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (lane < 32) svq[4 * kTile + lane] = 0.0f;
   }
 
-  // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
-  // fp16 or q8_0 K cache), split into an fp16 high part and residual.  Lane
-  // quarter q holds the quarter's 32 elements i of each head: dims 32 q + i,
-  // or for a q8_0 K cache 32 (i/8) + 8 q + i%8, so that MFMA step c spans
-  // q8_0 block c.  Lanes col and col + 8 carry the same head (the high part
-  // and the residual of its operand), so they share the work: lane part p =
-  // col / 8 rotates and splits elements 16 p .. 16 p + 15, and the two trade
-  // the fp16 words each needs from the other at the end.
-  half8 qop[4];
-  float qs_inv;
-  {
-    const int part = lo_part ? 1 : 0;
-    const bool live = head < G;
-    // a lane past the group reads head 0's row (in bounds) and is zeroed below
-    const QT *qp = (const QT *)a.q +
-                   ((size_t)b * a.n_q_heads + (size_t)g * G + (live ? head : 0)) * kHeadDim;
-    float qv[16];
-    if constexpr (KF == kFmtQ8) {
-      load_q8<QT>(qp + 64 * part + 8 * quarter, qv);
-      load_q8<QT>(qp + 64 * part + 32 + 8 * quarter, qv + 8);
-    } else {
-      load_q8<QT>(qp + 32 * quarter + 16 * part, qv);
-      load_q8<QT>(qp + 32 * quarter + 16 * part + 8, qv + 8);
-    }
-    if constexpr (kKRot) {
-      // signs, then the 128-point butterflies: elements 1..8 apart in
-      // registers, 16 apart between the two parts (lanes 8 apart), 32 and 64
-      // apart across quarters (lanes 16 and 32 apart)
-      const uint32_t sw = a.sign[quarter] >> (16 * part);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) qv[j] = ((sw >> j) & 1u) ? -qv[j] : qv[j];
-#pragma unroll
-      for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if ((j & h) == 0) {
-            const float x = qv[j], y = qv[j + h];
-            qv[j] = x + y;
-            qv[j + h] = x - y;
-          }
-        }
-      }
-      const float sg = part ? -1.0f : 1.0f;   // part 0: v + v', part 1: v' - v
-#pragma unroll
-      for (int j = 0; j < 16; ++j) qv[j] = fmaf(sg, qv[j], lane_xor_f32<8>(qv[j], lane));
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) butterfly_pair<16>(qv[j], qv[j + 1]);
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) butterfly_pair<32>(qv[j], qv[j + 1]);
-    }
-    // one power-of-two normalisation for the whole group: max |q'| in
-    // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
-    // range, and 2^-ex folds into the per-token key scale.  (The maximum of
-    // |v| f is the maximum of |v| times f, rounded: rounding is monotonic.)
-    const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
-    float mx = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(qv[j]));
-    mx = fmaxf(mx, lane_xor_f32<1>(mx, lane));
-    mx = fmaxf(mx, lane_xor_f32<2>(mx, lane));
-    mx = fmaxf(mx, lane_xor_f32<4>(mx, lane));
-    mx = fmaxf(mx, lane_xor_f32<8>(mx, lane));
-    mx = fmaxf(mx, lane_xor_f32<16>(mx, lane));
-    mx = fmaxf(mx, lane_xor_f32<32>(mx, lane));
-    mx *= fabsf(f);
-    int ex = 0;
-    if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
-    ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
-    qs_inv = ldexpf(1.0f, -ex);
-    const float fs = live ? ldexpf(f, ex) : 0.0f;   // f 2^ex: exact
-    // operand word k of block c holds elements (8c + e0, 8c + e0 + d): TBQ4 K
-    // operands hold the 4 even then the 4 odd dims of a code word (pairs 0 2,
-    // 4 6, 1 3, 5 7), the other formats 8 consecutive dims
-    uint32_t hw[2][4], lw[2][4];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e0 = KF == kFmtTbq4 ? (k < 2 ? 4 * k : 4 * (k - 2) + 1) : 2 * k;
-        const int e1 = KF == kFmtTbq4 ? e0 + 2 : e0 + 1;
-        const float x0 = qv[8 * cc + e0] * fs, x1 = qv[8 * cc + e1] * fs;
-        hw[cc][k] = pk_f16(x0, x1);
-        lw[cc][k] = pk_f16_residual(hw[cc][k], x0, x1);
-      }
-    }
-    // part 0 (high part) takes its own high words for blocks 0-1 and the
-    // partner's for blocks 2-3; part 1 (residual) the partner's residual
-    // words for blocks 0-1 and its own for 2-3
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      u32x4 w0, w1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t rh = lane_xor<8>(hw[cc][k], lane), rl = lane_xor<8>(lw[cc][k], lane);
-        w0[k] = part ? rl : hw[cc][k];
-        w1[k] = part ? lw[cc][k] : rh;
-      }
-      qop[cc] = __builtin_bit_cast(half8, w0);
-      qop[2 + cc] = __builtin_bit_cast(half8, w1);
-    }
-  }
-
   // ---------------- token range of this split: this sequence's length (from
   // device memory when given) in 32-token tiles, spread evenly over the splits
   // (a decode step: the slots before the new token's, none when its slot is
@@ -543,6 +392,112 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       r.skq[1] = buf_load_u16(rk, so + 34);
     }
   };
+
+  // the first tile's fetch is in flight while q' is formed
+  Raw r;
+  fetch(r, t_begin);
+
+  // ---------------- q' = R q * scale * log2(e) (q * scale * log2(e) for an
+  // fp16 or q8_0 K cache), split into an fp16 high part and residual.  Lane
+  // quarter q holds the quarter's 32 elements i of each head: dims 32 q + i,
+  // or for a q8_0 K cache 32 (i/8) + 8 q + i%8, so that MFMA step c spans
+  // q8_0 block c.  Lanes col and col + 8 carry the same head (the high part
+  // and the residual of its operand), so they share the work: lane part p =
+  // col / 8 rotates and splits elements 16 p .. 16 p + 15, and the two trade
+  // the fp16 words each needs from the other at the end.
+  half8 qop[4];
+  float qs_inv;
+  {
+    const int part = lo_part ? 1 : 0;
+    const bool live = head < G;
+    // a lane past the group reads head 0's row (in bounds) and is zeroed below
+    const QT *qp = (const QT *)a.q +
+                   ((size_t)b * a.n_q_heads + (size_t)g * G + (live ? head : 0)) * kHeadDim;
+    float qv[16];
+    if constexpr (KF == kFmtQ8) {
+      load_q8<QT>(qp + 64 * part + 8 * quarter, qv);
+      load_q8<QT>(qp + 64 * part + 32 + 8 * quarter, qv + 8);
+    } else {
+      load_q8<QT>(qp + 32 * quarter + 16 * part, qv);
+      load_q8<QT>(qp + 32 * quarter + 16 * part + 8, qv + 8);
+    }
+    if constexpr (kKRot) {
+      // signs, then the 128-point butterflies: elements 1..8 apart in
+      // registers, 16 apart between the two parts (lanes 8 apart), 32 and 64
+      // apart across quarters (lanes 16 and 32 apart)
+      const uint32_t sw = a.sign[quarter] >> (16 * part);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qv[j] = ((sw >> j) & 1u) ? -qv[j] : qv[j];
+#pragma unroll
+      for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if ((j & h) == 0) {
+            const float x = qv[j], y = qv[j + h];
+            qv[j] = x + y;
+            qv[j + h] = x - y;
+          }
+        }
+      }
+      const float sg = part ? -1.0f : 1.0f;   // part 0: v + v', part 1: v' - v
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qv[j] = fmaf(sg, qv[j], lane_xor_f32<8>(qv[j], lane));
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) butterfly_pair<16>(qv[j], qv[j + 1]);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) butterfly_pair<32>(qv[j], qv[j + 1]);
+    }
+    // one power-of-two normalisation for the whole group: max |q'| in
+    // [2^13, 2^14) keeps the fp16 high part and residual inside the fp16
+    // range, and 2^-ex folds into the per-token key scale.  (The maximum of
+    // |v| f is the maximum of |v| times f, rounded: rounding is monotonic.)
+    const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(qv[j]));
+    mx = fmaxf(mx, lane_xor_f32<1>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<2>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<4>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<8>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<16>(mx, lane));
+    mx = fmaxf(mx, lane_xor_f32<32>(mx, lane));
+    mx *= fabsf(f);
+    int ex = 0;
+    if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
+    ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+    qs_inv = ldexpf(1.0f, -ex);
+    const float fs = live ? ldexpf(f, ex) : 0.0f;   // f 2^ex: exact
+    // operand word k of block c holds elements (8c + e0, 8c + e0 + d): TBQ4 K
+    // operands hold the 4 even then the 4 odd dims of a code word (pairs 0 2,
+    // 4 6, 1 3, 5 7), the other formats 8 consecutive dims
+    uint32_t hw[2][4], lw[2][4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e0 = KF == kFmtTbq4 ? (k < 2 ? 4 * k : 4 * (k - 2) + 1) : 2 * k;
+        const int e1 = KF == kFmtTbq4 ? e0 + 2 : e0 + 1;
+        const float x0 = qv[8 * cc + e0] * fs, x1 = qv[8 * cc + e1] * fs;
+        hw[cc][k] = pk_f16(x0, x1);
+        lw[cc][k] = pk_f16_residual(hw[cc][k], x0, x1);
+      }
+    }
+    // part 0 (high part) takes its own high words for blocks 0-1 and the
+    // partner's for blocks 2-3; part 1 (residual) the partner's residual
+    // words for blocks 0-1 and its own for 2-3
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4 w0, w1;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t rh = lane_xor<8>(hw[cc][k], lane), rl = lane_xor<8>(lw[cc][k], lane);
+        w0[k] = part ? rl : hw[cc][k];
+        w1[k] = part ? lw[cc][k] : rh;
+      }
+      qop[cc] = __builtin_bit_cast(half8, w0);
+      qop[2 + cc] = __builtin_bit_cast(half8, w1);
+    }
+  }
 
   // kPartial: the tile may hold slots >= n_ctx (only the last tile of the
   // context); full tiles carry no masking code at all
@@ -860,8 +815,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  Raw r;
-  fetch(r, t_begin);
   const int t_full = min(t_end, n_ctx / kTile);   // tiles below t_full are full
   int t = t_begin;
   for (; t < t_full; ++t) process(r, t, std::false_type{});
@@ -988,14 +941,21 @@ __global__ __launch_bounds__(64 * NW) void decode_merge_kernel(DecodeArgs a) {
     dst[lane + 64] = (OT)o1;
     return;
   }
-  // o = s * (H o') / sqrt(128)
-#pragma unroll
-  for (int hh = 1; hh < 64; hh <<= 1) {
-    const float p0 = __shfl_xor(o0, hh, 64), p1 = __shfl_xor(o1, hh, 64);
+  // o = s * (H o') / sqrt(128); the butterflies across lanes use DPP and
+  // permlane exchanges (no LDS round trip on this serial chain)
+  auto level = [&](auto hc) {
+    constexpr int hh = decltype(hc)::value;
+    const float p0 = lane_xor_f32<hh>(o0, lane), p1 = lane_xor_f32<hh>(o1, lane);
     const bool upper = (lane & hh) != 0;
     o0 = upper ? (p0 - o0) : (o0 + p0);
     o1 = upper ? (p1 - o1) : (o1 + p1);
-  }
+  };
+  level(std::integral_constant<int, 1>{});
+  level(std::integral_constant<int, 2>{});
+  level(std::integral_constant<int, 4>{});
+  level(std::integral_constant<int, 8>{});
+  level(std::integral_constant<int, 16>{});
+  level(std::integral_constant<int, 32>{});
   {
     const float x = o0, y = o1;
     o0 = x + y;

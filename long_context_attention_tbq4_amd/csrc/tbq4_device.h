@@ -253,4 +253,77 @@ template <> __device__ __forceinline__ float load_q<uint16_t>(const uint16_t *p)
   return __uint_as_float((uint32_t)*p << 16);
 }
 
+// x of lane (lane ^ H), H in {1, 2, 4, 8, 16, 32}, without a round trip
+// through LDS: DPP quad permutations (1, 2), row shifts restricted to banks
+// (4: banks 0 and 2 read four lanes up, banks 1 and 3 four lanes down), a
+// row rotation (8), and gfx950's swaps of adjacent 16-lane rows and of the
+// two 32-lane halves (16, 32), whose two results hold the partner's value
+// for odd and even rows (halves) respectively.
+template <int H> __device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (H == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (H == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (H == 4) {
+    const int t = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x104, 0xF, 0x5, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x114, 0xF, 0xA, false);
+  } else if constexpr (H == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false);
+  } else if constexpr (H == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(H == 32, "lane_xor: H is a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+// x of lane (lane ^ H) for an fp32 value
+template <int H> __device__ __forceinline__ float lane_xor_f32(float x, int lane) {
+  return __uint_as_float(lane_xor<H>(__float_as_uint(x), lane));
+}
+
+// One butterfly level across lanes H apart (16: adjacent 16-lane rows, 32:
+// the two halves) for two registers at once: lanes with bit H clear take
+// x + x', the others x' - x (x' the partner lane's value).  The first swap
+// puts a and its partner side by side in the rows (halves) of a with bit H
+// clear and b and its partner in the others, so one add and one subtract
+// form every result, and the second swap puts them back in place.
+template <int H> __device__ __forceinline__ void butterfly_pair(float &a, float &b) {
+  static_assert(H == 16 || H == 32, "butterfly_pair: rows or halves");
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const auto r = H == 16 ? __builtin_amdgcn_permlane16_swap(ua, ub, false, false)
+                         : __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+  const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+  const float s = x + y, d = x - y;
+  const auto t = H == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(d), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(d), false, false);
+  a = __uint_as_float(t[0]);
+  b = __uint_as_float(t[1]);
+}
+
+// Eight consecutive query elements from a 16-byte aligned address, as fp32.
+template <typename QT> __device__ __forceinline__ void load_q8(const QT *p, float *x);
+template <> __device__ __forceinline__ void load_q8<float>(const float *p, float *x) {
+  const float4v a = *(const float4v *)p, b = *(const float4v *)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+template <> __device__ __forceinline__ void load_q8<_Float16>(const _Float16 *p, float *x) {
+  const half8 h = *(const half8 *)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+}
+template <> __device__ __forceinline__ void load_q8<uint16_t>(const uint16_t *p, float *x) {
+  const u32x4 w = *(const u32x4 *)p;   // bf16 pairs: the upper halves of fp32s
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 }  // namespace tbq4

@@ -66,31 +66,6 @@ __device__ __forceinline__ int half_round_sqrt(double ms) {
   return h;
 }
 
-// x of lane (lane ^ H), H in {1, 2, 4, 8, 16, 32}, without a round trip
-// through LDS: DPP quad permutations (1, 2), row shifts restricted to banks
-// (4: banks 0 and 2 read four lanes up, banks 1 and 3 four lanes down), a
-// row rotation (8), and gfx950's swaps of adjacent 16-lane rows and of the
-// two 32-lane halves (16, 32), whose two results hold the partner's value
-// for odd and even rows (halves) respectively.
-template <int H> __device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
-  if constexpr (H == 1) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false);
-  } else if constexpr (H == 2) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false);
-  } else if constexpr (H == 4) {
-    const int t = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x104, 0xF, 0x5, false);
-    return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x114, 0xF, 0xA, false);
-  } else if constexpr (H == 8) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x128, 0xF, 0xF, false);
-  } else if constexpr (H == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    static_assert(H == 32, "lane_xor: H is a power of two below 64");
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
 template <int H> __device__ __forceinline__ double lane_xor_f64(double v, int lane) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
   const uint64_t lo = lane_xor<H>((uint32_t)b, lane), hi = lane_xor<H>((uint32_t)(b >> 32), lane);

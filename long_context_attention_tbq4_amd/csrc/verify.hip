@@ -71,81 +71,83 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
 
   // ---------------- q' = R q * scale * log2(e) per (query, head) column
   float qv[CG][32];
+  bool live[CG];
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     const int qi = 2 * c + qsub;
-    const bool live = qi < a.n_q && head < G;
+    live[c] = qi < a.n_q && head < G;
     // lane quarter q holds dims 32 q + i; for a q8_0 K cache dims
-    // 32 (i/8) + 8 q + i%8 instead, so that MFMA step k spans q8_0 block k
+    // 32 (i/8) + 8 q + i%8 instead, so that MFMA step k spans q8_0 block k.
+    // A column past the drafted queries or the group reads query 0, head 0
+    // (in bounds) and is zeroed below.
     const QT *qp = (const QT *)a.q +
-                   (((size_t)b * a.n_q + (live ? qi : 0)) * a.n_q_heads + (size_t)g * G +
-                    (live ? head : 0)) * kHeadDim;
-    const uint32_t sw = kKRot ? a.sign[quarter] : 0u;
+                   (((size_t)b * a.n_q + (live[c] ? qi : 0)) * a.n_q_heads + (size_t)g * G +
+                    (live[c] ? head : 0)) * kHeadDim;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int d = KF == kFmtQ8 ? 32 * (i >> 3) + 8 * quarter + (i & 7) : 32 * quarter + i;
-      const float x = live ? load_q<QT>(qp + d) : 0.0f;
-      qv[c][i] = ((sw >> i) & 1u) ? -x : x;
-    }
+    for (int r = 0; r < 4; ++r)
+      load_q8<QT>(qp + (KF == kFmtQ8 ? 32 * r + 8 * quarter : 32 * quarter + 8 * r), &qv[c][8 * r]);
     if constexpr (kKRot) {
+      const uint32_t sw = a.sign[quarter];
 #pragma unroll
-    for (int h = 1; h < 32; h <<= 1)
+      for (int i = 0; i < 32; ++i) qv[c][i] = ((sw >> i) & 1u) ? -qv[c][i] : qv[c][i];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if ((i & h) == 0) {
-          const float x = qv[c][i], y = qv[c][i + h];
-          qv[c][i] = x + y;
-          qv[c][i + h] = x - y;
-        }
+      for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
-    for (int h = 16; h <= 32; h <<= 1) {
-      const bool upper = (lane & h) != 0;
+        for (int i = 0; i < 32; ++i)
+          if ((i & h) == 0) {
+            const float x = qv[c][i], y = qv[c][i + h];
+            qv[c][i] = x + y;
+            qv[c][i + h] = x - y;
+          }
+      // dims 32 and 64 apart: lanes 16 and 32 apart
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float o = __shfl_xor(qv[c][i], h, 64);
-        qv[c][i] = upper ? (o - qv[c][i]) : (qv[c][i] + o);
-      }
-    }
+      for (int i = 0; i < 32; i += 2) butterfly_pair<16>(qv[c][i], qv[c][i + 1]);
+#pragma unroll
+      for (int i = 0; i < 32; i += 2) butterfly_pair<32>(qv[c][i], qv[c][i + 1]);
     }
   }
+  // one power-of-two normalisation for all columns (the maximum of |v| f is
+  // the maximum of |v| times f, rounded: rounding is monotonic)
   const float f = (kKRot ? 0.08838834764831845f : 1.0f) * a.qscale;
   float mx = 0.0f;
 #pragma unroll
   for (int c = 0; c < CG; ++c)
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      qv[c][i] *= f;
-      mx = fmaxf(mx, fabsf(qv[c][i]));
-    }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(qv[c][i]));
+  mx = fmaxf(mx, lane_xor_f32<1>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f32<2>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f32<4>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f32<8>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f32<16>(mx, lane));
+  mx = fmaxf(mx, lane_xor_f32<32>(mx, lane));
+  mx *= fabsf(f);
   int ex = 0;
   if (mx > 0.0f) { int e2; frexpf(mx, &e2); ex = 14 - e2; }
   ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
   const float qs_inv = ldexpf(1.0f, -ex);
-  half8 qhi[CG][4], qlo[CG][4];
+  const float fs = ldexpf(f, ex);   // f 2^ex: exact
 #pragma unroll
-  for (int c = 0; c < CG; ++c)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int el = 0; el < 8; ++el) {
-        // TBQ4 K operands hold the 4 even then the 4 odd dims of a code
-        // word; TBQ3, fp16 and q8_0 K operands hold 8 consecutive elements
-        // of the lane's order above
-        const int i = KF == kFmtTbq4 ? 8 * k + (el < 4 ? 2 * el : 2 * el - 7) : 8 * k + el;
-        const float x = ldexpf(qv[c][i], ex);
-        const _Float16 hi = (_Float16)x;
-        qhi[c][k][el] = hi;
-        qlo[c][k][el] = (_Float16)(x - (float)hi);
-      }
-#pragma unroll
-  for (int c = 0; c < CG; ++c)
+  for (int c = 0; c < CG; ++c) {
+    const float fc = live[c] ? fs : 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      qlds[c][k][0][lane] = qhi[c][k];
-      qlds[c][k][1][lane] = qlo[c][k];
+      // operand word j holds elements (8k + e0, 8k + e1): TBQ4 K operands
+      // hold the 4 even then the 4 odd dims of a code word (pairs 0 2, 4 6,
+      // 1 3, 5 7); TBQ3, fp16 and q8_0 K operands 8 consecutive elements of
+      // the lane's order above
+      u32x4 hw, lw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e0 = KF == kFmtTbq4 ? (j < 2 ? 4 * j : 4 * (j - 2) + 1) : 2 * j;
+        const int e1 = KF == kFmtTbq4 ? e0 + 2 : e0 + 1;
+        const float x0 = qv[c][8 * k + e0] * fc, x1 = qv[c][8 * k + e1] * fc;
+        hw[j] = pk_f16(x0, x1);
+        lw[j] = pk_f16_residual(hw[j], x0, x1);
+      }
+      qlds[c][k][0][lane] = __builtin_bit_cast(half8, hw);
+      qlds[c][k][1][lane] = __builtin_bit_cast(half8, lw);
     }
+  }
 
   // ---------------- token range: slots [0, n_past + n_q) in 32-token tiles
   const int n_kv = a.n_past + a.n_q;
@@ -596,8 +598,8 @@ __global__ __launch_bounds__(64) void verify_split_kernel(VerifyArgs a) {
   const int P = a.n_splits;
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
-    l_run[c] += __shfl_xor(l_run[c], 16, 64);
-    l_run[c] += __shfl_xor(l_run[c], 32, 64);
+    l_run[c] += lane_xor_f32<16>(l_run[c], lane);
+    l_run[c] += lane_xor_f32<32>(l_run[c], lane);
     const int qi = 2 * c + qsub;
     if (lane < 16 && qi < a.n_q && head < G) {
       float *w = a.ws + (((size_t)b * a.n_q + qi) * a.n_q_heads + (size_t)g * G + head) * P * 130 +
