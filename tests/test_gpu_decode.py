@@ -107,6 +107,17 @@ def test_split_counts_agree(P):
     check_attn(out, ref, False, f"P={P}")
 
 
+@pytest.mark.parametrize("n_ctx,P", [(4113, 64), (4113, 65), (4113, 13), (4096, 64), (4096, 65),
+                                      (4096, 43), (90, 64), (33, 3)])
+def test_split_ranges(n_ctx, P):
+    """Batch 2, 8 KV heads, about one streaming wavefront per SIMD: split
+    ranges of odd and even tile counts, a ragged last tile, splits with a
+    single tile and empty splits, in fp32 output against the oracle."""
+    out, ref = _run_small(2, 8, 2, 4113, 4128, n_ctx, 0.1, seed=6, P=P, out_dtype=torch.float32,
+                          rng_seed=n_ctx + P)
+    check_attn(out, ref, False, f"n_ctx={n_ctx} P={P}")
+
+
 def test_deterministic():
     rng = np.random.default_rng(9)
     k = rng.standard_normal((1, 3000, 2, 128)).astype(np.float32)

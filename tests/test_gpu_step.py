@@ -78,7 +78,7 @@ def test_step_equals_append_then_decode(src, qdt, H, G):
 
 
 @pytest.mark.parametrize("pos", [0, 1, 31, 32, 33, 1023])
-@pytest.mark.parametrize("P", [0, 1, 5, 64])
+@pytest.mark.parametrize("P", [0, 1, 5, 64, 300])
 def test_step_positions_and_splits(pos, P):
     """slot 0 (the token alone), tile edges, the last slot; split counts
     from one to more splits than tiles; fp16 output."""
