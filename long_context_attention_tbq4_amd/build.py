@@ -19,9 +19,11 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtbq4.so")
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "verify.hip", "prefill.hip",
            "bench_kernels.hip"]
-# per-source options: the decode loop keeps its MFMA accumulators in
-# ordinary VGPRs (its conditional rescale then needs no register copies)
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source options: the decode and verify loops keep their MFMA
+# accumulators in ordinary VGPRs (the conditional rescale and the scores then
+# need no copies between accumulation and vector registers)
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():
