@@ -117,6 +117,7 @@ constexpr float kShareInv = 32.0f;
 template <typename QT, typename OT, int KF, int VF>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillLds<KF, VF> L;
+  __shared__ float q_wmax[kWaves];   // max |q'| per wavefront (the normalisation)
   constexpr bool kKRot = KF == kFmtTbq4 || KF == kFmtTbq3;   // stored rotated: q is rotated to meet it
   constexpr bool kVRot = VF == kFmtTbq4 || VF == kFmtTbq3;   // stored rotated: the output is rotated back
 
@@ -179,8 +180,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       x[i] *= f;
       mx = fmaxf(mx, fabsf(x[i]));
     }
+    // one power-of-two normalisation for all rows of the workgroup: the
+    // largest |q'| of its rows in [2^13, 2^14).  The staged key scales then
+    // carry the factor back (d^K 2^-ex), so a score reaches log2 units in
+    // the same fused multiply-add that subtracts the running maximum.
+    // (Smaller rows keep 22-bit q' pairs down to fp16's subnormal range,
+    // whose spacing is 2^-38 of the largest row's max |q'|.)
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // power-of-two normalisation: max |q'| in [2^13, 2^14)
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    if (lane == 0) q_wmax[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, q_wmax[w]);
     int ex = 0;
     if (mx > 0.0f) {
       int e2;
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq)) = c0;
     *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq + 16)) = c1;
     if (fq == 0) {
-      L.sk[buf][fkey] = scale_of(r.k, std::integral_constant<int, KF>{});
+      L.sk[buf][fkey] = scale_of(r.k, std::integral_constant<int, KF>{}) * rowscale;   // exact
       L.sv[buf][fkey] = scale_of(r.v, std::integral_constant<int, VF>{});
     }
     // q8_0: the block scales (a slot at or past n_keys reads as scale 0, so
@@ -386,33 +401,41 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       // the softmax issues at raised priority: the SIMD's other wavefront,
       // when it is in its MFMA phase, keeps the matrix core busy meanwhile
       __builtin_amdgcn_s_setprio(1);
-      // element e holds key kb0 + 8 (e/4) + 4 half + e%4.  Scores and the
-      // running maximum stay scaled by the row's 2^ex (q' was normalised by
-      // it); the exact power-of-two scaling back is folded into the
-      // exponent's fused multiply-add.
-      float s[16];
+      // element e holds key kb0 + 8 (e/4) + 4 half + e%4.  t = the score in
+      // log2 units minus the reference m_ref (the row's running maximum, 0
+      // before its first block): one fused multiply-add with the staged
+      // d^K 2^-ex.  Only a block that raises some row's maximum (and the
+      // first block) moves the reference, shifts t and rescales O' and l.
+      const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
+      float t[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float4v dk4 = *(const float4v *)(&L.sk[buf][kb0 + 8 * m + 4 * half]);
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) s[4 * m + e2] = sacc[4 * m + e2] * dk4[e2];
+        for (int e2 = 0; e2 < 4; ++e2) t[4 * m + e2] = fmaf(sacc[4 * m + e2], dk4[e2], -m_ref);
       }
       if (masked) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2)
-            s[4 * m + e2] += (key0 + kb0 + 8 * m + 4 * half + e2 <= key_limit) ? 0.0f : -INFINITY;
+            t[4 * m + e2] += (key0 + kb0 + 8 * m + 4 * half + e2 <= key_limit) ? 0.0f : -INFINITY;
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, t[e]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * rowscale);
-      m_run = m_new;
-      const float m_log2 = m_new * rowscale;
-      if (__any(alpha != 1.0f)) {
+      float alpha = 1.0f;
+      if (__any(tmax > 0.0f || m_run == -INFINITY)) {
+        // (every row sees key 0, so a row's first block has a finite maximum;
+        // a row with no key in this block keeps its reference: alpha 1)
+        const float m_new = fmaxf(m_run, m_ref + tmax);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 before the first block
+        const float sh = m_ref - m_new;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t[e] += sh;
+        tmax += sh;
+        m_run = m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -426,7 +449,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 4 * m + e2;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[e], rowscale, -m_log2));
+          const float p = __builtin_amdgcn_exp2f(t[e]);
           psum += p;
           pt[e] = p * dv4[e2];
         }
@@ -437,7 +460,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       // fp16 residual of P~ as a second PV product.  Keys below that share
       // enter with one fp16 rounding each, and those roundings average out
       // over the many keys that then carry the weight.
-      const float p_top = __builtin_amdgcn_exp2f(fmaf(tmax, rowscale, -m_log2));
+      const float p_top = __builtin_amdgcn_exp2f(tmax);
       const bool fine = __any(p_top * kShareInv > l_run);
 
       uint32_t pw[8], rw[8];
