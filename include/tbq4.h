@@ -407,6 +407,9 @@ tbq4_status tbq4_decode_step_timed(const tbq4_cache *cache, const void *k_new, c
  * n_q) must already hold the chunk's own K/V (tbq4_quantize_append first).
  *   q, out   device, [batch][n_q][n_q_heads][128]; q_dtype F32, F16 or BF16,
  *            out_dtype F16 or F32.
+ * Range: each entry of softmax_scale * log2(e) * (R q) (R q for a K stored
+ * unrotated) must stay below 2^28 in magnitude (scores far beyond any
+ * meaningful softmax); larger entries may overflow to inf.
  * Errors: n_past >= 0, n_q >= 1, n_past + n_q <= capacity else
  * TBQ4_ERR_CAPACITY; n_q_heads / n_kv_heads must be 1, 2, 4, 8, 16 or 32,
  * else TBQ4_ERR_UNSUPPORTED. */

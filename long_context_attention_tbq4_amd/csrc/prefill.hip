@@ -16,10 +16,12 @@
 //     current one (wavefront w loads eighth w of every key's index bytes;
 //     together the eight cover the tile's contiguous bytes) and dequantises
 //     them into the other half of a double-buffered LDS tile: fp16 codebook
-//     values, one fp32 scale per key and tensor,
+//     values (K times the power of two 2^-ex that normalises q', applied by
+//     the fp8 -> fp16 convert), and the key's two fp16 scales in one word,
 //   * S^T = K Q'^T on v_mfma_f32_32x32x16_f16, with q' split into an fp16
 //     high part and the fp16 residual that both accumulate into the same
-//     fp32 scores (~22 bits of q'), then scales by d^K per key,
+//     fp32 scores (~22 bits of q'), then scales by d^K per key (a mixed
+//     fp32 x fp16 multiply-add straight from the staged scale word),
 //   * online softmax in the log2 domain, P~ = p d^V in fp16 (plus its fp16
 //     residual as a second PV product in blocks where one key carries more
 //     than 1/32 of a row's running weight),
@@ -56,8 +58,8 @@ __device__ __forceinline__ int v_swizzle(int r, int byte) { return byte ^ (((r >
 template <int KF, int VF> struct __attribute__((aligned(16))) PrefillLds {
   uint8_t k[2][kTileB];
   uint8_t v[2][kVTileB];
-  float sk[2][kKT];
-  float sv[2][kKT];
+  // per key: the fp16 K scale in the low half, the fp16 V scale in the high
+  uint32_t skv[2][kKT];
   // q8_0 tensors: one scale per (key, 32-dim block)
   float skq[KF == kFmtQ8 ? 2 : 1][4][KF == kFmtQ8 ? kKT : 4];
   float svq[VF == kFmtQ8 ? 2 : 1][4][VF == kFmtQ8 ? kKT : 4];
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   // ---------------- q' = R q * scale * log2(e): fp16 high part + residual
   // lane holds positions 16 c + 8 half + e (c = 0..7, e = 0..7)
   half8 qh[8], ql[8];
-  float rowscale;
+  float kscale;           // 2^-ex: staged TBQ K values carry it
+  uint32_t kunit_bits;    // fp16 bits of 2^-ex
   {
     float x[64];
     const QT *qp = (const QT *)a.q + (((size_t)b * a.n_q + qi_c) * a.n_q_heads + hq) * kHeadDim;
@@ -181,11 +184,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       mx = fmaxf(mx, fabsf(x[i]));
     }
     // one power-of-two normalisation for all rows of the workgroup: the
-    // largest |q'| of its rows in [2^13, 2^14).  The staged key scales then
-    // carry the factor back (d^K 2^-ex), so a score reaches log2 units in
-    // the same fused multiply-add that subtracts the running maximum.
-    // (Smaller rows keep 22-bit q' pairs down to fp16's subnormal range,
-    // whose spacing is 2^-38 of the largest row's max |q'|.)
+    // largest |q'| of its rows in [2^13, 2^14), with ex at most 11.  The
+    // staged K values carry the factor back (codebook values times 2^-ex,
+    // exact fp16 normals for -14 <= ex <= 11), so a score reaches log2 units
+    // in the same fused multiply-add with d^K that subtracts the running
+    // maximum.  (With ex at 11 the largest |q'| is at least 2^-4 of fp16's
+    // largest power of two below its max; smaller elements keep 22-bit q'
+    // pairs down to fp16's subnormal range, whose spacing is 2^-34 of the
+    // largest |q'| or less.  ex is at least -14: q' entries stay below 2^28.)
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
@@ -202,8 +208,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       frexpf(mx, &e2);
       ex = 14 - e2;
     }
-    ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
-    rowscale = ldexpf(1.0f, -ex);
+    ex = ex > 11 ? 11 : (ex < -14 ? -14 : ex);
+    kscale = ldexpf(1.0f, -ex);
+    // K formats staged unscaled (fp16, q8_0) take 2^-ex as their key scale
+    kunit_bits = (uint32_t)(15 - ex) << 10;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -266,25 +274,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   };
   // the 16 fp16 values of a fetched share, in the tensor's position order,
   // as two 16-byte chunks; and the key's scale
-  auto expand = [&](const auto &part, u32x4 &c0, u32x4 &c1, auto fmt_tag) {
+  // (TBQ values times the power of two `sc`: 2^-ex for K, 1 for V)
+  auto expand = [&](const auto &part, u32x4 &c0, u32x4 &c1, float sc, auto fmt_tag) {
     constexpr int F = decltype(fmt_tag)::value;
     if constexpr (F == kFmtTbq4) {
       const uint32_t sh = ((uint32_t)fkey * kBlockBytes + 2 + 8 * fq) & 3u;
       const uint32_t w0 = alignbyte(part.w[1], part.w[0], sh), w1 = alignbyte(part.w[2], part.w[1], sh);
       uint32_t r0, r1, r2, r3;
-      nib4_to_f16(w0, r0, r1);
-      nib4_to_f16(w0 >> 4, r2, r3);
+      nib4_to_f16(w0, r0, r1, sc);
+      nib4_to_f16(w0 >> 4, r2, r3, sc);
       c0 = u32x4{r0, r1, r2, r3};
-      nib4_to_f16(w1, r0, r1);
-      nib4_to_f16(w1 >> 4, r2, r3);
+      nib4_to_f16(w1, r0, r1, sc);
+      nib4_to_f16(w1 >> 4, r2, r3, sc);
       c1 = u32x4{r0, r1, r2, r3};
     } else if constexpr (F == kFmtTbq3) {
       // 16 codes = 48 bits from the (even) start byte
       const uint32_t sh = ((uint32_t)fkey * kBlockBytes3 + 2 + 6 * fq) & 3u;
       const uint32_t lo = alignbyte(part.w[1], part.w[0], sh);
       const uint32_t hi = part.w[1] >> (8 * sh);
-      c0 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(lo & 0xFFFFFFu));
-      c1 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(((lo >> 24) | (hi << 8)) & 0xFFFFFFu));
+      c0 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(lo & 0xFFFFFFu, sc));
+      c1 = __builtin_bit_cast(u32x4, tbq3_chunk_to_half8(((lo >> 24) | (hi << 8)) & 0xFFFFFFu, sc));
     } else if constexpr (F == kFmtQ8) {
       // int8 codes as exact fp16 values, natural order; the block scale is
       // applied per key after the products
@@ -299,27 +308,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       c1 = part.w[1];
     }
   };
-  auto scale_of = [&](const auto &part, auto fmt_tag) -> float {
+  // fp16 bits of a key's scale (TBQ: the block's own, 0 for a slot past the
+  // chunk; fp16 and q8_0: `unit`)
+  auto scale_bits = [&](const auto &part, uint32_t unit, auto fmt_tag) -> uint32_t {
     constexpr int F = decltype(fmt_tag)::value;
-    if constexpr (F == kFmtF16 || F == kFmtQ8) return 1.0f;
-    else return half_bits_to_float(part.s);
+    if constexpr (F == kFmtF16 || F == kFmtQ8) return unit;
+    else return (uint32_t)part.s;
   };
   // dequantise a fetched share into LDS buffer `buf`: 16 fp16 values of K
   // and of V at row fkey, positions 16 fq .. 16 fq + 15
   auto stage = [&](const TileRaw<KF, VF> &r, int buf) {
     u32x4 c0, c1;
-    expand(r.k, c0, c1, std::integral_constant<int, KF>{});
+    expand(r.k, c0, c1, kscale, std::integral_constant<int, KF>{});
     uint8_t *kr = L.k[buf] + fkey * kRowB + 32 * fq;
     *(u32x4 *)kr = c0;
     *(u32x4 *)(kr + 16) = c1;
-    expand(r.v, c0, c1, std::integral_constant<int, VF>{});
+    expand(r.v, c0, c1, 1.0f, std::integral_constant<int, VF>{});
     uint8_t *vr = L.v[buf] + fkey * kVRowB;
     *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq)) = c0;
     *(u32x4 *)(vr + v_swizzle(fkey, 32 * fq + 16)) = c1;
-    if (fq == 0) {
-      L.sk[buf][fkey] = scale_of(r.k, std::integral_constant<int, KF>{}) * rowscale;   // exact
-      L.sv[buf][fkey] = scale_of(r.v, std::integral_constant<int, VF>{});
-    }
+    if (fq == 0)
+      L.skv[buf][fkey] = scale_bits(r.k, kunit_bits, std::integral_constant<int, KF>{}) |
+                         scale_bits(r.v, 0x3C00u, std::integral_constant<int, VF>{}) << 16;
     // q8_0: the block scales (a slot at or past n_keys reads as scale 0, so
     // its finite codes contribute nothing)
     if constexpr (KF == kFmtQ8) {
@@ -404,15 +414,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       // element e holds key kb0 + 8 (e/4) + 4 half + e%4.  t = the score in
       // log2 units minus the reference m_ref (the row's running maximum, 0
       // before its first block): one fused multiply-add with the staged
-      // d^K 2^-ex.  Only a block that raises some row's maximum (and the
-      // first block) moves the reference, shifts t and rescales O' and l.
+      // fp16 d^K (the K values already carry 2^-ex).  Only a block that
+      // raises some row's maximum (and the first block) moves the reference,
+      // shifts t and rescales O' and l.
       const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
       float t[16];
+      u32x4 kv4[4];   // scale words of the lane's 16 keys
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const float4v dk4 = *(const float4v *)(&L.sk[buf][kb0 + 8 * m + 4 * half]);
+        kv4[m] = *(const u32x4 *)(&L.skv[buf][kb0 + 8 * m + 4 * half]);
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) t[4 * m + e2] = fmaf(sacc[4 * m + e2], dk4[e2], -m_ref);
+        for (int e2 = 0; e2 < 4; ++e2) t[4 * m + e2] = fma_lo16(sacc[4 * m + e2], kv4[m][e2], -m_ref);
       }
       if (masked) {
 #pragma unroll
@@ -424,7 +436,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, t[e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      {   // the other half's maximum: one swap of the 32-lane halves leaves
+          // the lower half's value in one result and the upper's in the other
+        const auto hm = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                         false, false);
+        tmax = fmaxf(__uint_as_float(hm[0]), __uint_as_float(hm[1]));
+      }
       float alpha = 1.0f;
       if (__any(tmax > 0.0f || m_run == -INFINITY)) {
         // (every row sees key 0, so a row's first block has a finite maximum;
@@ -445,13 +462,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       float pt[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const float4v dv4 = *(const float4v *)(&L.sv[buf][kb0 + 8 * m + 4 * half]);
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = 4 * m + e2;
           const float p = __builtin_amdgcn_exp2f(t[e]);
           psum += p;
-          pt[e] = p * dv4[e2];
+          pt[e] = fma_hi16(p, kv4[m][e2], 0.0f);   // p d^V, rounded once
         }
       }
       l_run = l_run * alpha + psum;

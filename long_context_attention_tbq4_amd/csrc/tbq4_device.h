@@ -52,11 +52,14 @@ __device__ __forceinline__ uint32_t nib4_to_e4m3(uint32_t t) {
   return mag | ((t << 4) & 0x80808080u);
 }
 
-// Four codes -> four fp16 codebook values (two fp16x2 words).
-__device__ __forceinline__ void nib4_to_f16(uint32_t t, uint32_t &w01, uint32_t &w23) {
+// Four codes -> four fp16 codebook values (two fp16x2 words), each times
+// `scale`, a power of two that the convert applies exactly (the caller keeps
+// every product inside fp16's normal range).
+__device__ __forceinline__ void nib4_to_f16(uint32_t t, uint32_t &w01, uint32_t &w23,
+                                            float scale = 1.0f) {
   const uint32_t e = nib4_to_e4m3(t);
-  fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, 1.0f, false);
-  fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, 1.0f, true);
+  fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, scale, false);
+  fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e, scale, true);
   w01 = __builtin_bit_cast(uint32_t, a);
   w23 = __builtin_bit_cast(uint32_t, b);
 }
@@ -114,14 +117,15 @@ __device__ __forceinline__ void tbq3_chunk_to_e4m3(uint32_t x, uint32_t &e03, ui
   e47 = perm(kE4T3Hi, kE4T3Lo, spread3(x >> 12));
 }
 
-// Eight 3-bit codes -> an fp16 MFMA operand, codes in natural order.
-__device__ __forceinline__ half8 tbq3_chunk_to_half8(uint32_t x) {
+// Eight 3-bit codes -> an fp16 MFMA operand, codes in natural order (each
+// value times the power of two `scale`, as for nib4_to_f16).
+__device__ __forceinline__ half8 tbq3_chunk_to_half8(uint32_t x, float scale = 1.0f) {
   uint32_t e03, e47;
   tbq3_chunk_to_e4m3(x, e03, e47);
-  const fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e03, 1.0f, false);
-  const fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e03, 1.0f, true);
-  const fp16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e47, 1.0f, false);
-  const fp16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e47, 1.0f, true);
+  const fp16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e03, scale, false);
+  const fp16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e03, scale, true);
+  const fp16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e47, scale, false);
+  const fp16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e47, scale, true);
   u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
              __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
   return __builtin_bit_cast(half8, v);
@@ -236,6 +240,21 @@ __device__ __forceinline__ uint32_t pk_f16_residual(uint32_t hw, float x0, float
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// a * h + c with h the fp16 in the low (fma_lo16) or high (fma_hi16) half of
+// the word hw, widened exactly and fused in fp32 (one rounding): the same
+// value as fmaf(a, (float)h, c), without a separate widening instruction.
+__device__ __forceinline__ float fma_lo16(float a, uint32_t hw, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(hw), "v"(c));
+  return d;
+}
+__device__ __forceinline__ float fma_hi16(float a, uint32_t hw, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=v"(d) : "v"(a), "v"(hw), "v"(c));
+  return d;
 }
 
 // 16-lane row rotation by 8: lane j receives lane (j + 8) mod 16 of its row.

@@ -69,6 +69,16 @@ def test_peaky_scores():
     check_attn(out, ref, False, "peaky")
 
 
+@pytest.mark.parametrize("scale", [1e-4, 2.0, 30.0])
+def test_query_magnitudes(scale):
+    """q' is normalised by one power of two per workgroup, which the staged K
+    values carry back: tiny queries (the normalisation at its bound, near-
+    uniform weights), and large ones (the exponent well inside its range,
+    peaky weights) match the oracle like the usual scale."""
+    out, ref = _case(1, 2, 8, 300, 40, 344, scale, seed=4, rng_seed=11)
+    check_attn(out, ref, False, f"qscale={scale}")
+
+
 def test_matches_decode_for_single_query():
     """A one-query chunk is a decode step: both paths agree with the oracle."""
     rng = np.random.default_rng(7)
