@@ -112,6 +112,10 @@ template <int KF, int VF> struct TileRaw {
 };
 
 constexpr int kWaves = 8;           // wavefronts per workgroup (32 rows each)
+// TBQ4 K and V read each 32-key block's MFMA operands ahead of their use (the
+// other formats' staging holds more registers: there the same reads would
+// spill, so they read each operand just before its MFMA)
+template <int KF, int VF> constexpr bool kOpAheadOf = KF == kFmtTbq4 && VF == kFmtTbq4;
 // A 32-key block takes the fp16 residual of P~ as a second PV product when one
 // of its keys carries more than 1/kShareInv of a row's running weight sum.
 constexpr float kShareInv = 32.0f;
@@ -122,6 +126,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   __shared__ float q_wmax[kWaves];   // max |q'| per wavefront (the normalisation)
   constexpr bool kKRot = KF == kFmtTbq4 || KF == kFmtTbq3;   // stored rotated: q is rotated to meet it
   constexpr bool kVRot = VF == kFmtTbq4 || VF == kFmtTbq3;   // stored rotated: the output is rotated back
+  constexpr bool kOpAhead = kOpAheadOf<KF, VF>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -400,13 +405,49 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
               sacc[4 * m + e2] = fmaf(d4[e2], t[4 * m + e2], sacc[4 * m + e2]);
           }
         }
+      } else if constexpr (kOpAhead) {
+        // all eight K operands are read before the first MFMA, so the chain
+        // waits for LDS once rather than at every step
+        half8 ka[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ka[c] = *(const half8 *)(kb + (kb0 + row) * kRowB + 32 * c + 16 * half);
+        __builtin_amdgcn_sched_barrier(0);   // (the scheduler would sink the reads)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[c], qh[c], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[c], ql[c], sacc, 0, 0, 0);
+        }
       } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const half8 ka = *(const half8 *)(kb + (kb0 + row) * kRowB + 32 * c + 16 * half);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[c], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[c], sacc, 0, 0, 0);
+        for (int c = 0; c < 8; ++c) {
+          const half8 ka = *(const half8 *)(kb + (kb0 + row) * kRowB + 32 * c + 16 * half);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[c], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[c], sacc, 0, 0, 0);
+        }
       }
+      // the scale words of the lane's 16 keys are read while the MFMA chain
+      // runs; for TBQ4 K and V the block's V^T operands follow (LDS reads
+      // return in order, so the softmax waits for the scales only): their
+      // latency passes under the softmax, and the residual pass reuses them
+      u32x4 kv4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) kv4[m] = *(const u32x4 *)(&L.skv[buf][kb0 + 8 * m + 4 * half]);
+      typedef __attribute__((address_space(3))) short4v lds_s4;
+      // V^T operand (ks, db) of this block: dims 32 db .., keys 16 ks ..
+      auto v_operand = [&](int ks, int db) -> half8 {
+        const int r0 = kb0 + 16 * ks + tr_row;     // (rows r0 and r0 + 8 share bit 2)
+        const uint8_t *vbase = vb + r0 * kVRowB;
+        const int col = v_swizzle(r0, tr_col + 64 * db);
+        const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
+        const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
+        return __builtin_bit_cast(half8, short8v{ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]});
+      };
+      half8 vop[kOpAhead ? 2 : 1][4];
+      if constexpr (kOpAhead) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) vop[ks][db] = v_operand(ks, db);
       }
       // the softmax issues at raised priority: the SIMD's other wavefront,
       // when it is in its MFMA phase, keeps the matrix core busy meanwhile
@@ -419,13 +460,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       // shifts t and rescales O' and l.
       const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
       float t[16];
-      u32x4 kv4[4];   // scale words of the lane's 16 keys
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        kv4[m] = *(const u32x4 *)(&L.skv[buf][kb0 + 8 * m + 4 * half]);
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) t[4 * m + e2] = fma_lo16(sacc[4 * m + e2], kv4[m][e2], -m_ref);
-      }
       if (masked) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
@@ -494,20 +532,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       auto pv = [&](const uint32_t *w) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int r0 = kb0 + 16 * ks + tr_row;     // (rows r0 and r0 + 8 share bit 2)
-          const uint8_t *vbase = vb + r0 * kVRowB;
           const half8 pb = __builtin_bit_cast(half8, u32x4{w[4 * ks], w[4 * ks + 1], w[4 * ks + 2],
                                                            w[4 * ks + 3]});
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            typedef __attribute__((address_space(3))) short4v lds_s4;
-            const int col = v_swizzle(r0, tr_col + 64 * db);
-            const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
-            const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
-            const half8 vs = __builtin_bit_cast(
-                half8, short8v{ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]});
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vs, pb, o[db], 0, 0, 0);
-          }
+          for (int db = 0; db < 4; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kOpAhead ? vop[ks][db] : v_operand(ks, db), pb,
+                                                           o[db], 0, 0, 0);
         }
       };
       if constexpr (VF == kFmtQ8) {
@@ -531,14 +561,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
           }
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const int r0 = kb0 + 16 * ks + tr_row;
-            const uint8_t *vbase = vb + r0 * kVRowB;
-            typedef __attribute__((address_space(3))) short4v lds_s4;
-            const int col = v_swizzle(r0, tr_col + 64 * db);
-            const short4v ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + col));
-            const short4v rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(vbase + 8 * kVRowB + col));
-            const half8 vs = __builtin_bit_cast(
-                half8, short8v{ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]});
+            const half8 vs = v_operand(ks, db);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 vs, __builtin_bit_cast(half8, u32x4{w[4 * ks], w[4 * ks + 1], w[4 * ks + 2], w[4 * ks + 3]}),
                 o[db], 0, 0, 0);
