@@ -56,8 +56,8 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # the kernel's sources hash to the version the counters were taken on;
 # otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "5a35205ecc6794aff13e122e5e907bbb3198607c137559909d531e74f64e973e",
-           "n_splits": 64, "fetch_kib": 271259.1, "fetch_factor": 2.0,
+TRAFFIC = {"sources_sha256": "c3241e42138b435022491c8ecf067cd61e5c8034ba76336b2c0bc20379bdead4",
+           "n_splits": 64, "fetch_kib": 271259.4, "fetch_factor": 2.0,
            "write_kib": 8852.3, "write_factor": 1.0}
 
 
