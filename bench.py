@@ -403,7 +403,7 @@ def bench_decode(tb, torch, args):
     # every timed call)
     flush = Flush(torch)
     split = lambda: tb.attn_decode_partial(cache, q, T, w.softmax_scale, n_splits=P, workspace=ws)
-    n_d = max(args.steps, 30)
+    n_d = max(args.steps, 50)
     dists = {"step_warm": dist(time_each(torch, step, n_d)),
              "step_cold": dist(time_each(torch, step, n_d, flush)),
              "split_kernel_warm": dist(time_each(torch, split, n_d)),
@@ -766,7 +766,7 @@ def bench_prefill(tb, torch, args):
     q = torch.from_numpy(q_prefill(w)).cuda()
     out = torch.empty((1, n_q, Hq, 128), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
-    steps = args.prefill_steps or min(10, max(3, args.steps // 4))
+    steps = args.prefill_steps or 20   # timed calls, warm and cold alike
 
     def step(ev=None):
         tb.quantize_append(cache, k_new, v_new, n_past)
