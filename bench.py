@@ -56,8 +56,8 @@ METRIC = "TBQ4 attn: decode HBM GB/s (% peak) @128K; prefill-chunk TFLOP/s"
 # the kernel's sources hash to the version the counters were taken on;
 # otherwise the traffic is unknown (null).
 KERNEL_SOURCES = ("decode.hip", "tbq4_device.h", "tbq4_launch.h")
-TRAFFIC = {"sources_sha256": "c3241e42138b435022491c8ecf067cd61e5c8034ba76336b2c0bc20379bdead4",
-           "n_splits": 64, "fetch_kib": 271259.4, "fetch_factor": 2.0,
+TRAFFIC = {"sources_sha256": "a21e7c620ca1b13449fd852ef52e8acc2bbbc5ec6ec644a34074ab3851a0e758",
+           "n_splits": 64, "fetch_kib": 271259.7, "fetch_factor": 2.0,
            "write_kib": 8852.3, "write_factor": 1.0}
 
 

@@ -639,6 +639,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();   // staged V rows and scales are visible
+    const int own = lo_part ? 1 : 0;
+    // the lane's K and V scales first, then (TBQ4 V) the tile's transposed V
+    // reads: LDS reads return in order, so the scores wait for the scales
+    // only and the V reads' latency passes under the softmax rather than
+    // before the PV MFMAs
+    const float4v kd = *(const float4v *)(sk + 16 * own + 4 * quarter);
+    const float4v vd0 = *(const float4v *)(sv_rd + 4 * quarter);        // block 0
+    const float4v vd1 = *(const float4v *)(sv_rd + 16 + 4 * quarter);   // block 1
+    typedef __attribute__((address_space(3))) int2v lds_i2;
+    int2v vtr[VF == kFmtTbq4 ? 4 : 1];
+    if constexpr (VF == kFmtTbq4) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+        vtr[cg] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(vlds + tr_off + 16 * cg));
+    }
     if constexpr (KF == kFmtQ8) {
 #pragma unroll
       for (int blk = 0; blk < kBlk; ++blk)
@@ -666,12 +681,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // <= 256 * 255.875 = 65504 stays finite in fp16 (tiles with a larger V
     // scale, and q8_0 V, use lag 0).  A reference that trails the scores by
     // up to kLag spares the rescale on data whose scores drift upward.
-    const int own = lo_part ? 1 : 0;
     const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
     float t4[4];
     float tmax = -INFINITY;
     {
-      const float4v kd = *(const float4v *)(sk + 16 * own + 4 * quarter);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         t4[e] = fmaf(sc[e], kd[e], -m_ref);
@@ -726,8 +739,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       psum += p4[e];
     }
     l_run += psum;
-    const float4v vd0 = *(const float4v *)(sv_rd + 4 * quarter);        // block 0
-    const float4v vd1 = *(const float4v *)(sv_rd + 16 + 4 * quarter);   // block 1
     uint32_t pw[4];   // round to nearest (v_cvt_pk_f16_f32): no truncation bias
     {
       float pt[8];
@@ -765,13 +776,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // ---- O'^T += P~ V
     if constexpr (VF == kFmtTbq4) {
       // V read back transposed: 8 tokens x 1 byte (2 dims) per lane
+      static_assert(kBlk / 2 == 1, "one 32-token P~ operand per tile");
 #pragma unroll
       for (int kk = 0; kk < kBlk / 2; ++kk) {
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
-          typedef __attribute__((address_space(3))) int2v lds_i2;
-          const int2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i2 *)(vlds + tr_off + 32 * kk * kVRow + 16 * cg));
+          const int2v r = vtr[cg];
           const uint32_t w0 = (uint32_t)r[0], w1 = (uint32_t)r[1];
           const half8 ve = lo_nibbles_to_half8(w0, w1);
           const half8 vo = lo_nibbles_to_half8(w0 >> 4, w1 >> 4);
