@@ -134,14 +134,18 @@ def test_append_block_counts_not_multiple_of_four(kf, vf, B, H, n_new):
     assert not cache.k[:, :, :5].any() and not cache.k[:, :, 5 + n_new:].any()
 
 
+@pytest.mark.parametrize("scale", [0.09, 1e-4, 2.0])
 @pytest.mark.parametrize("kf,vf", ALL)
-def test_prefill_formats(kf, vf):
+def test_prefill_formats(kf, vf, scale):
     """Prefill chunk (query i at n_past + i sees slots 0 .. n_past + i) on K
     and V stored as TBQ4, TBQ3, q8_0 or fp16, against the fp64 definition on
     the dequantised tensors; unused slots hold 0xFF bytes (NaN fp16 values,
-    NaN scales) that must not leak."""
+    NaN scales) that must not leak.  The softmax scale sets the power of two
+    that normalises q': at its bound for 0.09 and (far past it) 1e-4, inside
+    its range for 2.0; TBQ K values carry it, fp16 and q8_0 K take it as
+    their key scale."""
     rng = np.random.default_rng(40 + kf + 4 * vf)
-    B, H, G, n_past, n_q, cap, seed, scale = 2, 2, 4, 301, 97, 424, 5, 0.09
+    B, H, G, n_past, n_q, cap, seed = 2, 2, 4, 301, 97, 424, 5
     T = n_past + n_q
     k = rng.standard_normal((B, T, H, 128)).astype(np.float32)
     v = rng.standard_normal((B, T, H, 128)).astype(np.float32)
@@ -166,7 +170,7 @@ def test_prefill_formats(kf, vf):
                 n = n_past + i + 1
                 ref[b, i, g * G:(g + 1) * G] = o.attn_decode_rows_ref(
                     q[b, i, g * G:(g + 1) * G], kh[b, g, :n], vh[b, g, :n], scale)
-    check_attn(out, ref, False, f"prefill k{kf} v{vf}")
+    check_attn(out, ref, False, f"prefill k{kf} v{vf} scale {scale}")
     if (kf, vf) == (tb.FMT_TBQ4, tb.FMT_TBQ4):   # the TBQ4 call computes the same
         plain = tb.KVCache(B, H, cap, sign_seed=seed)
         plain.k.copy_(cache.k)
